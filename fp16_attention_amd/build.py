@@ -1,0 +1,55 @@
+"""Compile libfa16attn.so for gfx950 in-tree with hipcc.
+
+Run `python -m fp16_attention_amd.build` (or call build()). The library is
+written next to this file so it travels with the source tree.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libfa16attn.so")
+SOURCES = ["abi.cpp", "attn_fwd.hip", "e4m3_bridge.hip", "vsa_select.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# -packed-fp32-ops: keep the compiler from forming packed FP32 VALU ops.
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include")]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link the shared library; returns its path."""
+    objs = []
+    bdir = os.path.join(ROOT, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
+        lang = ["-x", "hip"]
+        cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        objs.append(obj)
+    failed = False
+    for cmd, p in procs:
+        out = p.communicate()[0].decode(errors="replace")
+        out = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
+        if p.returncode != 0:
+            failed = True
+            sys.stderr.write(" ".join(cmd) + "\n" + out + "\n")
+        elif verbose and out.strip():
+            sys.stderr.write(out + "\n")
+    if failed:
+        raise RuntimeError("hipcc failed")
+    tmp = LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

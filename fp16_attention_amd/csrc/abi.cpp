@@ -1,0 +1,456 @@
+// C-ABI entry points of libfa16attn.so (declared in include/fa16attn.h).
+//
+// Each entry point validates every argument on the host before its first HIP
+// call, so rejected calls have no side effects and the rejection paths can be
+// exercised without a GPU. It then fills the kernel argument block, enqueues
+// the kernels on the caller's stream and returns; nothing here allocates
+// device memory or synchronises.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/fa16attn.h"
+#include "fa_internal.h"
+
+namespace {
+
+using fa::AttnArgs;
+
+constexpr int kRowsPerTile = 128;  // query rows per workgroup (dense / causal)
+constexpr int kSplitTarget = 1536; // aimed-for work items of a split causal launch
+constexpr int kMinSegTiles = 16;   // at least 1024 keys per segment
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi) in bytes
+};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Address range covered by a [B,H,S,D] strided view of elements of `esize` bytes.
+Span span_of(const void* p, int64_t sb, int64_t sh, int64_t ss, int B, int H, int S, int D, int esize)
+{
+    int64_t last = (int64_t)(B - 1) * sb + (int64_t)(H - 1) * sh + (int64_t)(S - 1) * ss + (D - 1);
+    return Span{(uintptr_t)p, (uintptr_t)p + (uintptr_t)((last + 1) * esize)};
+}
+
+Span span_flat(const void* p, int64_t n, int esize)
+{
+    return Span{(uintptr_t)p, (uintptr_t)p + (uintptr_t)(n * esize)};
+}
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int check_view(const fa_tensor& t)
+{
+    if (!t.data) return FA_ERR_NULL;
+    if (!aligned16(t.data)) return FA_ERR_ALIGN;
+    if (t.stride_b < 0 || t.stride_h < 0 || t.stride_s < 0) return FA_ERR_ALIGN;
+    if ((t.stride_b % 8) || (t.stride_h % 8) || (t.stride_s % 8)) return FA_ERR_ALIGN;
+    return FA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP + (int)e; }
+
+void fill_view(const fa_tensor& t, const _Float16*& p, int64_t& sb, int64_t& sh, int64_t& ss)
+{
+    p = (const _Float16*)t.data;
+    sb = t.stride_b;
+    sh = t.stride_h;
+    ss = t.stride_s;
+}
+
+// Split-KV policy for the causal prefill: a pure function of the shape, so the
+// workspace query and the launch agree and results are reproducible.
+struct SplitPlan {
+    int n_qt, nseg, seg_tiles;
+    size_t workspace;
+};
+
+SplitPlan plan_split(int B, int Hq, int D, int q_rows, int kv_len)
+{
+    SplitPlan p;
+    p.n_qt = (q_rows + kRowsPerTile - 1) / kRowsPerTile;
+    const int max_tiles = (kv_len + fa::kTileN - 1) / fa::kTileN;
+    const int64_t items = (int64_t)B * Hq * p.n_qt;
+    int want = (int)std::min<int64_t>(16, std::max<int64_t>(1, (kSplitTarget + items - 1) / items));
+    int seg_tiles = std::max(kMinSegTiles, (max_tiles + want - 1) / want);
+    p.nseg = (max_tiles + seg_tiles - 1) / seg_tiles;
+    p.seg_tiles = seg_tiles;
+    if (p.nseg <= 1) {
+        p.nseg = 1;
+        p.seg_tiles = max_tiles;
+        p.workspace = 0;
+    } else {
+        size_t rows = (size_t)p.nseg * B * Hq * q_rows;
+        size_t o_bytes = rows * (size_t)D * 4;
+        o_bytes = (o_bytes + 255) & ~(size_t)255;
+        p.workspace = o_bytes + rows * 2 * 4;
+    }
+    return p;
+}
+
+int check_causal_domain(int B, int Hq, int Hkv, int D, int q_rows, int q_real, int kv_len)
+{
+    if (D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || Hkv < 1 || Hq < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (q_rows < 64 || q_rows > 8192 || q_rows % 64 != 0) return FA_ERR_SHAPE;
+    if (q_real < 1 || q_real > q_rows) return FA_ERR_SHAPE;
+    if (kv_len <= q_real || kv_len > 262144 || kv_len % 32 != 0) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+int set_grid(AttnArgs& a, int64_t items, bool xcd)
+{
+    if (items <= 0 || items > (int64_t)1 << 30) return FA_ERR_SHAPE;
+    a.n_items = (int)items;
+    a.per_xcd = xcd ? (int)((items + 7) / 8) : 0;
+    return FA_OK;
+}
+
+// Shared body of the two causal entry points.
+int run_causal(AttnArgs& a, fa::KvSource src, int D, int q_rows, int kv_len, void* workspace,
+               size_t workspace_bytes, hipStream_t stream, const Span* inputs, int n_inputs,
+               Span out_span, Span lse_span)
+{
+    SplitPlan p = plan_split(a.B, a.Hq, D, q_rows, kv_len);
+    if (p.workspace > 0) {
+        if (!workspace || workspace_bytes < p.workspace) return FA_ERR_WORKSPACE;
+        if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
+        Span ws = span_flat(workspace, (int64_t)p.workspace, 1);
+        for (int i = 0; i < n_inputs; ++i)
+            if (overlap(ws, inputs[i])) return FA_ERR_ALIAS;
+        if (overlap(ws, out_span) || (a.lse && overlap(ws, lse_span))) return FA_ERR_ALIAS;
+    }
+    a.n_qt = p.n_qt;
+    a.nseg = p.nseg;
+    a.seg_tiles = p.seg_tiles;
+    const bool split = p.nseg > 1;
+    if (split) {
+        size_t rows = (size_t)p.nseg * a.B * a.Hq * q_rows;
+        size_t o_bytes = ((rows * (size_t)D * 4) + 255) & ~(size_t)255;
+        a.o_part = (float*)workspace;
+        a.ml_part = (float*)((char*)workspace + o_bytes);
+    }
+    int rc = set_grid(a, (int64_t)a.B * a.Hq * p.n_qt * p.nseg, true);
+    if (rc) return rc;
+    hipError_t e = fa::launch_attn(a, D, src, fa::KEYS_CAUSAL, split, stream);
+    if (e != hipSuccess || !split) return hip_status(e);
+    fa::MergeArgs m;
+    memset(&m, 0, sizeof(m));
+    m.o_part = a.o_part;
+    m.ml_part = a.ml_part;
+    m.o = a.o;
+    m.o_sb = a.o_sb;
+    m.o_sh = a.o_sh;
+    m.o_ss = a.o_ss;
+    m.lse = a.lse;
+    m.B = a.B;
+    m.Hq = a.Hq;
+    m.Lq = a.Lq;
+    m.nseg = p.nseg;
+    m.seg_tiles = p.seg_tiles;
+    m.n_qt = p.n_qt;
+    m.rows_per_tile = kRowsPerTile;
+    m.offset = a.offset;
+    m.Lkv = a.Lkv;
+    m.oscale = a.oscale;
+    return hip_status(fa::launch_merge(m, D, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA16ATTN_ABI_VERSION; }
+
+const char* fa_error_string(int code)
+{
+    switch (code) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "fa16attn: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "fa16attn: a size is outside the supported domain";
+    case FA_ERR_UNSUPPORTED: return "fa16attn: unsupported head dimension, page size or block size";
+    case FA_ERR_ALIGN: return "fa16attn: bad alignment or stride (D stride 1, 16-byte base, strides multiple of 8)";
+    case FA_ERR_WORKSPACE: return "fa16attn: workspace missing or too small";
+    case FA_ERR_ALIAS: return "fa16attn: an output overlaps an input or another output";
+    default: break;
+    }
+    if (code > FA_ERR_HIP) return "fa16attn: HIP error during launch (code - 1000 = hipError_t)";
+    return "fa16attn: unknown error code";
+}
+
+int attn_fwd_dense(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse, int B, int H,
+                   int Lq, int Lkv, int D, float scale, void* stream)
+{
+    int rc;
+    if ((rc = check_view(q)) || (rc = check_view(k)) || (rc = check_view(v)) || (rc = check_view(o)))
+        return rc;
+    if (D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || Lq < 0 || Lkv < 1) return FA_ERR_SHAPE;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SHAPE;
+    if (Lq == 0) return FA_OK;
+    Span sq = span_of(q.data, q.stride_b, q.stride_h, q.stride_s, B, H, Lq, D, 2);
+    Span sk = span_of(k.data, k.stride_b, k.stride_h, k.stride_s, B, H, Lkv, D, 2);
+    Span sv = span_of(v.data, v.stride_b, v.stride_h, v.stride_s, B, H, Lkv, D, 2);
+    Span so = span_of(o.data, o.stride_b, o.stride_h, o.stride_s, B, H, Lq, D, 2);
+    Span sl = lse ? span_flat(lse, (int64_t)B * H * Lq, 4) : Span{0, 0};
+    if (overlap(so, sq) || overlap(so, sk) || overlap(so, sv)) return FA_ERR_ALIAS;
+    if (lse && (overlap(sl, sq) || overlap(sl, sk) || overlap(sl, sv) || overlap(sl, so)))
+        return FA_ERR_ALIAS;
+
+    AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    fill_view(q, a.q, a.q_sb, a.q_sh, a.q_ss);
+    fill_view(k, a.k, a.k_sb, a.k_sh, a.k_ss);
+    fill_view(v, a.v, a.v_sb, a.v_sh, a.v_ss);
+    a.o = (_Float16*)o.data;
+    a.o_sb = o.stride_b;
+    a.o_sh = o.stride_h;
+    a.o_ss = o.stride_s;
+    a.lse = lse;
+    a.B = B;
+    a.Hq = H;
+    a.Hkv = H;
+    a.group = 1;
+    a.Lq = Lq;
+    a.Lkv = Lkv;
+    a.c = scale * 1.4426950408889634f;
+    a.oscale = 1.f;
+    a.n_qt = (Lq + kRowsPerTile - 1) / kRowsPerTile;
+    a.nseg = 1;
+    if ((rc = set_grid(a, (int64_t)B * H * a.n_qt, true))) return rc;
+    return hip_status(fa::launch_attn(a, D, fa::KV_FP16, fa::KEYS_DENSE, false, (hipStream_t)stream));
+}
+
+size_t attn_fwd_prefix_causal_workspace(int B, int Hq, int Hkv, int D, int q_rows, int kv_len)
+{
+    if (check_causal_domain(B, Hq, Hkv, D, q_rows, 1, kv_len)) return 0;
+    return plan_split(B, Hq, D, q_rows, kv_len).workspace;
+}
+
+int attn_fwd_prefix_causal(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse, int B,
+                           int Hq, int Hkv, int D, int q_rows, int q_real, int kv_len, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc;
+    if ((rc = check_view(q)) || (rc = check_view(k)) || (rc = check_view(v)) || (rc = check_view(o)))
+        return rc;
+    if ((rc = check_causal_domain(B, Hq, Hkv, D, q_rows, q_real, kv_len))) return rc;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SHAPE;
+    Span in[3] = {span_of(q.data, q.stride_b, q.stride_h, q.stride_s, B, Hq, q_rows, D, 2),
+                  span_of(k.data, k.stride_b, k.stride_h, k.stride_s, B, Hkv, kv_len, D, 2),
+                  span_of(v.data, v.stride_b, v.stride_h, v.stride_s, B, Hkv, kv_len, D, 2)};
+    Span so = span_of(o.data, o.stride_b, o.stride_h, o.stride_s, B, Hq, q_rows, D, 2);
+    Span sl = lse ? span_flat(lse, (int64_t)B * Hq * q_rows, 4) : Span{0, 0};
+    for (const Span& s : in) {
+        if (overlap(so, s)) return FA_ERR_ALIAS;
+        if (lse && overlap(sl, s)) return FA_ERR_ALIAS;
+    }
+    if (lse && overlap(sl, so)) return FA_ERR_ALIAS;
+
+    AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    fill_view(q, a.q, a.q_sb, a.q_sh, a.q_ss);
+    fill_view(k, a.k, a.k_sb, a.k_sh, a.k_ss);
+    fill_view(v, a.v, a.v_sb, a.v_sh, a.v_ss);
+    a.o = (_Float16*)o.data;
+    a.o_sb = o.stride_b;
+    a.o_sh = o.stride_h;
+    a.o_ss = o.stride_s;
+    a.lse = lse;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.group = Hq / Hkv;
+    a.Lq = q_rows;
+    a.Lkv = kv_len;
+    a.offset = (int64_t)kv_len - q_real;
+    a.c = scale * 1.4426950408889634f;
+    a.oscale = 1.f;
+    return run_causal(a, fa::KV_FP16, D, q_rows, kv_len, workspace, workspace_bytes,
+                      (hipStream_t)stream, in, 3, so, sl);
+}
+
+size_t attn_fwd_paged_e4m3_workspace(int B, int Hq, int Hkv, int D, int q_rows, int kv_len)
+{
+    return attn_fwd_prefix_causal_workspace(B, Hq, Hkv, D, q_rows, kv_len);
+}
+
+int attn_fwd_paged_e4m3(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_cache,
+                        const int32_t* page_table, int64_t table_stride, int num_phys_pages,
+                        int page_size, float k_scale, float v_scale, fa_tensor o, float* lse, int B,
+                        int Hq, int Hkv, int D, int q_rows, int q_real, int kv_len, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc;
+    if ((rc = check_view(q)) || (rc = check_view(o))) return rc;
+    if (!k_cache || !v_cache || !page_table) return FA_ERR_NULL;
+    if (page_size != 32) return FA_ERR_UNSUPPORTED;
+    if ((rc = check_causal_domain(B, Hq, Hkv, D, q_rows, q_real, kv_len))) return rc;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SHAPE;
+    if (!(k_scale > 0.f) || !isfinite(k_scale) || !(v_scale > 0.f) || !isfinite(v_scale))
+        return FA_ERR_SHAPE;
+    if (num_phys_pages < 1 || table_stride < (int64_t)(kv_len / 32)) return FA_ERR_SHAPE;
+    if (((uintptr_t)k_cache & 15u) || ((uintptr_t)v_cache & 15u) || ((uintptr_t)page_table & 3u))
+        return FA_ERR_ALIGN;
+    const int64_t cache_bytes = (int64_t)num_phys_pages * 32 * Hkv * D;
+    Span in[4] = {span_of(q.data, q.stride_b, q.stride_h, q.stride_s, B, Hq, q_rows, D, 2),
+                  span_flat(k_cache, cache_bytes, 1), span_flat(v_cache, cache_bytes, 1),
+                  span_flat(page_table, (int64_t)(B - 1) * table_stride + kv_len / 32, 4)};
+    Span so = span_of(o.data, o.stride_b, o.stride_h, o.stride_s, B, Hq, q_rows, D, 2);
+    Span sl = lse ? span_flat(lse, (int64_t)B * Hq * q_rows, 4) : Span{0, 0};
+    for (const Span& s : in) {
+        if (overlap(so, s)) return FA_ERR_ALIAS;
+        if (lse && overlap(sl, s)) return FA_ERR_ALIAS;
+    }
+    if (lse && overlap(sl, so)) return FA_ERR_ALIAS;
+
+    AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    fill_view(q, a.q, a.q_sb, a.q_sh, a.q_ss);
+    a.o = (_Float16*)o.data;
+    a.o_sb = o.stride_b;
+    a.o_sh = o.stride_h;
+    a.o_ss = o.stride_s;
+    a.lse = lse;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.table = page_table;
+    a.table_stride = table_stride;
+    a.num_pages = num_phys_pages;
+    a.page_shift = 5;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.group = Hq / Hkv;
+    a.Lq = q_rows;
+    a.Lkv = kv_len;
+    a.offset = (int64_t)kv_len - q_real;
+    a.c = scale * k_scale * 1.4426950408889634f;
+    a.oscale = v_scale;
+    return run_causal(a, fa::KV_E4M3_PAGED, D, q_rows, kv_len, workspace, workspace_bytes,
+                      (hipStream_t)stream, in, 4, so, sl);
+}
+
+int kv_e4m3_paged_to_fp16(const uint8_t* k_cache, const uint8_t* v_cache, const int32_t* page_table,
+                          int64_t table_stride, int num_phys_pages, int page_size, int B, int Hkv,
+                          int D, int kv_len, float k_scale, float v_scale, uint16_t* k_out,
+                          uint16_t* v_out, void* stream)
+{
+    if (!k_cache || !v_cache || !page_table || !k_out || !v_out) return FA_ERR_NULL;
+    if (page_size != 32) return FA_ERR_UNSUPPORTED;
+    if (D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || Hkv < 1 || kv_len < 1 || num_phys_pages < 1) return FA_ERR_SHAPE;
+    if (table_stride < (int64_t)((kv_len + 31) / 32)) return FA_ERR_SHAPE;
+    if (!isfinite(k_scale) || !isfinite(v_scale)) return FA_ERR_SHAPE;
+    if (((uintptr_t)k_cache & 15u) || ((uintptr_t)v_cache & 15u) || ((uintptr_t)page_table & 3u) ||
+        ((uintptr_t)k_out & 15u) || ((uintptr_t)v_out & 15u))
+        return FA_ERR_ALIGN;
+    const int64_t cache_bytes = (int64_t)num_phys_pages * 32 * Hkv * D;
+    const int64_t out_elems = (int64_t)B * Hkv * kv_len * D;
+    Span in[3] = {span_flat(k_cache, cache_bytes, 1), span_flat(v_cache, cache_bytes, 1),
+                  span_flat(page_table, (int64_t)(B - 1) * table_stride + (kv_len + 31) / 32, 4)};
+    Span ko = span_flat(k_out, out_elems, 2), vo = span_flat(v_out, out_elems, 2);
+    if (overlap(ko, vo)) return FA_ERR_ALIAS;
+    for (const Span& s : in)
+        if (overlap(ko, s) || overlap(vo, s)) return FA_ERR_ALIAS;
+    return hip_status(fa::launch_e4m3_bridge(k_cache, v_cache, page_table, table_stride,
+                                             num_phys_pages, B, Hkv, D, kv_len, k_scale, v_scale,
+                                             k_out, v_out, (hipStream_t)stream));
+}
+
+size_t vsa_block_select_workspace(int B, int H, int L, int D, int block)
+{
+    if (B < 1 || H < 1 || D != 128 || block != 64 || L < 64 || L % 64) return 0;
+    return (size_t)2 * B * H * (L / 64) * D * 4;
+}
+
+int vsa_block_select(const uint16_t* q, const uint16_t* k, int B, int H, int L, int D, int block,
+                     int topk, int32_t* idx_out, double* score_out, void* workspace,
+                     size_t workspace_bytes, void* stream)
+{
+    if (!q || !k || !idx_out) return FA_ERR_NULL;
+    if (D != 128 || block != 64) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || L < block || L % block) return FA_ERR_SHAPE;
+    const int NB = L / block;
+    if (NB > 1024 || topk < 1 || topk > NB) return FA_ERR_SHAPE;
+    if (((uintptr_t)q & 15u) || ((uintptr_t)k & 15u) || ((uintptr_t)idx_out & 3u) ||
+        ((uintptr_t)score_out & 7u))
+        return FA_ERR_ALIGN;
+    const size_t need = vsa_block_select_workspace(B, H, L, D, block);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 255u) return FA_ERR_ALIGN;
+    const int64_t elems = (int64_t)B * H * L * D;
+    Span in[2] = {span_flat(q, elems, 2), span_flat(k, elems, 2)};
+    Span outs[3] = {span_flat(idx_out, (int64_t)B * H * NB * topk, 4),
+                    score_out ? span_flat(score_out, (int64_t)B * H * NB * NB, 8) : Span{0, 0},
+                    span_flat(workspace, (int64_t)need, 1)};
+    for (int i = 0; i < 3; ++i) {
+        for (const Span& s : in)
+            if (overlap(outs[i], s)) return FA_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return FA_ERR_ALIAS;
+    }
+    return hip_status(fa::launch_vsa_select(q, k, B, H, L, D, topk, idx_out, score_out,
+                                            (float*)workspace, (hipStream_t)stream));
+}
+
+int vsa_block_sparse_attn(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, const int32_t* idx,
+                          float* lse, int B, int H, int L, int D, int block, int topk,
+                          int dense_prefix_qblocks, float scale, void* stream)
+{
+    int rc;
+    if ((rc = check_view(q)) || (rc = check_view(k)) || (rc = check_view(v)) || (rc = check_view(o)))
+        return rc;
+    if (!idx) return FA_ERR_NULL;
+    if (D != 128 || block != 64) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || L < block || L % block) return FA_ERR_SHAPE;
+    const int NB = L / block;
+    if (topk < 1 || topk > NB || dense_prefix_qblocks < 0 || dense_prefix_qblocks > NB)
+        return FA_ERR_SHAPE;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SHAPE;
+    if ((uintptr_t)idx & 3u) return FA_ERR_ALIGN;
+    Span in[4] = {span_of(q.data, q.stride_b, q.stride_h, q.stride_s, B, H, L, D, 2),
+                  span_of(k.data, k.stride_b, k.stride_h, k.stride_s, B, H, L, D, 2),
+                  span_of(v.data, v.stride_b, v.stride_h, v.stride_s, B, H, L, D, 2),
+                  span_flat(idx, (int64_t)B * H * NB * topk, 4)};
+    Span so = span_of(o.data, o.stride_b, o.stride_h, o.stride_s, B, H, L, D, 2);
+    Span sl = lse ? span_flat(lse, (int64_t)B * H * L, 4) : Span{0, 0};
+    for (const Span& s : in) {
+        if (overlap(so, s)) return FA_ERR_ALIAS;
+        if (lse && overlap(sl, s)) return FA_ERR_ALIAS;
+    }
+    if (lse && overlap(sl, so)) return FA_ERR_ALIAS;
+
+    AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    fill_view(q, a.q, a.q_sb, a.q_sh, a.q_ss);
+    fill_view(k, a.k, a.k_sb, a.k_sh, a.k_ss);
+    fill_view(v, a.v, a.v_sb, a.v_sh, a.v_ss);
+    a.o = (_Float16*)o.data;
+    a.o_sb = o.stride_b;
+    a.o_sh = o.stride_h;
+    a.o_ss = o.stride_s;
+    a.lse = lse;
+    a.idx = idx;
+    a.topk = topk;
+    a.dense_prefix = dense_prefix_qblocks;
+    a.nqb = NB;
+    a.B = B;
+    a.Hq = H;
+    a.Hkv = H;
+    a.group = 1;
+    a.Lq = L;
+    a.Lkv = L;
+    a.c = scale * 1.4426950408889634f;
+    a.oscale = 1.f;
+    a.n_qt = NB;
+    a.nseg = 1;
+    if ((rc = set_grid(a, (int64_t)B * H * NB, false))) return rc;
+    return hip_status(fa::launch_attn(a, D, fa::KV_FP16, fa::KEYS_BLOCKS, false, (hipStream_t)stream));
+}
+
+}  // extern "C"

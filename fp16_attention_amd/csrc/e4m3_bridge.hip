@@ -1,0 +1,107 @@
+// Exact paged E4M3 -> FP16 conversion ("[Kernel][SM70] Integrate FP32 v37
+// prefill and exact E4M3 bridge", Implementation: exact E4M3 byte conversion
+// with unit and non-unit scales).
+//
+// out = RNE16(RNE32(decode(code) * scale)): the hardware E4M3 -> FP32 decode
+// is exact, the FP32 multiply and the FP32 -> FP16 conversion both round to
+// nearest even, and FP16 subnormals are produced (the FP16 denormal mode is
+// not flushing). A NaN code (0x7F / 0xFF) becomes 0x7E00 with the code's sign.
+//
+// The kernel is HBM-bound: every thread moves one 16-byte chunk of codes of
+// one token row and writes 32 bytes of FP16; consecutive threads cover
+// consecutive chunks of a row and then consecutive tokens, so both the page
+// reads (contiguous within a page when Hkv == 1) and the output writes are
+// coalesced.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// The FP32 products are pinned in VGPRs before the FP16 conversion: left
+// alone, the compiler fuses multiply and conversion into one mixed-precision
+// FMA with a +0 addend, which rounds once (not FP32 then FP16) and turns -0
+// into +0.
+__device__ __forceinline__ uint32_t cvt2(float a, float b, uint32_t code_a, uint32_t code_b)
+{
+    asm volatile("" : "+v"(a), "+v"(b));
+    uint16_t ha = __builtin_bit_cast(uint16_t, (_Float16)a);
+    uint16_t hb = __builtin_bit_cast(uint16_t, (_Float16)b);
+    if ((code_a & 0x7Fu) == 0x7Fu) ha = (uint16_t)(((code_a & 0x80u) << 8) | 0x7E00u);
+    if ((code_b & 0x7Fu) == 0x7Fu) hb = (uint16_t)(((code_b & 0x80u) << 8) | 0x7E00u);
+    return (uint32_t)ha | ((uint32_t)hb << 16);
+}
+
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+// Four codes packed in w -> two dwords of FP16 pairs.
+__device__ __forceinline__ u2 convert4(uint32_t w, float scale)
+{
+    f2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);  // bytes 0, 1
+    f2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);   // bytes 2, 3
+    u2 r;
+    r.x = cvt2(a.x * scale, a.y * scale, w & 0xFFu, (w >> 8) & 0xFFu);
+    r.y = cvt2(b.x * scale, b.y * scale, (w >> 16) & 0xFFu, w >> 24);
+    return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void e4m3_bridge_kernel(const uint8_t* __restrict__ kc,
+                                                          const uint8_t* __restrict__ vc,
+                                                          const int32_t* __restrict__ table,
+                                                          int64_t table_stride, int num_pages,
+                                                          int B, int Hkv, int kv_len, float k_scale,
+                                                          float v_scale, uint16_t* __restrict__ k_out,
+                                                          uint16_t* __restrict__ v_out)
+{
+    constexpr int CPR = D / 16;  // 16-byte chunks per row
+    const int64_t rows = (int64_t)B * Hkv * kv_len;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= rows * CPR) return;
+    const bool is_v = blockIdx.y != 0;
+    const int chunk = (int)(gid % CPR);
+    const int64_t row = gid / CPR;  // (b, g, t) in output order
+    const int t = (int)(row % kv_len);
+    const int64_t bg = row / kv_len;
+    const int g = (int)(bg % Hkv);
+    const int b = (int)(bg / Hkv);
+
+    int page = table[(int64_t)b * table_stride + (t >> 5)];
+    page = min(max(page, 0), num_pages - 1);
+    const int64_t src = (((int64_t)page * 32 + (t & 31)) * Hkv + g) * D + chunk * 16;
+    const u4 w = *(const u4*)((is_v ? vc : kc) + src);
+    const float scale = is_v ? v_scale : k_scale;
+    const u2 c0 = convert4(w.x, scale), c1 = convert4(w.y, scale);
+    const u2 c2 = convert4(w.z, scale), c3 = convert4(w.w, scale);
+    const u4 o0 = {c0.x, c0.y, c1.x, c1.y};
+    const u4 o1 = {c2.x, c2.y, c3.x, c3.y};
+    uint16_t* dst = (is_v ? v_out : k_out) + row * D + chunk * 16;
+    *(u4*)dst = o0;
+    *(u4*)(dst + 8) = o1;
+}
+
+hipError_t launch_e4m3_bridge(const uint8_t* kc, const uint8_t* vc, const int32_t* table,
+                              int64_t table_stride, int num_pages, int B, int Hkv, int D,
+                              int kv_len, float k_scale, float v_scale, uint16_t* k_out,
+                              uint16_t* v_out, hipStream_t stream)
+{
+    const int64_t threads = (int64_t)B * Hkv * kv_len * (D / 16);
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks <= 0) return hipSuccess;
+    dim3 grid((unsigned)blocks, 2);
+    if (D == 128)
+        hipLaunchKernelGGL(e4m3_bridge_kernel<128>, grid, dim3(256), 0, stream, kc, vc, table,
+                           table_stride, num_pages, B, Hkv, kv_len, k_scale, v_scale, k_out, v_out);
+    else if (D == 256)
+        hipLaunchKernelGGL(e4m3_bridge_kernel<256>, grid, dim3(256), 0, stream, kc, vc, table,
+                           table_stride, num_pages, B, Hkv, kv_len, k_scale, v_scale, k_out, v_out);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace fa

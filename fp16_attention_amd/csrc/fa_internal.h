@@ -1,0 +1,88 @@
+// Internal launch interface between the C-ABI layer (abi.cpp) and the HIP
+// kernels. Not installed; the public interface is include/fa16attn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Keys per K/V tile staged in LDS.
+constexpr int kTileN = 64;
+// Query rows per wave (one 32-wide MFMA column block).
+constexpr int kRowsPerWave = 32;
+
+enum KvSource { KV_FP16 = 0, KV_E4M3_PAGED = 1 };
+enum KeyMode { KEYS_DENSE = 0, KEYS_CAUSAL = 1, KEYS_BLOCKS = 2 };
+
+// Everything one attention launch needs; passed by value as the kernel
+// argument. Strides are in elements.
+struct AttnArgs {
+    const _Float16* q;
+    int64_t q_sb, q_sh, q_ss;
+    const _Float16* k;
+    int64_t k_sb, k_sh, k_ss;
+    const _Float16* v;
+    int64_t v_sb, v_sh, v_ss;
+    _Float16* o;
+    int64_t o_sb, o_sh, o_ss;
+    float* lse;  // optional [B, Hq, Lq]
+
+    // paged E4M3 source
+    const uint8_t* kc;
+    const uint8_t* vc;
+    const int32_t* table;
+    int64_t table_stride;
+    int num_pages;
+    int page_shift;  // log2(page_size)
+
+    // block lists
+    const int32_t* idx;  // [B, Hq, Lq / 64, topk]
+    int topk;
+    int dense_prefix;
+    int nqb;  // Lq / 64
+
+    // split-KV partial states (FP32): o_part [nseg][B*Hq][Lq][D] unnormalised,
+    // ml_part [nseg][B*Hq][Lq][2] = (running max in log2 units, running sum)
+    float* o_part;
+    float* ml_part;
+    int nseg;
+    int seg_tiles;
+
+    int B, Hq, Hkv, group;
+    int Lq, Lkv;
+    int64_t offset;  // causal: kv_len - q_real
+    float c;         // softmax scale * log2(e) (times k_scale for E4M3)
+    float oscale;    // output scale (v_scale for E4M3, else 1)
+
+    int n_qt;     // query tiles per (b, h)
+    int n_items;  // work items
+    int per_xcd;  // work items per XCD slice (0: identity mapping)
+};
+
+struct MergeArgs {
+    const float* o_part;
+    const float* ml_part;
+    _Float16* o;
+    int64_t o_sb, o_sh, o_ss;
+    float* lse;
+    int B, Hq, Lq, nseg, seg_tiles, n_qt, rows_per_tile;
+    int64_t offset;
+    int Lkv;
+    float oscale;
+};
+
+hipError_t launch_attn(const AttnArgs& a, int D, KvSource src, KeyMode mode, bool split,
+                       hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& m, int D, hipStream_t stream);
+
+hipError_t launch_e4m3_bridge(const uint8_t* kc, const uint8_t* vc, const int32_t* table,
+                              int64_t table_stride, int num_pages, int B, int Hkv, int D,
+                              int kv_len, float k_scale, float v_scale, uint16_t* k_out,
+                              uint16_t* v_out, hipStream_t stream);
+
+hipError_t launch_vsa_select(const uint16_t* q, const uint16_t* k, int B, int H, int L, int D,
+                             int topk, int32_t* idx_out, double* score_out, float* pooled,
+                             hipStream_t stream);
+
+}  // namespace fa

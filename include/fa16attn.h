@@ -1,0 +1,199 @@
+/*
+ * fa16attn — FP16 fused scaled-dot-product attention forward for AMD MI355X
+ * (gfx950), as a plain C ABI.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] "[Kernel] Share SM70 projection, attention and row reduction paths"
+ *        — Purpose: the default D128 attention backend of a video diffusion
+ *        transformer, with explicit query tiling; FP32 accumulation.
+ *   [P3] "[Video] Integrate H3 SM70 execution, metrics and VSA diagnostics"
+ *        — Purpose: VSA with top-k = 64 KV blocks per query block and
+ *        prefix-dense queries; a native FP16 VSA kernel.
+ *   [P4] "[Kernel][SM70] Integrate FP32 v37 prefill and exact E4M3 bridge"
+ *        — Purpose and Implementation: FP16 causal prefill, B1/Hq6/Hkv1/D256,
+ *        Q 64..8192 in multiples of 64, Q < KV <= 262144, KV a multiple of 32,
+ *        real-query causal offsets kept when padded; FP32 prefix/tail state
+ *        and a final merge; exact E4M3 paged-to-FP16 conversion with unit and
+ *        non-unit scales; bounded per-device workspace.
+ *   [P5] "[perf] FastH3 two-Spark: gather packed FP4 inputs before head
+ *        projections" — minimax_h3_prefix.cu: BHSD operands with a unit
+ *        stride along D and per-tensor batch/head/row strides, an FP32 LSE
+ *        [B,H,Lq], the softmax scale 1/sqrt(D) rounded to FP32;
+ *        minimax_h3_swiglu_gemm.cu / h3_swiglu_gemm_binding.py: integer
+ *        return codes, a raw stream pointer, a caller-owned workspace and a
+ *        binding that raises on a nonzero code.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     memory) on the current HIP device, except where stated.
+ *   - Tensors are described by element strides; the last (D) stride is 1.
+ *     Base pointers of FP16 tensors must be 16-byte aligned and every batch,
+ *     head and row stride a multiple of 8 elements.
+ *   - The caller owns every buffer, the workspace and the stream. The library
+ *     allocates no device memory and never synchronises: a call validates its
+ *     arguments on the host, enqueues its kernels on `stream` (a hipStream_t;
+ *     NULL = the null stream) and returns. Outputs are valid once the stream
+ *     reaches that point. Arguments are checked before any HIP call, so a
+ *     rejected call has no side effects.
+ *   - Results are bitwise reproducible run to run for the same inputs and
+ *     shapes: no atomics take part in any reduction and merges run in a fixed
+ *     order.
+ *   - Calls on different streams may run concurrently if they share no
+ *     output or workspace memory.
+ *   - FP16 is IEEE binary16, passed as uint16_t bit patterns where a C type is
+ *     needed. E4M3 is the OCP E4M3FN byte format (bias 7, no infinities,
+ *     NaN = 0x7F/0xFF, max 448).
+ */
+#ifndef FA16ATTN_H
+#define FA16ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA16ATTN_ABI_VERSION 1
+
+/* Return codes. 0 is success; 1..6 are argument errors detected on the host
+ * before any HIP call; FA_ERR_HIP + e reports HIP error e from a launch. */
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,        /* a required pointer is NULL */
+    FA_ERR_SHAPE = 2,       /* a size is out of the supported domain */
+    FA_ERR_UNSUPPORTED = 3, /* a head dimension, page size or block size not built */
+    FA_ERR_ALIGN = 4,       /* D stride != 1, misaligned base, stride not a multiple of 8 */
+    FA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than the size query returns */
+    FA_ERR_ALIAS = 6,       /* an output overlaps an input or another output */
+    FA_ERR_HIP = 1000
+};
+
+/* A 4-D [B, H, S, D] tensor view: element strides for batch, head and row;
+ * the D stride is 1. */
+typedef struct fa_tensor {
+    void* data;
+    int64_t stride_b;
+    int64_t stride_h;
+    int64_t stride_s;
+} fa_tensor;
+
+/* ABI version of the loaded library (FA16ATTN_ABI_VERSION). */
+int fa_abi_version(void);
+
+/* Static description of a return code; never NULL. */
+const char* fa_error_string(int code);
+
+/*
+ * Dense non-causal attention ([P1] Purpose; [P5] minimax_h3_prefix.cu).
+ *   O[b,h,i,:] = sum_j softmax_j(scale * Q[b,h,i,:] . K[b,h,j,:]) V[b,h,j,:]
+ * q [B,H,Lq,D], k and v [B,H,Lkv,D], o [B,H,Lq,D]: FP16. QK^T and PV are
+ * accumulated in FP32, the softmax runs in FP32 and P is rounded to FP16
+ * before the PV product; O is rounded to FP16 (nearest even).
+ * lse: optional FP32 [B,H,Lq] contiguous, natural-log sum of exp of the
+ * scaled scores; NULL to skip.
+ * Domain: B,H >= 1; Lq >= 0 (0 is a no-op); 1 <= Lkv; D in {128, 256};
+ * B*H*ceil(Lq/128) < 2^31. o must not overlap q, k, v or lse.
+ */
+int attn_fwd_dense(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse, int B, int H,
+                   int Lq, int Lkv, int D, float scale, void* stream);
+
+/*
+ * Causal prefill against a prefix KV with grouped-query heads ([P4]
+ * Implementation). Query row i (0 <= i < q_rows) of query head h sees keys
+ * j <= (kv_len - q_real) + i of kv head h / (Hq / Hkv). Rows i >= q_real are
+ * padding: they follow the same rule (and so see every key); real rows never
+ * depend on padded rows.
+ * q [B,Hq,q_rows,D], k and v [B,Hkv,kv_len,D], o [B,Hq,q_rows,D]: FP16;
+ * lse optional FP32 [B,Hq,q_rows].
+ * The key range of each query tile is split into segments whose FP32 states
+ * (running max, running sum, unnormalised O) go to the workspace and are
+ * merged in segment order by a second kernel.
+ * Domain: B >= 1, Hkv >= 1, Hq % Hkv == 0; D in {128, 256};
+ * 64 <= q_rows <= 8192, q_rows % 64 == 0; 1 <= q_real <= q_rows;
+ * q_real < kv_len <= 262144; kv_len % 32 == 0.
+ * workspace: device memory of at least attn_fwd_prefix_causal_workspace(...)
+ * bytes, 256-byte aligned; may be NULL when that size is 0. Its contents are
+ * scratch and are overwritten.
+ */
+size_t attn_fwd_prefix_causal_workspace(int B, int Hq, int Hkv, int D, int q_rows, int kv_len);
+int attn_fwd_prefix_causal(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse, int B,
+                           int Hq, int Hkv, int D, int q_rows, int q_real, int kv_len, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The causal prefill of attn_fwd_prefix_causal reading K and V from a paged
+ * E4M3 cache ([P4] Purpose, Implementation).
+ * k_cache, v_cache: uint8 [num_phys_pages, page_size, Hkv, D], E4M3 codes.
+ * page_table: int32 [B, table_stride], entry t / page_size of row b is the
+ * physical page of logical token t (t < kv_len). Entries must lie in
+ * [0, num_phys_pages); an entry outside is clamped into range (no fault, the
+ * result for that sequence is then unspecified).
+ * The loader decodes each byte to FP16 exactly (every E4M3 value is an FP16
+ * value); k_scale multiplies the scores and v_scale the output in FP32.
+ * Domain as attn_fwd_prefix_causal, plus page_size == 32,
+ * table_stride >= kv_len / 32, num_phys_pages >= 1, finite scales > 0.
+ */
+size_t attn_fwd_paged_e4m3_workspace(int B, int Hq, int Hkv, int D, int q_rows, int kv_len);
+int attn_fwd_paged_e4m3(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_cache,
+                        const int32_t* page_table, int64_t table_stride, int num_phys_pages,
+                        int page_size, float k_scale, float v_scale, fa_tensor o, float* lse, int B,
+                        int Hq, int Hkv, int D, int q_rows, int q_real, int kv_len, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Exact paged E4M3 -> FP16 conversion ([P4] Implementation, the "exact E4M3
+ * bridge"). For every logical token t < kv_len of row b and kv head g:
+ *   k_out[b,g,t,:] = RNE16(RNE32(decode(k_cache[page][t % page_size][g][:]) * k_scale))
+ * and likewise v_out with v_scale, where page = page_table[b*table_stride +
+ * t/page_size]; one FP32 multiply then one FP16 conversion, both rounding to
+ * nearest even; FP16 subnormals are kept. A NaN code becomes 0x7E00 with the
+ * code's sign. Outputs are contiguous FP16 [B, Hkv, kv_len, D].
+ * Domain: B, Hkv >= 1; D in {128, 256}; page_size == 32; kv_len >= 1;
+ * table_stride >= ceil(kv_len / 32); page entries in [0, num_phys_pages)
+ * (clamped otherwise); scales finite.
+ */
+int kv_e4m3_paged_to_fp16(const uint8_t* k_cache, const uint8_t* v_cache, const int32_t* page_table,
+                          int64_t table_stride, int num_phys_pages, int page_size, int B, int Hkv,
+                          int D, int kv_len, float k_scale, float v_scale, uint16_t* k_out,
+                          uint16_t* v_out, void* stream);
+
+/*
+ * VSA block selection ([P3] Purpose; [P5] key_quant.py and query_pool.py for
+ * the tile means). With NB = L / block:
+ *   qbar[b,h,t,:] = RNE32(sum of the block's FP16 query rows / block),
+ *   kbar likewise from k,
+ *   s[b,h,i,j]    = sum over d ascending of qbar[b,h,i,d] * kbar[b,h,j,d] in FP64,
+ * and idx_out[b,h,i,:] = the topk block indices j with the largest s[b,h,i,j]
+ * (equal scores ranked by the lower j), written in ascending order.
+ * q, k: FP16 [B,H,L,D] contiguous. idx_out: int32 [B,H,NB,topk] contiguous.
+ * score_out: optional FP64 [B,H,NB,NB] (NULL to skip).
+ * Domain: D == 128; block == 64; L % block == 0; 1 <= NB <= 1024;
+ * 1 <= topk <= NB.
+ * workspace: at least vsa_block_select_workspace(...) bytes (the pooled
+ * means), 256-byte aligned.
+ */
+size_t vsa_block_select_workspace(int B, int H, int L, int D, int block);
+int vsa_block_select(const uint16_t* q, const uint16_t* k, int B, int H, int L, int D, int block,
+                     int topk, int32_t* idx_out, double* score_out, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * VSA block-sparse attention ([P3] Purpose). Query block bq = i / block of
+ * head h attends to the keys of the blocks idx[b,h,bq,0..topk) when
+ * bq >= dense_prefix_qblocks, and to every key when bq < dense_prefix_qblocks.
+ * q, k, v, o: FP16 [B,H,L,D] views; idx: int32 [B,H,L/block,topk] contiguous,
+ * entries distinct and in [0, L/block) (out-of-range entries are clamped);
+ * lse: optional FP32 [B,H,L].
+ * Domain: D == 128; block == 64; L % block == 0; 1 <= topk <= L/block;
+ * 0 <= dense_prefix_qblocks <= L/block.
+ */
+int vsa_block_sparse_attn(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, const int32_t* idx,
+                          float* lse, int B, int H, int L, int D, int block, int topk,
+                          int dense_prefix_qblocks, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA16ATTN_H */

@@ -1,0 +1,170 @@
+"""Host-side checks of the C-ABI library (no GPU, no compute calls).
+
+The library must load, export every function include/fa16attn.h declares,
+and reject invalid arguments with the documented codes before any HIP call.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp16_attention_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa16attn.h")
+
+# fake, 256-byte aligned, distinct host addresses: only ever validated, never dereferenced
+A, B_, C, O, L, W = (0x10000000 * (i + 1) for i in range(6))
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b([a-z_0-9]+)\s*\([^;{]*\)\s*;", text)) - {"if", "while"}
+
+
+def test_header_declarations_are_all_exported():
+    declared = _declared()
+    assert declared == set(fa.EXPORTS), declared ^ set(fa.EXPORTS)
+    out = subprocess.check_output(["nm", "-D", "--defined-only", fa.LIB_PATH]).decode()
+    exported = {line.split()[-1] for line in out.splitlines()}
+    assert declared <= exported
+    lib = fa.load()
+    for name in declared:
+        assert hasattr(lib, name)
+    assert lib.fa_abi_version() == 1
+
+
+def test_error_strings():
+    for code in range(7):
+        assert fa.error_string(code)
+    assert "HIP" in fa.error_string(1000 + 1)
+
+
+def T(addr, sb=1 << 20, sh=1 << 16, ss=128):
+    return fa.FaTensor(addr, sb, sh, ss)
+
+
+def dense(**kw):
+    args = dict(q=T(A), k=T(B_), v=T(C), o=T(O), lse=None, B=1, H=2, Lq=256, Lkv=256, D=128, scale=0.088)
+    args.update(kw)
+    return fa.load().attn_fwd_dense(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"],
+                                    args["H"], args["Lq"], args["Lkv"], args["D"], args["scale"], None)
+
+
+def test_dense_rejections():
+    assert dense(q=T(0)) == fa.FA_ERR_NULL
+    assert dense(q=T(A + 2)) == fa.FA_ERR_ALIGN
+    assert dense(k=T(B_, ss=130)) == fa.FA_ERR_ALIGN
+    assert dense(D=64) == fa.FA_ERR_UNSUPPORTED
+    assert dense(Lkv=0) == fa.FA_ERR_SHAPE
+    assert dense(B=0) == fa.FA_ERR_SHAPE
+    assert dense(scale=0.0) == fa.FA_ERR_SHAPE
+    assert dense(scale=float("nan")) == fa.FA_ERR_SHAPE
+    assert dense(o=T(A)) == fa.FA_ERR_ALIAS            # output aliases q
+    assert dense(o=T(A + (1 << 16) * 2)) == fa.FA_ERR_ALIAS  # overlaps q's second head
+    assert dense(lse=O) == fa.FA_ERR_ALIAS
+    assert dense(Lq=0) == fa.FA_OK                     # empty query: a no-op, no launch
+
+
+def causal(**kw):
+    args = dict(q=T(A), k=T(B_, sh=1 << 22, sb=1 << 22, ss=256), v=T(C, sh=1 << 22, sb=1 << 22, ss=256),
+                o=T(O), lse=None, B=1, Hq=6, Hkv=1, D=256, q_rows=128, q_real=100, kv_len=4096, scale=0.0625,
+                ws=W, ws_bytes=1 << 30)
+    args.update(kw)
+    a = args
+    return fa.load().attn_fwd_prefix_causal(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                                            a["Hkv"], a["D"], a["q_rows"], a["q_real"], a["kv_len"],
+                                            a["scale"], a["ws"], a["ws_bytes"], None)
+
+
+def test_causal_domain_rejections():
+    q = T(A, sb=1 << 20, sh=128 * 256, ss=256)
+    assert causal(q=q, q_rows=100) == fa.FA_ERR_SHAPE       # not a multiple of 64
+    assert causal(q=q, q_rows=8256) == fa.FA_ERR_SHAPE      # above 8192
+    assert causal(q=q, q_real=0) == fa.FA_ERR_SHAPE
+    assert causal(q=q, q_real=129) == fa.FA_ERR_SHAPE       # more real rows than rows
+    assert causal(q=q, kv_len=100) == fa.FA_ERR_SHAPE       # q_real >= kv_len
+    assert causal(q=q, kv_len=4000 + 16) == fa.FA_ERR_SHAPE  # not a multiple of 32
+    assert causal(q=q, kv_len=262144 + 32) == fa.FA_ERR_SHAPE
+    assert causal(q=q, Hq=5, Hkv=2) == fa.FA_ERR_SHAPE
+    assert causal(q=q, D=192) == fa.FA_ERR_UNSUPPORTED
+    need = fa.prefix_causal_workspace(1, 6, 1, 256, 128, 4096)
+    assert need > 0
+    assert causal(q=q, ws=0) == fa.FA_ERR_WORKSPACE
+    assert causal(q=q, ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
+    assert causal(q=q, ws=W + 16) == fa.FA_ERR_ALIGN
+    assert causal(q=q, ws=A) == fa.FA_ERR_ALIAS             # workspace over q
+
+
+def test_workspace_queries_are_pure_functions_of_shape():
+    lib = fa.load()
+    a = lib.attn_fwd_prefix_causal_workspace(1, 6, 1, 256, 8000, 128000)
+    assert a == lib.attn_fwd_prefix_causal_workspace(1, 6, 1, 256, 8000, 128000) > 0
+    assert lib.attn_fwd_paged_e4m3_workspace(1, 6, 1, 256, 8000, 256000) >= a
+    assert lib.attn_fwd_prefix_causal_workspace(1, 6, 1, 256, 100, 128000) == 0  # invalid shape -> 0
+    # a short key range needs no split and no workspace
+    assert lib.attn_fwd_prefix_causal_workspace(1, 6, 1, 256, 64, 512) == 0
+    assert lib.vsa_block_select_workspace(1, 8, 36864, 128, 64) == 2 * 8 * 576 * 128 * 4
+
+
+def test_paged_and_bridge_rejections():
+    lib = fa.load()
+    q = T(A, sb=1 << 20, sh=128 * 256, ss=256)
+
+    def paged(**kw):
+        a = dict(page_size=32, ks=1.0, vs=1.0, table_stride=128, pages=128, kv_len=4096, kc=B_, vc=C)
+        a.update(kw)
+        return lib.attn_fwd_paged_e4m3(q, a["kc"], a["vc"], L, a["table_stride"], a["pages"], a["page_size"],
+                                       a["ks"], a["vs"], T(O), None, 1, 6, 1, 256, 128, 100, a["kv_len"],
+                                       0.0625, W, 1 << 30, None)
+    assert paged(page_size=16) == fa.FA_ERR_UNSUPPORTED
+    assert paged(ks=0.0) == fa.FA_ERR_SHAPE
+    assert paged(vs=float("inf")) == fa.FA_ERR_SHAPE
+    assert paged(table_stride=10) == fa.FA_ERR_SHAPE
+    assert paged(pages=0) == fa.FA_ERR_SHAPE
+    assert paged(kc=0) == fa.FA_ERR_NULL
+    assert paged(kc=B_ + 1) == fa.FA_ERR_ALIGN
+
+    def bridge(**kw):
+        a = dict(kc=B_, vc=C, ko=O, vo=O + (1 << 24), D=256, kv_len=4096, page_size=32)
+        a.update(kw)
+        return lib.kv_e4m3_paged_to_fp16(a["kc"], a["vc"], L, 128, 128, a["page_size"], 1, 1, a["D"],
+                                         a["kv_len"], 1.0, 1.0, a["ko"], a["vo"], None)
+    assert bridge(kc=0) == fa.FA_ERR_NULL
+    assert bridge(D=64) == fa.FA_ERR_UNSUPPORTED
+    assert bridge(page_size=64) == fa.FA_ERR_UNSUPPORTED
+    assert bridge(kv_len=0) == fa.FA_ERR_SHAPE
+    assert bridge(vo=O + 64) == fa.FA_ERR_ALIAS       # k_out and v_out overlap
+    assert bridge(ko=B_) == fa.FA_ERR_ALIAS           # output over the cache
+
+
+def test_vsa_rejections():
+    lib = fa.load()
+
+    def select(**kw):
+        a = dict(L=4096, D=128, block=64, topk=8, ws=W, ws_bytes=1 << 30, idx=O)
+        a.update(kw)
+        return lib.vsa_block_select(A, B_, 1, 2, a["L"], a["D"], a["block"], a["topk"], a["idx"], None, a["ws"],
+                                    a["ws_bytes"], None)
+    assert select(block=128) == fa.FA_ERR_UNSUPPORTED
+    assert select(D=256) == fa.FA_ERR_UNSUPPORTED
+    assert select(L=4000) == fa.FA_ERR_SHAPE
+    assert select(topk=0) == fa.FA_ERR_SHAPE
+    assert select(topk=65) == fa.FA_ERR_SHAPE         # more than NB = 64
+    assert select(L=64 * 1025, topk=4) == fa.FA_ERR_SHAPE
+    assert select(ws=0) == fa.FA_ERR_WORKSPACE
+    assert select(idx=0) == fa.FA_ERR_NULL
+    assert select(idx=A) == fa.FA_ERR_ALIAS
+
+    def sparse(**kw):
+        a = dict(topk=8, dp=2, L=4096, o=O)
+        a.update(kw)
+        return lib.vsa_block_sparse_attn(T(A), T(B_), T(C), T(a["o"]), L, None, 1, 2, a["L"], 128, 64, a["topk"],
+                                         a["dp"], 0.088, None)
+    assert sparse(topk=65) == fa.FA_ERR_SHAPE
+    assert sparse(dp=65) == fa.FA_ERR_SHAPE
+    assert sparse(dp=-1) == fa.FA_ERR_SHAPE
+    assert sparse(o=C) == fa.FA_ERR_ALIAS

@@ -1,0 +1,197 @@
+"""GPU parity of every entry point against the FP64 oracle on small seeded
+shapes that span several tiles and ragged tails (marked gpu)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity_util import LSE_ABS, assert_close, qkv, say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+@pytest.mark.parametrize("B,H,Lq,Lkv,D", [(1, 2, 256, 256, 128),     # the tiny dense workload
+                                          (2, 3, 300, 1000, 128),    # ragged query and key tails
+                                          (1, 2, 129, 65, 256),
+                                          (1, 1, 1, 1, 128)])        # single row, single key
+def test_dense_parity(lib, B, H, Lq, Lkv, D):
+    say(f"dense B{B} H{H} Lq{Lq} Lkv{Lkv} D{D}")
+    q, k, v = qkv(1, B, H, H, Lq, Lkv, D)
+    scale = lib.default_scale(D)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device="cuda")
+    out = lib.attn_fwd_dense(dev(q), dev(k), dev(v), lse=lse, scale=scale)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attention(q, k, v, scale)
+    assert_close(out.cpu().numpy().reshape(-1, D), ref, "O")
+    assert np.abs(lse.cpu().numpy().ravel() - ref_lse).max() < LSE_ABS
+
+
+def test_dense_strided_views(lib):
+    """[B, L, H, D] storage passed as BHSD views with a unit D stride."""
+    say("dense strided views")
+    B, H, L, D = 1, 4, 200, 128
+    rng = np.random.default_rng(0)
+    base = [rng.standard_normal((B, L, H, D)).astype(np.float16) for _ in range(3)]
+    qd, kd, vd = (dev(x).transpose(1, 2) for x in base)
+    out_store = torch.zeros((B, L, H, D), dtype=torch.float16, device="cuda")
+    lib.attn_fwd_dense(qd, kd, vd, out=out_store.transpose(1, 2))
+    torch.cuda.synchronize()
+    q, k, v = (x.transpose(0, 2, 1, 3) for x in base)
+    ref, _ = oracle.attention(q, k, v, lib.default_scale(D))
+    assert_close(out_store.transpose(1, 2).cpu().numpy().reshape(-1, D), ref, "O strided")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,q_rows,q_real,kv_len", [
+    (6, 1, 256, 256, 200, 4096),   # split over the key range, padded rows
+    (6, 1, 256, 128, 128, 160),    # one segment, KV tail not a multiple of 64
+    (4, 2, 128, 192, 150, 2400),   # GQA groups of 2, D128
+])
+def test_prefix_causal_parity(lib, Hq, Hkv, D, q_rows, q_real, kv_len):
+    say(f"causal Hq{Hq} Hkv{Hkv} D{D} rows{q_rows} real{q_real} kv{kv_len} "
+        f"ws={lib.prefix_causal_workspace(1, Hq, Hkv, D, q_rows, kv_len)}")
+    q, k, v = qkv(3, 1, Hq, Hkv, q_rows, kv_len, D)
+    scale = lib.default_scale(D)
+    lse = torch.empty((1, Hq, q_rows), dtype=torch.float32, device="cuda")
+    out = lib.attn_fwd_prefix_causal(dev(q), dev(k), dev(v), q_real, lse=lse, scale=scale)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attention(q, k, v, scale, mode=oracle.MODE_CAUSAL, offset=kv_len - q_real)
+    assert_close(out.cpu().numpy().reshape(-1, D), ref, "O")
+    assert np.abs(lse.cpu().numpy().ravel() - ref_lse).max() < LSE_ABS
+
+
+def test_prefix_causal_real_rows_ignore_padding(lib):
+    """Real rows are bitwise independent of what the padded query rows hold."""
+    say("causal padding independence")
+    Hq, Hkv, D, q_rows, q_real, kv_len = 6, 1, 256, 128, 70, 2048
+    q, k, v = qkv(4, 1, Hq, Hkv, q_rows, kv_len, D)
+    a = lib.attn_fwd_prefix_causal(dev(q), dev(k), dev(v), q_real)
+    q2 = q.copy()
+    q2[:, :, q_real:] = np.float16(7.0)
+    b = lib.attn_fwd_prefix_causal(dev(q2), dev(k), dev(v), q_real)
+    torch.cuda.synchronize()
+    assert torch.equal(a[:, :, :q_real], b[:, :, :q_real])
+
+
+def _paged_inputs(seed, Hkv, D, kv_len, pages, ks, vs):
+    k_codes = synth.e4m3_codes(seed, synth.TID_K, (pages, 32, Hkv, D), ks)
+    v_codes = synth.e4m3_codes(seed, synth.TID_V, (pages, 32, Hkv, D), vs)
+    table = synth.permutation(seed, synth.TID_TABLE, pages)[None, : kv_len // 32].copy()
+    return k_codes, v_codes, table
+
+
+@pytest.mark.parametrize("ks,vs", [(1.0, 1.0), (0.0625, 0.03125), (0.0371, 0.0815)])
+def test_paged_e4m3_parity(lib, ks, vs):
+    Hq, Hkv, D, q_rows, q_real, kv_len, pages = 6, 1, 256, 128, 100, 2048, 80
+    say(f"paged e4m3 scales {ks} {vs}")
+    ks, vs = float(np.float32(ks)), float(np.float32(vs))
+    q = synth.normal_f16(5, synth.TID_Q, (1, Hq, q_rows, D))
+    kc, vc, table = _paged_inputs(5, Hkv, D, kv_len, pages, ks, vs)
+    scale = lib.default_scale(D)
+    out = lib.attn_fwd_paged_e4m3(dev(q), dev(kc), dev(vc), dev(table), kv_len, q_real, ks, vs, scale=scale)
+    torch.cuda.synchronize()
+    kf = oracle.e4m3_to_f16(oracle.paged_gather(kc, table, kv_len), ks).view(np.float16)
+    vf = oracle.e4m3_to_f16(oracle.paged_gather(vc, table, kv_len), vs).view(np.float16)
+    ref, _ = oracle.attention(q, kf, vf, scale, mode=oracle.MODE_CAUSAL, offset=kv_len - q_real)
+    assert_close(out.cpu().numpy().reshape(-1, D), ref, "O")
+
+
+def _bits_equal(got, want, codes, what):
+    got = np.asarray(got).view(np.uint16).ravel()
+    want = np.asarray(want).ravel()
+    bad = np.nonzero(got != want)[0]
+    if bad.size:
+        c = np.asarray(codes).ravel()[bad[:8]]
+        raise AssertionError(f"{what}: {bad.size} mismatches; codes {[hex(x) for x in c]} "
+                             f"got {[hex(x) for x in got[bad[:8]]]} want {[hex(x) for x in want[bad[:8]]]}")
+
+
+def test_bridge_bit_exact_all_codes_many_scales(lib):
+    say("bridge all codes")
+    D, Hkv, kv_len = 256, 1, 64
+    codes = np.arange(256, dtype=np.uint8)
+    cache = np.tile(codes, (2 * 32 * Hkv * D) // 256).reshape(2, 32, Hkv, D)
+    rng = np.random.default_rng(9)
+    cache_v = rng.integers(0, 256, cache.shape, dtype=np.uint8)
+    table = np.array([[1, 0]], dtype=np.int32)
+    scales = np.concatenate([[1.0, 0.5, 2.0, 1 / 3, 0.01, 0.1, 146.0, 2.0 ** -16, 1e-7],
+                             rng.uniform(0.01, 0.1, 40), np.ldexp(rng.uniform(1, 2, 40), rng.integers(-20, 8, 40))])
+    kd, vd, td = dev(cache), dev(cache_v), dev(table)
+    for s in scales.astype(np.float32):
+        s = float(s)
+        ko, vo = lib.kv_e4m3_paged_to_fp16(kd, vd, td, 1, kv_len, s, 0.5 * s)
+        torch.cuda.synchronize()
+        g = oracle.paged_gather(cache, table, kv_len)
+        gv = oracle.paged_gather(cache_v, table, kv_len)
+        _bits_equal(ko.cpu().numpy(), oracle.e4m3_to_f16(g, s), g, f"K scale {s}")
+        _bits_equal(vo.cpu().numpy(), oracle.e4m3_to_f16(gv, float(np.float32(0.5 * s))), gv, f"V scale {0.5 * s}")
+
+
+def test_bridge_paged_layout_bit_exact(lib):
+    say("bridge paged layout")
+    Hkv, D, kv_len, pages = 2, 128, 1000, 40
+    kc = synth.e4m3_codes(6, synth.TID_K, (pages, 32, Hkv, D), 0.05)
+    vc = synth.e4m3_codes(6, synth.TID_V, (pages, 32, Hkv, D), 0.05)
+    table = np.stack([synth.permutation(6, synth.TID_TABLE, pages)[:32],
+                      synth.permutation(7, synth.TID_TABLE, pages)[:32]]).astype(np.int32)
+    ko, vo = lib.kv_e4m3_paged_to_fp16(dev(kc), dev(vc), dev(table), 2, kv_len, 0.05, 0.07)
+    torch.cuda.synchronize()
+    for b in range(2):
+        g = oracle.paged_gather(kc, table[b:b + 1], kv_len)
+        assert np.array_equal(ko[b:b + 1].cpu().numpy().view(np.uint16), oracle.e4m3_to_f16(g, 0.05))
+        g = oracle.paged_gather(vc, table[b:b + 1], kv_len)
+        assert np.array_equal(vo[b:b + 1].cpu().numpy().view(np.uint16),
+                              oracle.e4m3_to_f16(g, float(np.float32(0.07))))
+
+
+@pytest.mark.parametrize("B,H,L,topk", [(1, 2, 4096, 8), (2, 1, 64 * 300, 64), (1, 1, 128, 2)])
+def test_vsa_select_bit_exact(lib, B, H, L, topk):
+    say(f"vsa select B{B} H{H} L{L} k{topk}")
+    q = synth.normal_f16(8, synth.TID_Q, (B, H, L, 128))
+    k = synth.normal_f16(8, synth.TID_K, (B, H, L, 128))
+    idx, s = lib.vsa_block_select(dev(q), dev(k), topk, scores=True)
+    torch.cuda.synchronize()
+    ref_idx, ref_s = oracle.vsa_select(q, k, 64, topk)
+    assert np.array_equal(s.cpu().numpy(), ref_s)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+
+
+def test_vsa_select_ties_take_lower_index(lib):
+    say("vsa select ties")
+    L = 64 * 40
+    q = np.ones((1, 1, L, 128), np.float16)
+    k = np.ones((1, 1, L, 128), np.float16)  # every block scores the same
+    idx = lib.vsa_block_select(dev(q), dev(k), 5)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy()[0, 0], np.broadcast_to(np.arange(5), (40, 5)))
+
+
+@pytest.mark.parametrize("L,topk,dp", [(2048, 8, 2), (64 * 20, 20, 0), (1024, 3, 16)])
+def test_vsa_sparse_attn_parity(lib, L, topk, dp):
+    say(f"vsa sparse L{L} k{topk} dp{dp}")
+    B, H, D = 1, 2, 128
+    q, k, v = qkv(10, B, H, H, L, L, D)
+    ref_idx, _ = oracle.vsa_select(q, k, 64, topk)
+    scale = lib.default_scale(D)
+    out = lib.vsa_block_sparse_attn(dev(q), dev(k), dev(v), dev(ref_idx), dense_prefix_qblocks=dp)
+    torch.cuda.synchronize()
+    ref, _ = oracle.attention(q, k, v, scale, mode=oracle.MODE_BLOCKS, idx=ref_idx, block=64, dense_prefix=dp)
+    assert_close(out.cpu().numpy().reshape(-1, D), ref, "O")
+
+
+def test_bitwise_repeatability_without_sync(lib):
+    """Three complete runs with no synchronisation in between give identical bits."""
+    say("repeatability")
+    q, k, v = (dev(x) for x in qkv(11, 1, 6, 1, 256, 4096, 256))
+    outs = [lib.attn_fwd_prefix_causal(q, k, v, 256) for _ in range(3)]
+    qd, kd, vd = (dev(x) for x in qkv(12, 1, 2, 2, 333, 777, 128))
+    dens = [lib.attn_fwd_dense(qd, kd, vd) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    for o in dens[1:]:
+        assert torch.equal(o, dens[0])
