@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP16 fused-attention forward hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--only NAME] [--no-cpu] [--no-extra]
+
+Headline (one step = one attn_fwd_dense launch over the whole workload): the
+dense non-causal D128 attention of a video diffusion transformer, B1 H8
+L36864, FP16 inputs N(0,1), FP32 accumulation, FP16 output. `value` is its
+algorithmic throughput, 4*D FLOP per (query, key) pair, in TFLOP/s.
+
+The same JSON line carries, under "extra", the other workloads of the hot
+path, each timed with HIP events on the launch stream:
+  * causal prefill D256 Hq6/Hkv1 Q8000 KV128000 (split-KV + merge), TFLOP/s
+    over the visible pairs only;
+  * the same prefill reading a paged E4M3 cache, KV256000, non-unit scales;
+  * the exact paged E4M3 -> FP16 bridge, GB/s over the bytes it must move;
+  * VSA block selection (pool, score, top-k), GB/s over Q and K read once
+    plus the indices written, and VSA block-sparse attention, TFLOP/s over
+    the selected pairs.
+HBM-bound kernels run after a 512 MiB buffer fill that evicts the 256 MB
+last-level cache, outside the timed events.
+
+"cpu_baseline" times the FP64 CPU oracle on a sample of query rows of the
+headline workload on this host's cores (a reported baseline, not a target),
+and "parity_sample" compares those rows with the GPU output.
+
+Only one GPU is supported: --gpus N with N > 1 exits with an error.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16 MFMA, published
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+METRIC = "attention TFLOP/s and % FP16 MFMA peak (D128 dense, D256 causal prefix)"
+
+
+def log(*msg):
+    print("[bench]", *msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ FLOP / byte accounting
+
+def dense_flops(w):
+    return 4 * w["D"] * w["B"] * w["H"] * w["Lq"] * w["Lkv"]
+
+
+def causal_flops(w):
+    """4*D per visible pair; query row i sees keys 0 .. (kv_len - q_real) + i."""
+    off = w["kv_len"] - w["q_real"]
+    vis = np.minimum(off + np.arange(w["q_rows"], dtype=np.int64) + 1, w["kv_len"])
+    return 4 * w["D"] * w["B"] * w["Hq"] * int(vis.sum())
+
+
+def vsa_flops(w):
+    nb, blk, dp = w["L"] // w["block"], w["block"], w["dense_prefix"]
+    pairs = dp * blk * w["L"] + (nb - dp) * blk * w["topk"] * blk
+    return 4 * w["D"] * w["B"] * w["H"] * pairs
+
+
+def bridge_bytes(w):
+    n = w["B"] * w["Hkv"] * w["kv_len"] * w["D"]
+    return 2 * n + 2 * 2 * n + 4 * (w["kv_len"] // w["page_size"]) * w["B"]
+
+
+def select_bytes(w):
+    nb = w["L"] // w["block"]
+    return 2 * 2 * w["B"] * w["H"] * w["L"] * w["D"] + 4 * w["B"] * w["H"] * nb * w["topk"]
+
+
+# ------------------------------------------------------------------------------ timing
+
+class Timer:
+    """HIP events around each launch on torch's current stream (the stream the
+    library enqueues on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, iters, warmup, flush=None):
+        torch = self.torch
+        for _ in range(warmup):
+            if flush is not None:
+                flush()
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        t0 = time.perf_counter()
+        for s, e in ev:
+            if flush is not None:
+                flush()
+            s.record()
+            fn()
+            e.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = np.array([s.elapsed_time(e) for s, e in ev])
+        return ms, wall
+
+
+def stats(ms):
+    return {"median_ms": float(np.median(ms)), "mean_ms": float(ms.mean()),
+            "cv": float(ms.std() / ms.mean()) if ms.mean() > 0 else 0.0}
+
+
+# --------------------------------------------------------------------------- workloads
+
+def bench_dense(fa, torch, W, steps, warmup, timer):
+    import synth.workloads as wl
+    w = wl.VIDEO_DENSE
+    log("generating", w["name"])
+    q, k, v = wl.dense_inputs(w)
+    dq, dk, dv = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    out = torch.empty_like(dq)
+    fn = lambda: fa.attn_fwd_dense(dq, dk, dv, out=out)
+    log(f"dense: warmup {warmup}, {steps} timed steps")
+    ms, wall = timer.run(fn, steps, warmup)
+    return w, (q, k, v), out, ms, wall
+
+
+def bench_causal(fa, torch, iters, timer):
+    import synth.workloads as wl
+    w = wl.PREFIX_CAUSAL
+    log("generating", w["name"])
+    q, k, v = wl.causal_inputs(w)
+    dq, dk, dv = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    del q, k, v
+    ws_bytes = fa.prefix_causal_workspace(w["B"], w["Hq"], w["Hkv"], w["D"], w["q_rows"], w["kv_len"])
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(dq)
+    fn = lambda: fa.attn_fwd_prefix_causal(dq, dk, dv, w["q_real"], out=out, workspace=ws)
+    ms, _ = timer.run(fn, iters, 2)
+    f = causal_flops(w)
+    tf = f / (np.median(ms) * 1e-3) / 1e12
+    log(f"causal: {np.median(ms):.3f} ms  {tf:.1f} TFLOP/s")
+    return {"workload": w["name"], "flop": f, **stats(ms), "tflops": tf,
+            "frac_mfma_peak": tf / MFMA_F16_PEAK_TFLOPS, "workspace_bytes": ws_bytes,
+            "kernels": "attn split-KV + merge"}
+
+
+def bench_paged(fa, torch, iters, timer, flush):
+    import synth.workloads as wl
+    w = wl.PAGED_E4M3
+    log("generating", w["name"])
+    q, kc, vc, table, ks, vs = wl.paged_inputs(w, unit_scales=False)
+    dq, dkc, dvc, dt = (torch.from_numpy(x).cuda() for x in (q, kc, vc, table))
+    del q, kc, vc
+    ws_bytes = fa.prefix_causal_workspace(w["B"], w["Hq"], w["Hkv"], w["D"], w["q_rows"], w["kv_len"])
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(dq)
+    fn = lambda: fa.attn_fwd_paged_e4m3(dq, dkc, dvc, dt, w["kv_len"], w["q_real"], ks, vs, out=out,
+                                        workspace=ws)
+    ms, _ = timer.run(fn, iters, 2)
+    f = causal_flops(w)
+    tf = f / (np.median(ms) * 1e-3) / 1e12
+    log(f"paged e4m3: {np.median(ms):.3f} ms  {tf:.1f} TFLOP/s")
+    fused = {"workload": w["name"] + f" k_scale={ks:.6g} v_scale={vs:.6g}", "flop": f, **stats(ms),
+             "tflops": tf, "frac_mfma_peak": tf / MFMA_F16_PEAK_TFLOPS}
+
+    ko = torch.empty((w["B"], w["Hkv"], w["kv_len"], w["D"]), dtype=torch.float16, device="cuda")
+    vo = torch.empty_like(ko)
+    fn = lambda: fa.kv_e4m3_paged_to_fp16(dkc, dvc, dt, w["B"], w["kv_len"], ks, vs, k_out=ko, v_out=vo)
+    ms, _ = timer.run(fn, iters, 2, flush=flush)
+    nb = bridge_bytes(w)
+    gbs = nb / (np.median(ms) * 1e-3) / 1e9
+    log(f"bridge: {np.median(ms) * 1e3:.1f} us  {gbs:.0f} GB/s")
+    bridge = {"workload": "exact paged E4M3 -> FP16 bridge, K and V, KV256000 D256 page32", "bytes": nb,
+              **stats(ms), "gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS, "llc_flushed": True}
+    return fused, bridge
+
+
+def bench_vsa(fa, torch, iters, timer, flush):
+    import synth.workloads as wl
+    w = wl.VSA
+    log("generating", w["name"])
+    q, k, v = wl.vsa_inputs(w)
+    dq, dk, dv = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    del q, k, v
+    nb = w["L"] // w["block"]
+    idx = torch.empty((w["B"], w["H"], nb, w["topk"]), dtype=torch.int32, device="cuda")
+    ws = torch.empty(fa.load().vsa_block_select_workspace(w["B"], w["H"], w["L"], w["D"], w["block"]),
+                     dtype=torch.uint8, device="cuda")
+    sel = lambda: fa.vsa_block_select(dq, dk, w["topk"], block=w["block"], workspace=ws, out=idx)
+    ms_s, _ = timer.run(sel, iters, 2, flush=flush)
+    sb = select_bytes(w)
+    gbs = sb / (np.median(ms_s) * 1e-3) / 1e9
+    log(f"vsa select: {np.median(ms_s) * 1e3:.1f} us  {gbs:.0f} GB/s")
+    out = torch.empty_like(dq)
+    att = lambda: fa.vsa_block_sparse_attn(dq, dk, dv, idx, dense_prefix_qblocks=w["dense_prefix"],
+                                           block=w["block"], out=out)
+    ms_a, _ = timer.run(att, iters, 2)
+    f = vsa_flops(w)
+    tf = f / (np.median(ms_a) * 1e-3) / 1e12
+    log(f"vsa sparse: {np.median(ms_a):.3f} ms  {tf:.1f} TFLOP/s")
+    return ({"workload": w["name"] + " (pool + FP64 block scores + top-k)", "bytes": sb, **stats(ms_s),
+             "gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS, "llc_flushed": True},
+            {"workload": w["name"] + " (sparse attention)", "flop": f, **stats(ms_a), "tflops": tf,
+             "frac_mfma_peak": tf / MFMA_F16_PEAK_TFLOPS,
+             "selected_fraction_of_dense": f / (4 * w["D"] * w["B"] * w["H"] * w["L"] * w["L"])})
+
+
+# -------------------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(w, qkv, out_gpu, rows_per_head):
+    """Time the FP64 oracle on a seeded sample of query rows of the headline
+    workload and compare the GPU output on those rows."""
+    import oracle
+    q, k, v = qkv
+    rng = np.random.default_rng(1234)
+    rows = []
+    for h in range(w["H"]):
+        sel = {0, w["Lq"] - 1, *rng.integers(0, w["Lq"], rows_per_head - 2).tolist()}
+        rows += [(0, h, i) for i in sorted(sel)]
+    rows = np.array(rows, dtype=np.int32)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    oracle.build()
+    log(f"cpu oracle: {len(rows)} rows on {threads} threads")
+    t0 = time.perf_counter()
+    ref, _ = oracle.attention(q, k, v, float(np.float32(1.0 / np.sqrt(w["D"]))), rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    flop = 4 * w["D"] * w["Lkv"] * len(rows)
+    got = out_gpu[rows[:, 0], rows[:, 1], rows[:, 2]].astype(np.float64)
+    err = got - ref
+    parity = {"rows": int(len(rows)), "max_abs": float(np.abs(err).max()),
+              "rel_l2": float(np.linalg.norm(err) / np.linalg.norm(ref))}
+    cpu = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"{len(rows)} query rows ({rows_per_head} per head, seeded) of the headline workload, "
+                     f"each against all {w['Lkv']} keys, FP64; {dt:.2f} s wall",
+           "seconds": dt}
+    return cpu, parity
+
+
+# --------------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--iters", type=int, default=10, help="timed launches of each extra workload")
+    ap.add_argument("--only", choices=["dense", "causal", "paged", "vsa"], default=None,
+                    help="run one workload only (for profiling)")
+    ap.add_argument("--no-extra", action="store_true", help="skip the non-headline workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=128, help="oracle rows per head for cpu_baseline")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch of the dense kernel (from rocprofv3 PMC runs)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the attention path has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fp16_attention_amd as fa
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(2)
+    fa.load()  # raises if the HIP library is not built
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+    timer = Timer(torch)
+    flush_buf = None
+
+    def flush():
+        flush_buf.zero_()
+
+    extra = {}
+    result = None
+    if args.only in (None, "dense"):
+        w, qkv, out, ms, wall = bench_dense(fa, torch, None, args.steps, args.warmup, timer)
+        flop = dense_flops(w)
+        avg_ms = float(ms.mean())
+        value = flop * args.steps / wall / 1e12
+        achieved = flop / (avg_ms * 1e-3) / 1e12
+        log(f"dense: {avg_ms:.3f} ms/launch (events), {wall / args.steps * 1e3:.3f} ms/step (wall), "
+            f"{achieved:.1f} TFLOP/s = {100 * achieved / MFMA_F16_PEAK_TFLOPS:.1f}% of peak")
+        traffic = None
+        if os.path.exists(args.traffic):
+            with open(args.traffic) as f:
+                t = json.load(f)
+            traffic = t.get("attn_fwd_dense_video", None)
+        result = {
+            "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+            "config": {"workload": w["name"], "B": w["B"], "H": w["H"], "D": w["D"], "Lq": w["Lq"],
+                       "Lkv": w["Lkv"], "causal": False, "scale": "1/sqrt(128) in FP32",
+                       "inputs": "N(0,1) FP16, counter-based generator seed 2"},
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": traffic,
+                         "kernel": "attn_fwd_kernel (dense, D128)", "launch_ms_mean": avg_ms,
+                         "algorithmic_flop_per_launch": flop},
+        }
+        result["headline_stats"] = stats(ms)
+        if not args.no_cpu:
+            out_np = out.cpu().numpy()
+            cpu, parity = cpu_baseline(w, qkv, out_np, args.cpu_rows)
+            result["cpu_baseline"] = cpu
+            result["parity_sample"] = parity
+            log(f"cpu oracle {cpu['value'] * 1e3:.3f} GFLOP/s; GPU vs oracle on the sample: {parity}")
+        del qkv, out
+        torch.cuda.empty_cache()
+
+    if not args.no_extra or args.only not in (None, "dense"):
+        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        if args.only in (None, "causal"):
+            extra["prefix_causal"] = bench_causal(fa, torch, args.iters, timer)
+            torch.cuda.empty_cache()
+        if args.only in (None, "paged"):
+            extra["paged_e4m3"], extra["e4m3_bridge"] = bench_paged(fa, torch, args.iters, timer, flush)
+            torch.cuda.empty_cache()
+        if args.only in (None, "vsa"):
+            extra["vsa_select"], extra["vsa_sparse_attn"] = bench_vsa(fa, torch, args.iters, timer, flush)
+            torch.cuda.empty_cache()
+
+    if result is None:
+        print(json.dumps({"metric": METRIC, "partial": True, "only": args.only, "extra": extra}), flush=True)
+        return
+    result["extra"] = extra
+    result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                        "compute_units": props.multi_processor_count}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

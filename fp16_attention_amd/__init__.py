@@ -202,15 +202,19 @@ def kv_e4m3_paged_to_fp16(k_cache, v_cache, page_table, B, kv_len, k_scale=1.0, 
 
 # ---------------------------------------------------------------------------------- VSA
 
-def vsa_block_select(q, k, topk, block=64, scores=False, workspace=None):
+def vsa_block_select(q, k, topk, block=64, scores=False, workspace=None, out=None):
     """Top-k KV blocks per query block. Returns idx int32 [B,H,NB,topk] (and FP64 scores if asked)."""
     import torch
-    _need_cuda(q, k)
+    _need_cuda(q, k, out)
     if not (q.is_contiguous() and k.is_contiguous()):
         raise ValueError("q and k must be contiguous")
     B, H, L, D = q.shape
     NB = L // block
-    idx = torch.empty((B, H, NB, topk), dtype=torch.int32, device=q.device)
+    idx = out
+    if idx is None:
+        idx = torch.empty((B, H, NB, topk), dtype=torch.int32, device=q.device)
+    elif tuple(idx.shape) != (B, H, NB, topk) or idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError("out must be a contiguous int32 [B, H, L/block, topk] tensor")
     s = torch.empty((B, H, NB, NB), dtype=torch.float64, device=q.device) if scores else None
     ws = _workspace(int(load().vsa_block_select_workspace(B, H, L, D, block)), q.device, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()

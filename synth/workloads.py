@@ -1,0 +1,75 @@
+"""The five seeded synthetic workloads of the attention hot path (shapes and
+seeds only; no attention arithmetic).
+
+Shapes follow the pages' workloads:
+  * dense non-causal D128 attention of a video diffusion transformer, one
+    GPU's share of heads ("[Kernel] Share SM70 projection, attention and row
+    reduction paths", Purpose);
+  * the long causal D256 GQA prefill against a prefix KV, Hq6/Hkv1, Q8000,
+    KV 128000 and 256000, paged E4M3 cache with 32-token pages ("[Kernel][SM70]
+    Integrate FP32 v37 prefill and exact E4M3 bridge", Implementation and
+    Test plan);
+  * VSA block-sparse video attention, top-k = 64 of 64-token blocks with two
+    dense prefix query blocks ("[Video] Integrate H3 SM70 execution, metrics
+    and VSA diagnostics", Purpose).
+Values are N(0,1) FP16 draws from synth's counter-based generator with
+seed = workload number and tensor ids Q=1, K=2, V=3, page table=4, scales=5.
+"""
+from __future__ import annotations
+
+from . import TID_K, TID_Q, TID_SCALES, TID_TABLE, TID_V, e4m3_codes, normal_f16, permutation, uniform_f32
+
+TINY_DENSE = dict(name="tiny dense attention B1 H2 D128 L256 non-causal", seed=1, B=1, H=2, D=128,
+                  Lq=256, Lkv=256)
+VIDEO_DENSE = dict(name="video-DiT dense attention B1 H8 D128 L36864 non-causal", seed=2, B=1, H=8,
+                   D=128, Lq=36864, Lkv=36864)
+PREFIX_CAUSAL = dict(name="causal prefill B1 Hq6 Hkv1 D256 Q8000 KV128000 (prefix 120000)", seed=3, B=1,
+                     Hq=6, Hkv=1, D=256, q_rows=8000, q_real=8000, kv_len=128000)
+PAGED_E4M3 = dict(name="paged E4M3 causal prefill B1 Hq6 Hkv1 D256 Q8000 KV256000 page32", seed=4, B=1,
+                  Hq=6, Hkv=1, D=256, q_rows=8000, q_real=8000, kv_len=256000, page_size=32)
+VSA = dict(name="VSA block-sparse attention B1 H8 D128 L36864 block64 top-k 64 dense-prefix 2", seed=5,
+           B=1, H=8, D=128, L=36864, block=64, topk=64, dense_prefix=2)
+
+
+def dense_inputs(w):
+    s = w["seed"]
+    q = normal_f16(s, TID_Q, (w["B"], w["H"], w["Lq"], w["D"]))
+    k = normal_f16(s, TID_K, (w["B"], w["H"], w["Lkv"], w["D"]))
+    v = normal_f16(s, TID_V, (w["B"], w["H"], w["Lkv"], w["D"]))
+    return q, k, v
+
+
+def causal_inputs(w):
+    s = w["seed"]
+    q = normal_f16(s, TID_Q, (w["B"], w["Hq"], w["q_rows"], w["D"]))
+    k = normal_f16(s, TID_K, (w["B"], w["Hkv"], w["kv_len"], w["D"]))
+    v = normal_f16(s, TID_V, (w["B"], w["Hkv"], w["kv_len"], w["D"]))
+    return q, k, v
+
+
+def paged_scales(w, unit: bool):
+    """(k_scale, v_scale): 1.0 each, or U(0.01, 0.1) draws rounded to FP32."""
+    if unit:
+        return 1.0, 1.0
+    ks, vs = uniform_f32(w["seed"], TID_SCALES, 0.01, 0.1, 2)
+    return float(ks), float(vs)
+
+
+def paged_inputs(w, unit_scales: bool):
+    """q FP16, E4M3 caches uint8 [pages, 32, Hkv, D], page table int32 [B, pages] (a
+    permutation of the physical pages), and the two scales. The cache holds
+    RNE_e4m3(x / scale) for x ~ N(0,1), so decode(code) * scale ~ N(0,1)."""
+    s = w["seed"]
+    ks, vs = paged_scales(w, unit_scales)
+    pages = w["B"] * w["kv_len"] // w["page_size"]
+    q = normal_f16(s, TID_Q, (w["B"], w["Hq"], w["q_rows"], w["D"]))
+    kc = e4m3_codes(s, TID_K, (pages, w["page_size"], w["Hkv"], w["D"]), ks)
+    vc = e4m3_codes(s, TID_V, (pages, w["page_size"], w["Hkv"], w["D"]), vs)
+    table = permutation(s, TID_TABLE, pages).reshape(w["B"], -1).copy()
+    return q, kc, vc, table, ks, vs
+
+
+def vsa_inputs(w):
+    s = w["seed"]
+    shape = (w["B"], w["H"], w["L"], w["D"])
+    return normal_f16(s, TID_Q, shape), normal_f16(s, TID_K, shape), normal_f16(s, TID_V, shape)
