@@ -1,0 +1,89 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py
+times (same entry points, shapes and split plans), on sampled outputs the
+FP64 oracle computes one row at a time; E4M3 conversion and block indices
+are compared bit-exactly over the whole output (marked gpu)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth.workloads as wl
+from parity_util import LSE_ABS, assert_close, sample_rows, say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _rows_of(out_np, rows):
+    return out_np[rows[:, 0], rows[:, 1], rows[:, 2]].astype(np.float64)
+
+
+def test_video_dense_full(lib):
+    w = wl.VIDEO_DENSE
+    say("full dense", w["name"])
+    q, k, v = wl.dense_inputs(w)
+    lse = torch.empty((w["B"], w["H"], w["Lq"]), dtype=torch.float32, device="cuda")
+    out = lib.attn_fwd_dense(dev(q), dev(k), dev(v), lse=lse)
+    torch.cuda.synchronize()
+    rows = sample_rows(w["B"], w["H"], w["Lq"], 24, seed=2)
+    ref, ref_lse = oracle.attention(q, k, v, lib.default_scale(w["D"]), rows=rows)
+    assert_close(_rows_of(out.cpu().numpy(), rows), ref, f"O ({len(rows)} rows)")
+    got_lse = lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert np.abs(got_lse - ref_lse).max() < LSE_ABS
+
+
+def test_prefix_causal_full(lib):
+    w = wl.PREFIX_CAUSAL
+    say("full causal", w["name"])
+    q, k, v = wl.causal_inputs(w)
+    lse = torch.empty((w["B"], w["Hq"], w["q_rows"]), dtype=torch.float32, device="cuda")
+    out = lib.attn_fwd_prefix_causal(dev(q), dev(k), dev(v), w["q_real"], lse=lse)
+    torch.cuda.synchronize()
+    rows = sample_rows(w["B"], w["Hq"], w["q_rows"], 12, seed=3, tile=2048)
+    ref, ref_lse = oracle.attention(q, k, v, lib.default_scale(w["D"]), mode=oracle.MODE_CAUSAL,
+                                    offset=w["kv_len"] - w["q_real"], rows=rows)
+    assert_close(_rows_of(out.cpu().numpy(), rows), ref, f"O ({len(rows)} rows)")
+    got_lse = lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert np.abs(got_lse - ref_lse).max() < LSE_ABS
+
+
+@pytest.mark.parametrize("unit_scales", [True, False])
+def test_paged_e4m3_full(lib, unit_scales):
+    w = wl.PAGED_E4M3
+    q, kc, vc, table, ks, vs = wl.paged_inputs(w, unit_scales)
+    say("full paged", w["name"], "scales", ks, vs)
+    dq, dkc, dvc, dt = dev(q), dev(kc), dev(vc), dev(table)
+    out = lib.attn_fwd_paged_e4m3(dq, dkc, dvc, dt, w["kv_len"], w["q_real"], ks, vs)
+    ko, vo = lib.kv_e4m3_paged_to_fp16(dkc, dvc, dt, w["B"], w["kv_len"], ks, vs)
+    torch.cuda.synchronize()
+    # the bridge, bit-exact over every converted element
+    kf = oracle.e4m3_to_f16(oracle.paged_gather(kc, table, w["kv_len"]), ks)
+    vf = oracle.e4m3_to_f16(oracle.paged_gather(vc, table, w["kv_len"]), vs)
+    assert np.array_equal(ko.cpu().numpy().view(np.uint16), kf), "bridge K bits differ"
+    assert np.array_equal(vo.cpu().numpy().view(np.uint16), vf), "bridge V bits differ"
+    del ko, vo
+    rows = sample_rows(w["B"], w["Hq"], w["q_rows"], 8, seed=4, tile=2048)
+    ref, _ = oracle.attention(q, kf.view(np.float16), vf.view(np.float16), lib.default_scale(w["D"]),
+                              mode=oracle.MODE_CAUSAL, offset=w["kv_len"] - w["q_real"], rows=rows)
+    assert_close(_rows_of(out.cpu().numpy(), rows), ref, f"O ({len(rows)} rows)")
+
+
+def test_vsa_full(lib):
+    w = wl.VSA
+    say("full vsa", w["name"])
+    q, k, v = wl.vsa_inputs(w)
+    dq, dk, dv = dev(q), dev(k), dev(v)
+    idx = lib.vsa_block_select(dq, dk, w["topk"], block=w["block"])
+    torch.cuda.synchronize()
+    ref_idx, _ = oracle.vsa_select(q, k, w["block"], w["topk"])
+    assert np.array_equal(idx.cpu().numpy(), ref_idx), "selected blocks differ"
+    out = lib.vsa_block_sparse_attn(dq, dk, dv, idx, dense_prefix_qblocks=w["dense_prefix"], block=w["block"])
+    torch.cuda.synchronize()
+    # dense prefix rows (query blocks 0-1) and sparse rows
+    rows = sample_rows(w["B"], w["H"], w["L"], 16, seed=5, extra=(63, 64, 127, 128))
+    ref, _ = oracle.attention(q, k, v, lib.default_scale(w["D"]), mode=oracle.MODE_BLOCKS, idx=ref_idx,
+                              block=w["block"], dense_prefix=w["dense_prefix"], rows=rows)
+    assert_close(_rows_of(out.cpu().numpy(), rows), ref, f"O ({len(rows)} rows)")
