@@ -14,23 +14,37 @@
 //     VSA diagnostics", Purpose).
 //
 // Work decomposition (MI355X-first, not the pages' SM70/SM121 designs):
-//   - A workgroup owns WAVES x 32 query rows of one (batch, head) and streams
-//     64-key tiles of K and V through LDS, double-buffered: tile t+1 is loaded
-//     from HBM/L2 into registers while tile t is consumed from LDS.
+//   - A workgroup owns WAVES x 32 query rows of one (batch, head); every wave
+//     keeps its 32 query rows in registers as the MFMA B operand and streams
+//     64-key tiles of K and V through LDS.
+//   - LDS holds two K slots and two V slots. FP16 tiles move from HBM/L2 into
+//     LDS with buffer_load ... lds (no register staging; rows past the end of
+//     the key range read as zero through the buffer range check). E4M3 tiles
+//     are loaded into registers, decoded exactly to FP16 and written to LDS.
+//     K and V are stored row-major with 16-byte chunks XOR-swizzled by the
+//     row, which keeps the K operand reads and the transposing V reads free of
+//     bank conflicts.
 //   - Scores are computed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_f16: the MFMA result puts one query per lane
-//     (lane % 32) and 16 keys per lane, so the row max and row sum need only
-//     in-lane work plus one exchange between the two lane halves.
-//   - The output is also kept transposed, O^T = V^T P^T, so the per-query
-//     rescale factor is a per-lane scalar. P never leaves registers: the
-//     score accumulator registers are exactly the B operand of the PV MFMA
-//     once the V^T tile in LDS stores each 16-key group in the matching
-//     permuted key order.
-//   - The softmax runs in base 2 with the scale folded into one FP32 factor
-//     c = scale * log2(e), so each probability is one FMA and one v_exp_f32.
+//     v_mfma_f32_32x32x16_f16: each lane owns one query (lane % 32) and 16
+//     keys per 32-key block, so the row max and row sum are in-lane work plus
+//     one exchange between the two lane halves.
+//   - The output is kept transposed too, O^T = V^T P^T. The V^T operand comes
+//     straight from the row-major V tile with ds_read_b64_tr_b16, and P never
+//     leaves registers: the score accumulators are the B operand once each
+//     16-key group is read in the matching key order.
+//   - The scores of tile t+1 are issued on the matrix cores before the softmax
+//     of tile t runs on the VALU, so the two overlap inside a wave.
+//   - The softmax runs in base 2 with c = scale * log2(e) folded into one FMA.
+//     The running maximum is only raised when a score exceeds it by more than
+//     2^8, so the O accumulators are rescaled a handful of times per row
+//     instead of every tile; P then stays below 2^8, exact in FP16 range, and
+//     the normalisation divides by the sum of the same FP16 probabilities that
+//     multiply V.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "fa_internal.h"
 
@@ -39,39 +53,49 @@ namespace fa {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef short s4 __attribute__((ext_vector_type(4)));
 typedef float f16x __attribute__((ext_vector_type(16)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s4 lds_s4_t;
 
-// LDS layout of one stage (K tile + V^T tile), in FP16 elements.
-//   K   [64 keys][D + 8]: rows padded by 16 bytes so the 32 rows one MFMA
-//       operand read touches spread over all banks.
-//   V^T [D][64 keys]: 16-byte chunks of each row XOR-swizzled by
-//       (d + d/8) mod 8, which keeps both the transposing writes (8 rows d
-//       apart) and the operand reads (32 consecutive rows) free of bank
-//       conflicts. Within each 16-key group the keys are stored in the order
-//       0-3, 8-11, 4-7, 12-15 (see vt_pos).
+// Word 3 of a raw buffer resource (32-bit data, no swizzle) on the gfx9 family.
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+// The running maximum (log2 units) is raised only when exceeded by this much.
+constexpr float kRescaleSlack = 8.0f;
+
+#ifndef FA_NO_SCHED_HINTS
+#define SCHED_GROUP(mask, n, id) __builtin_amdgcn_sched_group_barrier(mask, n, id)
+#else
+#define SCHED_GROUP(mask, n, id) ((void)0)
+#endif
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt in [3:0] and [15:14], expcnt in
+// [6:4], lgkmcnt in [11:8].
+constexpr int kWaitVm0 = 0x0F70;
+
+// ---------------------------------------------------------------------------
+// LDS tile layout: 64 rows (keys) of D FP16, row-major, 2*D bytes per row;
+// 16-byte chunk c of row r sits at position c ^ swz(r % 16).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 template <int D>
-struct Lds {
-    static constexpr int kKStride = D + 8;
-    static constexpr int kKElems = kTileN * kKStride;
-    static constexpr int kVtElems = D * kTileN;
-    static constexpr int kStage = kKElems + kVtElems;
-    static constexpr int kElems = 2 * kStage;
-};
-
-__device__ __forceinline__ int vt_swz(int d) { return (d + (d >> 3)) & 7; }
-
-// Element offset of (row d, 8-key chunk c) in the swizzled V^T tile.
-__device__ __forceinline__ int vt_chunk(int d, int c) { return d * kTileN + ((c ^ vt_swz(d)) << 3); }
+__device__ __forceinline__ int tile_off(int row, int chunk)
+{
+    return row * (2 * D) + ((chunk ^ swz(row & 15)) << 4);
+}
 
 __device__ __forceinline__ float wave_half_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float wave_half_sum(float x) { return x + __shfl_xor(x, 32); }
 
-// Pack the low (sel = 0) or high (sel = 1) FP16 halves of two dwords.
-__device__ __forceinline__ uint32_t pack_halves(uint32_t lo_src, uint32_t hi_src, int sel)
+// Three-input maximum in one instruction (fmaxf chains are emitted with extra
+// NaN-quieting operations).
+__device__ __forceinline__ float vmax3(float a, float b, float c)
 {
-    return __builtin_amdgcn_perm(hi_src, lo_src, sel ? 0x07060302u : 0x05040100u);
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
 }
 
 // Four E4M3 bytes -> four FP16 values, exactly (scale 1: every E4M3 value is
@@ -87,144 +111,83 @@ __device__ __forceinline__ u2 e4m3x4_to_f16(uint32_t w)
 }
 
 // ---------------------------------------------------------------------------
-// Global -> register -> LDS staging of one 64-key tile.
+// FP16 tiles: buffer_load_dwordx4 ... lds. Wave w's j-th load writes the
+// 1 KB block (w + WAVES * j) of the tile; lane i of it writes bytes
+// [16 i, 16 i + 16) of that block, so each lane loads the global chunk that
+// belongs at that LDS position.
 // ---------------------------------------------------------------------------
-template <int D, int SRC, int NT>
-struct Stager;
+template <int D, int WAVES>
+struct DirectLoader {
+    static constexpr int kLoads = (kTileN * D * 2 / 1024) / WAVES;  // per wave per tile
+    int koff[kLoads];
+    int voff[kLoads];
 
-// FP16 K/V rows.
-template <int D, int NT>
-struct Stager<D, KV_FP16, NT> {
-    static constexpr int kKChunks = kTileN * D / 8 / NT;   // 16-byte K chunks per thread
-    static constexpr int kVTasks = (kTileN / 4) * (D / 8) / NT;  // 4 keys x 8 d per task
-    u4 kr[kKChunks];
-    u4 vr[kVTasks][4];
-
-    __device__ __forceinline__ void load(const AttnArgs& a, const _Float16* kbase,
-                                         const _Float16* vbase, int key0, int key_last, int tid)
+    __device__ __forceinline__ void init(int64_t k_ss, int64_t v_ss, int wave, int lane)
     {
 #pragma unroll
-        for (int i = 0; i < kKChunks; ++i) {
-            int c = tid + NT * i;
-            int row = c / (D / 8), col = c % (D / 8);
-            int key = min(key0 + row, key_last);
-            kr[i] = *(const u4*)(kbase + (int64_t)key * a.k_ss + col * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < kVTasks; ++i) {
-            int t = tid + NT * i;
-            int grp = t / (D / 8), col = t % (D / 8);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                int key = min(key0 + 4 * grp + j, key_last);
-                vr[i][j] = *(const u4*)(vbase + (int64_t)key * a.v_ss + col * 8);
-            }
+        for (int j = 0; j < kLoads; ++j) {
+            const int byte = (wave + WAVES * j) * 1024 + lane * 16;
+            const int row = byte / (2 * D);
+            const int pos = (byte % (2 * D)) >> 4;
+            const int chunk = pos ^ swz(row & 15);
+            koff[j] = (int)(((int64_t)row * k_ss + chunk * 8) * 2);
+            voff[j] = (int)(((int64_t)row * v_ss + chunk * 8) * 2);
         }
     }
 
-    __device__ __forceinline__ void store(_Float16* ks, _Float16* vt, int tid) const
+    // rows: number of valid rows from key0 (the rest read as zero)
+    static __device__ __forceinline__ void issue(const _Float16* base, int64_t ss, const int* off,
+                                                 int rows, unsigned char* tile, int wave)
     {
+        __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, rows * (int)ss * 2, kRsrcWord3);
 #pragma unroll
-        for (int i = 0; i < kKChunks; ++i) {
-            int c = tid + NT * i;
-            int row = c / (D / 8), col = c % (D / 8);
-            *(u4*)(ks + row * Lds<D>::kKStride + col * 8) = kr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < kVTasks; ++i) {
-            int t = tid + NT * i;
-            int grp = t / (D / 8), col = t % (D / 8);
-            store_vt(vt, grp, col, vr[i][0], vr[i][1], vr[i][2], vr[i][3]);
-        }
-    }
-
-    // Rows 4*grp..4*grp+3 (keys) x columns 8*col..8*col+7 (d) -> V^T.
-    static __device__ __forceinline__ void store_vt(_Float16* vt, int grp, int col, u4 r0, u4 r1,
-                                                    u4 r2, u4 r3)
-    {
-        // key group of 4 -> position inside its 16-key group: 0, 8, 4, 12
-        int chunk = 2 * (grp >> 2) + (grp & 1);
-        int within = (grp & 2) ? 4 : 0;
-        uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
-        uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
-        uint32_t w2[4] = {r2.x, r2.y, r2.z, r2.w};
-        uint32_t w3[4] = {r3.x, r3.y, r3.z, r3.w};
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-            int d = col * 8 + dd;
-            u2 val;
-            val.x = pack_halves(w0[dd >> 1], w1[dd >> 1], dd & 1);
-            val.y = pack_halves(w2[dd >> 1], w3[dd >> 1], dd & 1);
-            *(u2*)(vt + vt_chunk(d, chunk) + within) = val;
-        }
+        for (int j = 0; j < kLoads; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (lds_void_t*)(tile + (wave + WAVES * j) * 1024), 16, off[j], 0, 0, 0);
     }
 };
 
-// Paged E4M3 K/V rows: raw bytes are staged in registers and decoded to FP16
-// when written to LDS.
+// ---------------------------------------------------------------------------
+// Paged E4M3 tiles: 16-code chunks loaded into registers, decoded to FP16 and
+// written to LDS as two 16-byte chunks. Thread tid handles chunks
+// tid + NT * i of the tile (row = chunk / (D/16), 16-code column chunk % (D/16)).
+// ---------------------------------------------------------------------------
 template <int D, int NT>
-struct Stager<D, KV_E4M3_PAGED, NT> {
-    static constexpr int kKChunks = kTileN * D / 16 / NT;  // 16-byte (16-code) K chunks
-    static constexpr int kVTasks = (kTileN / 4) * (D / 8) / NT;
-    u4 kr[kKChunks];
-    u2 vr[kVTasks][4];
+struct E4m3 {
+    static constexpr int kChunks = kTileN * D / 16 / NT;  // per thread per K or V tile
 
-    static __device__ __forceinline__ const uint8_t* row_ptr(const AttnArgs& a, const uint8_t* cache,
-                                                             const int32_t* table, int g, int key)
+    static __device__ __forceinline__ void load(const AttnArgs& a, const uint8_t* cache,
+                                                const int32_t* table, int g, int key0, int key_last,
+                                                int tid, u4 (&dst)[kChunks])
     {
-        int page = table[key >> a.page_shift];
-        page = min(max(page, 0), a.num_pages - 1);
-        int slot = key & ((1 << a.page_shift) - 1);
-        return cache + (((int64_t)page << a.page_shift) + slot) * ((int64_t)a.Hkv * D) + (int64_t)g * D;
-    }
-
-    __device__ __forceinline__ void load(const AttnArgs& a, const int32_t* table, int g, int key0,
-                                         int key_last, int tid)
-    {
+        const int pi0 = key0 >> 5;
+        const int pi1 = min(pi0 + 1, key_last >> 5);
+        const int p0 = min(max(table[pi0], 0), a.num_pages - 1);
+        const int p1 = min(max(table[pi1], 0), a.num_pages - 1);
+        const int cache_bytes = a.num_pages * 32 * a.Hkv * D;
+        __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)cache, 0, cache_bytes, kRsrcWord3);
 #pragma unroll
-        for (int i = 0; i < kKChunks; ++i) {
-            int c = tid + NT * i;
-            int row = c / (D / 16), col = c % (D / 16);
-            int key = min(key0 + row, key_last);
-            kr[i] = *(const u4*)(row_ptr(a, a.kc, table, g, key) + col * 16);
-        }
-#pragma unroll
-        for (int i = 0; i < kVTasks; ++i) {
-            int t = tid + NT * i;
-            int grp = t / (D / 8), col = t % (D / 8);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                int key = min(key0 + 4 * grp + j, key_last);
-                vr[i][j] = *(const u2*)(row_ptr(a, a.vc, table, g, key) + col * 8);
-            }
+        for (int i = 0; i < kChunks; ++i) {
+            const int c = tid + NT * i;
+            const int row = c / (D / 16), c16 = c % (D / 16);
+            const int page = row < 32 ? p0 : p1;
+            const int off = ((page * 32 + (row & 31)) * a.Hkv + g) * D + c16 * 16;
+            dst[i] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
         }
     }
 
-    __device__ __forceinline__ void store(_Float16* ks, _Float16* vt, int tid) const
+    static __device__ __forceinline__ void store(unsigned char* tile, const u4 (&src)[kChunks], int tid)
     {
 #pragma unroll
-        for (int i = 0; i < kKChunks; ++i) {
-            int c = tid + NT * i;
-            int row = c / (D / 16), col = c % (D / 16);
-            u2 a0 = e4m3x4_to_f16(kr[i].x), a1 = e4m3x4_to_f16(kr[i].y);
-            u2 a2 = e4m3x4_to_f16(kr[i].z), a3 = e4m3x4_to_f16(kr[i].w);
-            u4 lo = {a0.x, a0.y, a1.x, a1.y};
-            u4 hi = {a2.x, a2.y, a3.x, a3.y};
-            _Float16* dst = ks + row * Lds<D>::kKStride + col * 16;
-            *(u4*)dst = lo;
-            *(u4*)(dst + 8) = hi;
-        }
-#pragma unroll
-        for (int i = 0; i < kVTasks; ++i) {
-            int t = tid + NT * i;
-            int grp = t / (D / 8), col = t % (D / 8);
-            u4 rows[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                u2 x = e4m3x4_to_f16(vr[i][j].x), y = e4m3x4_to_f16(vr[i][j].y);
-                rows[j] = u4{x.x, x.y, y.x, y.y};
-            }
-            Stager<D, KV_FP16, NT>::store_vt(vt, grp, col, rows[0], rows[1], rows[2], rows[3]);
+        for (int i = 0; i < kChunks; ++i) {
+            const int c = tid + NT * i;
+            const int row = c / (D / 16), c16 = c % (D / 16);
+            const u4 w = src[i];
+            const u2 a0 = e4m3x4_to_f16(w.x), a1 = e4m3x4_to_f16(w.y);
+            const u2 a2 = e4m3x4_to_f16(w.z), a3 = e4m3x4_to_f16(w.w);
+            *(u4*)(tile + tile_off<D>(row, 2 * c16)) = u4{a0.x, a0.y, a1.x, a1.y};
+            *(u4*)(tile + tile_off<D>(row, 2 * c16 + 1)) = u4{a2.x, a2.y, a3.x, a3.y};
         }
     }
 };
@@ -233,12 +196,18 @@ struct Stager<D, KV_E4M3_PAGED, NT> {
 // The attention kernel.
 // ---------------------------------------------------------------------------
 template <int D, int WAVES, int SRC, int MODE, bool SPLIT>
-__global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(const AttnArgs a)
+__global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kernel(const AttnArgs a)
 {
+    constexpr int NT = WAVES * 64;
     constexpr int M = WAVES * kRowsPerWave;
     constexpr int KK = D / 16;  // MFMA k-steps over D for S
     constexpr int DB = D / 32;  // 32-wide d blocks of O^T
-    __shared__ __attribute__((aligned(16))) _Float16 lds[Lds<D>::kElems];
+    constexpr int TB = kTileN * D * 2;
+    constexpr int ROW = 2 * D;  // bytes per LDS row
+    __shared__ __attribute__((aligned(1024))) unsigned char kslot0[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kslot1[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char vslot0[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char vslot1[TB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -319,16 +288,37 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(const AttnArgs a)
         return (tile_begin + it) * kTileN;
     };
 
-    // ---- pointers ------------------------------------------------------------
+    // ---- K/V sources -----------------------------------------------------
     const _Float16* kbase = nullptr;
     const _Float16* vbase = nullptr;
     const int32_t* table = nullptr;
+    DirectLoader<D, WAVES> dl;
+    using E8 = E4m3<D, NT>;
+    u4 kst[E8::kChunks], vst[E8::kChunks];  // staged E4M3 tiles (paged source only)
     if (SRC == KV_FP16) {
         kbase = a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh;
         vbase = a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh;
+        dl.init(a.k_ss, a.v_ss, wave, lane);
     } else {
         table = a.table + (int64_t)b * a.table_stride;
     }
+    auto rows_from = [&](int key0) { return min(kTileN, key_end - key0); };
+    auto load_k8 = [&](int it, u4 (&dst)[E8::kChunks]) {
+        E8::load(a, a.kc, table, g, tile_key0(it), key_last, tid, dst);
+    };
+    auto load_v8 = [&](int it, u4 (&dst)[E8::kChunks]) {
+        E8::load(a, a.vc, table, g, tile_key0(it), key_last, tid, dst);
+    };
+    auto issue_k = [&](int it, unsigned char* slot) {
+        const int key0 = tile_key0(it);
+        DirectLoader<D, WAVES>::issue(kbase + (int64_t)key0 * a.k_ss, a.k_ss, dl.koff, rows_from(key0), slot,
+                                      wave);
+    };
+    auto issue_v = [&](int it, unsigned char* slot) {
+        const int key0 = tile_key0(it);
+        DirectLoader<D, WAVES>::issue(vbase + (int64_t)key0 * a.v_ss, a.v_ss, dl.voff, rows_from(key0), slot,
+                                      wave);
+    };
 
     // ---- Q fragment in registers: lane holds Q[row][16kk + 8hlf .. +7] ------
     const int my_row = q0 + wave * kRowsPerWave + l32;
@@ -340,36 +330,37 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(const AttnArgs a)
         for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const h8*)(qp + 16 * kk + 8 * hlf);
     }
 
+    // ---- per-lane LDS offsets ------------------------------------------------
+    // K operand of S^T = K Q^T: row l32 (+32), chunk 2kk + hlf.
+    // V^T operand of O^T += V^T P^T through ds_read_b64_tr_b16: within each
+    // 16-lane group G, source lane s points at 4 FP16 of key row
+    // 4*(G/2) + s/4 (+8 for the second read), d = 32db + 16(G%2) + 4(s%4); the
+    // transposing read then hands lane (G, t) the 4 keys of d = 32db+16(G%2)+t.
+    const int grp = lane >> 4, sl = lane & 15;
+    const int vrow = 4 * (grp >> 1) + (sl >> 2);
+    const int vbyte = (sl & 1) * 8;
+    const int vchunk = 2 * (grp & 1) + ((sl & 3) >> 1);
+
+    int koff_s[KK];           // K operand: row l32, chunk 2kk + hlf
+    int voff_a[DB], voff_b[DB];  // V^T operand source addresses (keys +0..7, +8..15)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) koff_s[kk] = tile_off<D>(l32, 2 * kk + hlf);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        voff_a[db] = tile_off<D>(vrow, 4 * db + vchunk) + vbyte;
+        voff_b[db] = tile_off<D>(vrow + 8, 4 * db + vchunk) + vbyte;
+    }
+
     f16x oacc[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-    float m_run = -INFINITY;  // running max of scores * c (log2 units)
-    float l_run = 0.f;        // this lane half's share of the running sum
+    float m_run = -INFINITY;  // reference maximum of scores * c (log2 units)
+    float l_run = 0.f;        // this lane half's share of the sum of P
 
-    Stager<D, SRC, WAVES * 64> st;
-    auto stage_load = [&](int it) {
-        int key0 = tile_key0(it);
-        if constexpr (SRC == KV_FP16)
-            st.load(a, kbase, vbase, key0, key_last, tid);
-        else
-            st.load(a, table, g, key0, key_last, tid);
-    };
-
-    stage_load(0);
-    st.store(lds, lds + Lds<D>::kKElems, tid);
-    __syncthreads();
-
-    for (int it = 0; it < n_tiles; ++it) {
-        const int key0 = tile_key0(it);
-        if (it + 1 < n_tiles) stage_load(it + 1);
-
-        const _Float16* ks = lds + (it & 1) * Lds<D>::kStage;
-        const _Float16* vt = ks + Lds<D>::kKElems;
-
-        // ---- S^T = K Q^T for 64 keys x 32 queries (two 32x32 blocks) -------
-        f16x s0, s1;
+    // S^T = K Q^T for 64 keys x 32 queries (two 32x32 blocks)
+    auto compute_s = [&](const unsigned char* kt, f16x& s0, f16x& s1) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             s0[r] = 0.f;
@@ -377,23 +368,40 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(const AttnArgs a)
         }
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            h8 k0 = *(const h8*)(ks + l32 * Lds<D>::kKStride + 16 * kk + 8 * hlf);
-            h8 k1 = *(const h8*)(ks + (32 + l32) * Lds<D>::kKStride + 16 * kk + 8 * hlf);
+            const int off = tile_off<D>(l32, 2 * kk + hlf);
+            h8 k0 = *(const h8*)(kt + off);
+            h8 k1 = *(const h8*)(kt + off + 32 * ROW);
             s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qf[kk], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qf[kk], s1, 0, 0, 0);
         }
+    };
 
-        // ---- masks: register r of block kb holds key kb*32 + 8(r/4) + 4hlf + r%4
-        bool need_mask;
-        if (MODE == KEYS_CAUSAL)
-            need_mask = (int64_t)key0 + kTileN > a.offset + q0 + 1 || key0 + kTileN > key_end;
-        else if (MODE == KEYS_DENSE)
-            need_mask = key0 + kTileN > key_end;
-        else
-            need_mask = false;
-        if (need_mask) {
-            int64_t lim = (MODE == KEYS_CAUSAL) ? min((int64_t)key_last, a.offset + my_row)
-                                                : (int64_t)key_last;
+    // O^T += V^T P^T
+    auto compute_pv = [&](const unsigned char* vt, const h8* pk) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int offa = tile_off<D>(vrow, 4 * db + vchunk) + vbyte;
+            const int offb = tile_off<D>(vrow + 8, 4 * db + vchunk) + vbyte;
+#pragma unroll
+            for (int kstep = 0; kstep < 4; ++kstep) {
+                s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + offa));
+                s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + offb));
+                h8 vf = __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pk[kstep], oacc[db], 0, 0, 0);
+            }
+        }
+    };
+
+    // Mask the keys a row may not see (register r of block kb holds key
+    // kb*32 + 8(r/4) + 4hlf + r%4), then return the row maximum times c.
+    auto tile_needs_mask = [&](int key0) -> bool {
+        if (MODE == KEYS_CAUSAL) return (int64_t)key0 + kTileN > a.offset + q0 + 1 || key0 + kTileN > key_end;
+        if (MODE == KEYS_DENSE) return key0 + kTileN > key_end;
+        return false;
+    };
+    auto row_max = [&](f16x& s0, f16x& s1, int key0, bool masked) -> float {
+        if (masked && tile_needs_mask(key0)) {
+            int64_t lim = (MODE == KEYS_CAUSAL) ? min((int64_t)key_last, a.offset + my_row) : (int64_t)key_last;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 int kr = key0 + 8 * (r >> 2) + 4 * hlf + (r & 3);
@@ -401,53 +409,241 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(const AttnArgs a)
                 if (kr + 32 > lim) s1[r] = -INFINITY;
             }
         }
-
-        // ---- online softmax (base 2) --------------------------------------
-        float mx = -INFINITY;
+        float t[11];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-        mx = wave_half_max(mx);
-        const float m_new = fmaxf(m_run, mx * a.c);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
+        for (int i = 0; i < 5; ++i) {
+            t[i] = vmax3(s0[3 * i], s0[3 * i + 1], s0[3 * i + 2]);
+            t[5 + i] = vmax3(s1[3 * i], s1[3 * i + 1], s1[3 * i + 2]);
+        }
+        t[10] = fmaxf(s0[15], s1[15]);
+        float u0 = vmax3(t[0], t[1], t[2]), u1 = vmax3(t[3], t[4], t[5]), u2 = vmax3(t[6], t[7], t[8]);
+        float mx = vmax3(vmax3(u0, u1, u2), t[9], t[10]);
+        return wave_half_max(mx) * a.c;
+    };
 
-        float psum = 0.f;
+    // Raise the reference maximum of the rows whose scores exceed it by more
+    // than the slack, rescaling their O and l (wave-uniform branch).
+    auto raise_max = [&](float mc) {
+        const bool raise = mc > m_run + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+            const float m_new = raise ? mc : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < DB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        }
+    };
+
+    // P = 2^(S*c - m) in FP16, in the PV operand order; l += sum of P
+    auto exp_tile = [&](const f16x& s0, const f16x& s1, h8* pk) {
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        const h2 ones = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            h2 p0 = {(_Float16)__builtin_amdgcn_exp2f(fmaf(s0[r], a.c, -m_use)),
+                     (_Float16)__builtin_amdgcn_exp2f(fmaf(s0[r + 1], a.c, -m_use))};
+            h2 p1 = {(_Float16)__builtin_amdgcn_exp2f(fmaf(s1[r], a.c, -m_use)),
+                     (_Float16)__builtin_amdgcn_exp2f(fmaf(s1[r + 1], a.c, -m_use))};
+            l_run = __builtin_amdgcn_fdot2(p0, ones, l_run, false);
+            l_run = __builtin_amdgcn_fdot2(p1, ones, l_run, false);
+            pk[r >> 3][r & 7] = p0.x;
+            pk[r >> 3][(r & 7) + 1] = p0.y;
+            pk[2 + (r >> 3)][r & 7] = p1.x;
+            pk[2 + (r >> 3)][(r & 7) + 1] = p1.y;
+        }
+    };
+
+    // ---- pipeline --------------------------------------------------------------
+    // Invariant entering iteration it: S(it) is in scur with its maximum
+    // folded into m_run; K(it+1) and V(it) are in LDS; the loads of K(it+2) and
+    // V(it+1) are in flight (FP16) or written to LDS (E4M3, with K(it+3) and
+    // V(it+2) staged in registers).
+    auto kslot = [&](auto par) -> unsigned char* {
+        if constexpr (decltype(par)::value == 0) return kslot0; else return kslot1;
+    };
+    auto vslot = [&](auto par) -> unsigned char* {
+        if constexpr (decltype(par)::value == 0) return vslot0; else return vslot1;
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+
+    if constexpr (SRC == KV_FP16) {
+        issue_k(0, kslot0);
+        issue_v(0, vslot0);
+        if (n_tiles > 1) issue_k(1, kslot1);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    } else {
+        load_k8(0, kst);
+        load_v8(0, vst);
+        E8::store(kslot0, kst, tid);
+        E8::store(vslot0, vst, tid);
+        if (n_tiles > 1) {
+            load_k8(1, kst);
+            E8::store(kslot1, kst, tid);
+        }
+    }
+    __syncthreads();
+    f16x scur0, scur1;
+    compute_s(kslot0, scur0, scur1);
+    raise_max(row_max(scur0, scur1, tile_key0(0), true));
+    __syncthreads();
+    if constexpr (SRC == KV_FP16) {
+        if (n_tiles > 2) issue_k(2, kslot0);
+        if (n_tiles > 1) issue_v(1, vslot1);
+    } else {
+        // K(2) and V(1) are written now; K(3) and V(2) are staged in registers
+        if (n_tiles > 2) {
+            load_k8(2, kst);
+            E8::store(kslot0, kst, tid);
+        }
+        if (n_tiles > 1) {
+            load_v8(1, vst);
+            E8::store(vslot1, vst, tid);
+        }
+        if (n_tiles > 3) load_k8(3, kst);
+        if (n_tiles > 2) load_v8(2, vst);
+    }
+
+    // refill the slots after the iteration's reads: K(it+3) and V(it+2)
+    auto refill = [&](auto par, int it) {
+        using PN = std::integral_constant<int, decltype(par)::value ^ 1>;
+        if constexpr (SRC == KV_FP16) {
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);
+            __syncthreads();
+            if (it + 3 < n_tiles) issue_k(it + 3, kslot(PN{}));
+            if (it + 2 < n_tiles) issue_v(it + 2, vslot(par));
+        } else {
+            __syncthreads();
+            if (it + 3 < n_tiles) E8::store(kslot(PN{}), kst, tid);
+            if (it + 2 < n_tiles) E8::store(vslot(par), vst, tid);
+            if (it + 4 < n_tiles) load_k8(it + 4, kst);
+            if (it + 3 < n_tiles) load_v8(it + 3, vst);
+        }
+    };
+
+    // Steady state: tile it+1 exists and needs no mask. Written as explicit
+    // steps separated by scheduling fences: block B issues the 2*KK score
+    // MFMAs of tile it+1 with the exponentials of tile it between them, block
+    // C the 4*DB PV MFMAs of tile it with the row maximum of tile it+1 between
+    // them; every LDS operand read is issued two or three MFMAs ahead.
+    auto iteration_main = [&](auto par, int it) {
+        using PN = std::integral_constant<int, decltype(par)::value ^ 1>;
+        const unsigned char* kt = kslot(PN{});
+        const unsigned char* vt = vslot(par);
+        constexpr int NB = 2 * KK;  // score MFMAs
+        constexpr int NC = 4 * DB;  // PV MFMAs
+        f16x sn0, sn1;
         h8 pk[4];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float p0 = __builtin_amdgcn_exp2f(fmaf(s0[r], a.c, -m_use));
-            float p1 = __builtin_amdgcn_exp2f(fmaf(s1[r], a.c, -m_use));
-            psum += p0 + p1;
-            pk[r >> 3][r & 7] = (_Float16)p0;
-            pk[2 + (r >> 3)][r & 7] = (_Float16)p1;
-        }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int i = 0; i < DB; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
 
-        // ---- O^T += V^T P^T ---------------------------------------------------
+        // ---- block B ----
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        const h2 ones = {(_Float16)1.f, (_Float16)1.f};
+        h8 kop[NB];
+        auto kread = [&](int i) { return *(const h8*)(kt + koff_s[i >> 1] + (i & 1) * 32 * ROW); };
+        kop[0] = kread(0);
+        kop[1] = kread(1);
+        kop[2] = kread(2);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int d = db * 32 + l32;
+        for (int i = 0; i < NB; ++i) {
+            if (i + 3 < NB) kop[i + 3] = kread(i + 3);
+            if (i == 0)
+                sn0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[0], qf[0], f16x{}, 0, 0, 0);
+            else if (i == 1)
+                sn1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[1], qf[0], f16x{}, 0, 0, 0);
+            else if (i & 1)
+                sn1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[i], qf[i >> 1], sn1, 0, 0, 0);
+            else
+                sn0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[i], qf[i >> 1], sn0, 0, 0, 0);
+            // exponential unit: 16 units of 2 scores cover the tile
+            constexpr int UPS = 16 / NB > 0 ? 16 / NB : 1;  // units per step
 #pragma unroll
-            for (int kstep = 0; kstep < 4; ++kstep) {
-                h8 vf = *(const h8*)(vt + vt_chunk(d, 2 * kstep + hlf));
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pk[kstep], oacc[db], 0, 0, 0);
+            for (int uu = 0; uu < UPS; ++uu) {
+                const int u = i * UPS + uu;
+                if (u < 16) {
+                    const int blk = u & 1, r = 2 * (u >> 1);
+                    const f16x& sc = blk ? scur1 : scur0;
+                    h2 p = {(_Float16)__builtin_amdgcn_exp2f(fmaf(sc[r], a.c, -m_use)),
+                            (_Float16)__builtin_amdgcn_exp2f(fmaf(sc[r + 1], a.c, -m_use))};
+                    l_run = __builtin_amdgcn_fdot2(p, ones, l_run, false);
+                    pk[2 * blk + (r >> 3)][r & 7] = p.x;
+                    pk[2 * blk + (r >> 3)][(r & 7) + 1] = p.y;
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
 
-        if (it + 1 < n_tiles) {
-            _Float16* nks = lds + ((it + 1) & 1) * Lds<D>::kStage;
-            st.store(nks, nks + Lds<D>::kKElems, tid);
+        // ---- block C ----
+        auto vread = [&](int i) {
+            const int kstep = i / DB, db = i % DB;
+            s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + voff_a[db]));
+            s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + voff_b[db]));
+            return __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        h8 vop[NC];
+        vop[0] = vread(0);
+        vop[1] = vread(1);
+        __builtin_amdgcn_sched_barrier(0);
+        float macc = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            if (i + 2 < NC) vop[i + 2] = vread(i + 2);
+            const int kstep = i / DB, db = i % DB;
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[i], pk[kstep], oacc[db], 0, 0, 0);
+            // row-maximum unit: two MFMAs in, 16 units of 2 scores
+            constexpr int MPS = 16 / (NC - 2) + 1;
+#pragma unroll
+            for (int uu = 0; uu < MPS; ++uu) {
+                const int u = (i - 2) * MPS + uu;
+                if (i >= 2 && u < 16) macc = vmax3(macc, sn0[u], sn1[u]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();
+        raise_max(wave_half_max(macc) * a.c);
+        refill(par, it);
+        scur0 = sn0;
+        scur1 = sn1;
+    };
+
+    // Any iteration, masked tiles and the last tile included.
+    auto iteration_tail = [&](auto par, int it) {
+        using PN = std::integral_constant<int, decltype(par)::value ^ 1>;
+        f16x snext0 = {}, snext1 = {};
+        h8 pk[4];
+        if (it + 1 < n_tiles) compute_s(kslot(PN{}), snext0, snext1);
+        exp_tile(scur0, scur1, pk);
+        compute_pv(vslot(par), pk);
+        if (it + 1 < n_tiles) raise_max(row_max(snext0, snext1, tile_key0(it + 1), true));
+        refill(par, it);
+        scur0 = snext0;
+        scur1 = snext1;
+    };
+
+    // tiles 0 .. n_plain-1 need no mask (a prefix of the tile sequence)
+    int n_plain = n_tiles;
+    if (MODE == KEYS_CAUSAL) {
+        int64_t lim = min(a.offset + q0 + 1, (int64_t)key_end);  // keys every row sees
+        n_plain = (int)max((int64_t)0, min((int64_t)n_tiles, (lim - (int64_t)tile_begin * kTileN) / kTileN));
+    } else if (MODE == KEYS_DENSE) {
+        n_plain = key_end / kTileN;
+    }
+    int it = 0;
+    for (; it + 2 < n_plain; it += 2) {
+        iteration_main(P0{}, it);
+        iteration_main(P1{}, it + 1);
+    }
+    for (; it < n_tiles; ++it) {
+        if (it & 1)
+            iteration_tail(P1{}, it);
+        else
+            iteration_tail(P0{}, it);
     }
 
     // ---- epilogue ------------------------------------------------------------
-    const float l_tot = wave_half_sum(l_run);
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (my_row >= a.Lq) return;
     const int64_t bh = (int64_t)b * a.Hq + h;
     if (SPLIT) {
