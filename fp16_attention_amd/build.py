@@ -17,8 +17,13 @@ SOURCES = ["abi.cpp", "attn_fwd.hip", "e4m3_bridge.hip", "vsa_select.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming packed FP32 VALU ops.
+# -amdgpu-mfma-vgpr-form: MFMA accumulators in VGPRs, so the D=256 attention
+# kernels can rescale their FP32 output accumulators without moving them
+# between the AGPR and VGPR files every iteration (read-only operands go to
+# AGPRs instead).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include")]
 
 

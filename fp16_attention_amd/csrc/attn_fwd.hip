@@ -328,6 +328,13 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         const _Float16* qp = a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)row * a.q_ss;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const h8*)(qp + 16 * kk + 8 * hlf);
+        // With D = 256 the FP32 output accumulators take half the register
+        // file; the read-only Q operands live in AGPRs (MFMA sources may) so
+        // that the accumulators stay in VGPRs, where the rescale can scale them.
+        if constexpr (D > 128) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) asm volatile("; q fragment to AGPRs" : "=a"(qf[kk]) : "0"(qf[kk]));
+        }
     }
 
     // ---- per-lane LDS offsets ------------------------------------------------
