@@ -75,6 +75,21 @@ constexpr float kRescaleSlack = 8.0f;
 // [6:4], lgkmcnt in [11:8].
 constexpr int kWaitVm0 = 0x0F70;
 
+// Workgroup barrier for the K/V ring: the caller's s_waitcnt (vmcnt(n) with
+// lgkmcnt(0)) makes this wave's loads into LDS older than the n most recent
+// ones, and its LDS accesses, complete; s_barrier then orders them before
+// every wave's later LDS reads. A C++ fence here would wait for all loads
+// into LDS (vmcnt(0)), so the compiler is only kept from moving memory
+// accesses across the barrier.
+template <int WAITCNT>
+__device__ __forceinline__ void ring_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(WAITCNT);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // LDS tile layout: 64 rows (keys) of D FP16, row-major, 2*D bytes per row;
 // 16-byte chunk c of row r sits at position c ^ swz(r % 16).
@@ -116,9 +131,9 @@ __device__ __forceinline__ u2 e4m3x4_to_f16(uint32_t w)
 // [16 i, 16 i + 16) of that block, so each lane loads the global chunk that
 // belongs at that LDS position.
 // ---------------------------------------------------------------------------
-template <int D, int WAVES>
+template <int D, int WAVES, int KT>
 struct DirectLoader {
-    static constexpr int kLoads = (kTileN * D * 2 / 1024) / WAVES;  // per wave per tile
+    static constexpr int kLoads = (KT * D * 2 / 1024) / WAVES;  // per wave per tile
     int koff[kLoads];
     int voff[kLoads];
 
@@ -153,9 +168,9 @@ struct DirectLoader {
 // written to LDS as two 16-byte chunks. Thread tid handles chunks
 // tid + NT * i of the tile (row = chunk / (D/16), 16-code column chunk % (D/16)).
 // ---------------------------------------------------------------------------
-template <int D, int NT>
+template <int D, int NT, int KT>
 struct E4m3 {
-    static constexpr int kChunks = kTileN * D / 16 / NT;  // per thread per K or V tile
+    static constexpr int kChunks = KT * D / 16 / NT;  // per thread per K or V tile
 
     static __device__ __forceinline__ void load(const AttnArgs& a, const uint8_t* cache,
                                                 const int32_t* table, int g, int key0, int key_last,
@@ -194,24 +209,55 @@ struct E4m3 {
 
 // ---------------------------------------------------------------------------
 // The attention kernel.
+//
+// Tiling<D, SRC, MODE>: KT keys per K/V tile and R slots per K and V ring.
+// FP16 K/V stream through rings of four 32-key slots (64 KB of LDS at
+// D = 128, so two workgroups share a CU; 128 KB at D = 256), giving each
+// load three iterations to arrive: all workgroups on an XCD read the same
+// tiles at about the same time, so every tile costs them the latency of an
+// L2 miss together. Block lists use 64-key tiles (one block each); the paged
+// E4M3 source is staged through registers with two slots.
 // ---------------------------------------------------------------------------
+template <int D, int SRC, int MODE>
+struct Tiling {
+    static constexpr int KT = MODE == KEYS_BLOCKS ? 64 : 32;
+    static constexpr int R = (SRC == KV_FP16 && MODE != KEYS_BLOCKS) ? 4 : 2;
+};
+
 template <int D, int WAVES, int SRC, int MODE, bool SPLIT>
 __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kernel(const AttnArgs a)
 {
     constexpr int NT = WAVES * 64;
     constexpr int M = WAVES * kRowsPerWave;
-    constexpr int KK = D / 16;  // MFMA k-steps over D for S
-    constexpr int DB = D / 32;  // 32-wide d blocks of O^T
-    constexpr int TB = kTileN * D * 2;
-    constexpr int ROW = 2 * D;  // bytes per LDS row
+    constexpr int KT = Tiling<D, SRC, MODE>::KT;
+    constexpr int NSB = KT / 32;  // 32-key score blocks per tile
+    constexpr int KS = KT / 16;   // 16-key PV k-steps per tile
+    constexpr int KK = D / 16;    // MFMA k-steps over D for S
+    constexpr int DB = D / 32;    // 32-wide d blocks of O^T
+    constexpr int TB = KT * D * 2;
+    constexpr int ROW = 2 * D;    // bytes per LDS row
+    static_assert(MODE != KEYS_BLOCKS || KT == kTileN, "block lists need 64-key tiles");
+    constexpr int R = Tiling<D, SRC, MODE>::R;
+    static_assert(R >= 2 && R <= 4 && (SRC == KV_FP16 || R == 2), "ring depth");
     __shared__ __attribute__((aligned(1024))) unsigned char kslot0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char kslot1[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kslot2[R > 2 ? TB : 16];
+    __shared__ __attribute__((aligned(1024))) unsigned char kslot3[R > 3 ? TB : 16];
     __shared__ __attribute__((aligned(1024))) unsigned char vslot0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char vslot1[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char vslot2[R > 2 ? TB : 16];
+    __shared__ __attribute__((aligned(1024))) unsigned char vslot3[R > 3 ? TB : 16];
+    // s_waitcnt that leaves the R-2 most recent load groups in flight
+    constexpr int kGroupLoads = 2 * DirectLoader<D, WAVES, KT>::kLoads;
+    constexpr int kVmLeft = (R - 2) * kGroupLoads;
+    static_assert(kVmLeft < 64, "vmcnt range");
+    constexpr int kWaitGroups = (kVmLeft & 15) | ((kVmLeft >> 4) << 14) | 0x0070;  // and lgkmcnt(0)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave index in a scalar register: the LDS destinations of the loads into
+    // LDS (M0) are then computed on the scalar unit
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int hlf = lane >> 5;
 
@@ -255,26 +301,25 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     const int g = h / a.group;
     const int q0 = qt * M;
 
-    int tile_begin = 0, n_tiles;
+    // keys [key_begin, key_stop) are streamed; key_end bounds every row's keys
+    int key_begin = 0, key_stop = a.Lkv, key_end = a.Lkv, n_tiles;
     const int32_t* blist = nullptr;
-    int key_end = a.Lkv;
     if (MODE == KEYS_CAUSAL) {
-        int last_row = min(q0 + M, a.Lq) - 1;
+        const int last_row = min(q0 + M, a.Lq) - 1;
         key_end = (int)min((int64_t)a.Lkv, a.offset + last_row + 1);
-        int nt = (key_end + kTileN - 1) / kTileN;
-        tile_begin = seg * a.seg_tiles;
-        n_tiles = min(nt, tile_begin + a.seg_tiles) - tile_begin;
-        if (n_tiles <= 0) return;  // the merge skips segments past the key range
+        key_begin = seg * a.seg_tiles * kTileN;
+        key_stop = min(key_end, (seg + 1) * a.seg_tiles * kTileN);
+        if (key_begin >= key_stop) return;  // the merge skips segments past the key range
+        n_tiles = (key_stop - key_begin + KT - 1) / KT;
     } else if (MODE == KEYS_BLOCKS) {
-        int qb = qt;  // M == 64: one query block per workgroup
-        if (qb < a.dense_prefix) {
-            n_tiles = a.Lkv / kTileN;
+        if (qt < a.dense_prefix) {
+            n_tiles = a.Lkv / KT;
         } else {
             n_tiles = a.topk;
-            blist = a.idx + (((int64_t)b * a.Hq + h) * a.nqb + qb) * a.topk;
+            blist = a.idx + (((int64_t)b * a.Hq + h) * a.nqb + qt) * a.topk;
         }
     } else {
-        n_tiles = (a.Lkv + kTileN - 1) / kTileN;
+        n_tiles = (a.Lkv + KT - 1) / KT;
     }
     const int key_last = key_end - 1;
     const int nblk = a.Lkv / kTileN;
@@ -285,15 +330,15 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
             blk = min(max(blk, 0), nblk - 1);
             return blk * kTileN;
         }
-        return (tile_begin + it) * kTileN;
+        return key_begin + it * KT;
     };
 
     // ---- K/V sources -----------------------------------------------------
     const _Float16* kbase = nullptr;
     const _Float16* vbase = nullptr;
     const int32_t* table = nullptr;
-    DirectLoader<D, WAVES> dl;
-    using E8 = E4m3<D, NT>;
+    DirectLoader<D, WAVES, KT> dl;
+    using E8 = E4m3<D, NT, KT>;
     u4 kst[E8::kChunks], vst[E8::kChunks];  // staged E4M3 tiles (paged source only)
     if (SRC == KV_FP16) {
         kbase = a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh;
@@ -302,22 +347,26 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     } else {
         table = a.table + (int64_t)b * a.table_stride;
     }
-    auto rows_from = [&](int key0) { return min(kTileN, key_end - key0); };
+    // Every load group issues the same number of loads, so that s_waitcnt
+    // counts stay exact: a tile past the end is loaded with zero valid rows
+    // (the buffer range check returns zeros) into its free slot.
+    auto issue_k = [&](int it, unsigned char* slot) {
+        const bool ok = it < n_tiles;
+        const int key0 = tile_key0(ok ? it : n_tiles - 1);
+        DirectLoader<D, WAVES, KT>::issue(kbase + (int64_t)key0 * a.k_ss, a.k_ss, dl.koff,
+                                          ok ? min(KT, key_end - key0) : 0, slot, wave);
+    };
+    auto issue_v = [&](int it, unsigned char* slot) {
+        const bool ok = it < n_tiles;
+        const int key0 = tile_key0(ok ? it : n_tiles - 1);
+        DirectLoader<D, WAVES, KT>::issue(vbase + (int64_t)key0 * a.v_ss, a.v_ss, dl.voff,
+                                          ok ? min(KT, key_end - key0) : 0, slot, wave);
+    };
     auto load_k8 = [&](int it, u4 (&dst)[E8::kChunks]) {
         E8::load(a, a.kc, table, g, tile_key0(it), key_last, tid, dst);
     };
     auto load_v8 = [&](int it, u4 (&dst)[E8::kChunks]) {
         E8::load(a, a.vc, table, g, tile_key0(it), key_last, tid, dst);
-    };
-    auto issue_k = [&](int it, unsigned char* slot) {
-        const int key0 = tile_key0(it);
-        DirectLoader<D, WAVES>::issue(kbase + (int64_t)key0 * a.k_ss, a.k_ss, dl.koff, rows_from(key0), slot,
-                                      wave);
-    };
-    auto issue_v = [&](int it, unsigned char* slot) {
-        const int key0 = tile_key0(it);
-        DirectLoader<D, WAVES>::issue(vbase + (int64_t)key0 * a.v_ss, a.v_ss, dl.voff, rows_from(key0), slot,
-                                      wave);
     };
 
     // ---- Q fragment in registers: lane holds Q[row][16kk + 8hlf .. +7] ------
@@ -338,7 +387,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     }
 
     // ---- per-lane LDS offsets ------------------------------------------------
-    // K operand of S^T = K Q^T: row l32 (+32), chunk 2kk + hlf.
+    // K operand of S^T = K Q^T: row l32 (+32 per score block), chunk 2kk + hlf.
     // V^T operand of O^T += V^T P^T through ds_read_b64_tr_b16: within each
     // 16-lane group G, source lane s points at 4 FP16 of key row
     // 4*(G/2) + s/4 (+8 for the second read), d = 32db + 16(G%2) + 4(s%4); the
@@ -347,9 +396,8 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     const int vrow = 4 * (grp >> 1) + (sl >> 2);
     const int vbyte = (sl & 1) * 8;
     const int vchunk = 2 * (grp & 1) + ((sl & 3) >> 1);
-
-    int koff_s[KK];           // K operand: row l32, chunk 2kk + hlf
-    int voff_a[DB], voff_b[DB];  // V^T operand source addresses (keys +0..7, +8..15)
+    int koff_s[KK];
+    int voff_a[DB], voff_b[DB];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) koff_s[kk] = tile_off<D>(l32, 2 * kk + hlf);
 #pragma unroll
@@ -366,65 +414,70 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     float m_run = -INFINITY;  // reference maximum of scores * c (log2 units)
     float l_run = 0.f;        // this lane half's share of the sum of P
 
-    // S^T = K Q^T for 64 keys x 32 queries (two 32x32 blocks)
-    auto compute_s = [&](const unsigned char* kt, f16x& s0, f16x& s1) {
+    // S^T = K Q^T for KT keys x 32 queries (NSB blocks of 32 x 32)
+    auto compute_s = [&](const unsigned char* kt, f16x (&s)[NSB]) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            s0[r] = 0.f;
-            s1[r] = 0.f;
-        }
+        for (int kb = 0; kb < NSB; ++kb)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const int off = tile_off<D>(l32, 2 * kk + hlf);
-            h8 k0 = *(const h8*)(kt + off);
-            h8 k1 = *(const h8*)(kt + off + 32 * ROW);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qf[kk], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qf[kk], s1, 0, 0, 0);
-        }
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < NSB; ++kb) {
+                h8 k = *(const h8*)(kt + koff_s[kk] + kb * 32 * ROW);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k, qf[kk], s[kb], 0, 0, 0);
+            }
     };
 
     // O^T += V^T P^T
+    auto vread = [&](const unsigned char* vt, int i) {
+        const int kstep = i / DB, db = i % DB;
+        s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + voff_a[db]));
+        s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + voff_b[db]));
+        return __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
     auto compute_pv = [&](const unsigned char* vt, const h8* pk) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int offa = tile_off<D>(vrow, 4 * db + vchunk) + vbyte;
-            const int offb = tile_off<D>(vrow + 8, 4 * db + vchunk) + vbyte;
-#pragma unroll
-            for (int kstep = 0; kstep < 4; ++kstep) {
-                s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + offa));
-                s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + offb));
-                h8 vf = __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pk[kstep], oacc[db], 0, 0, 0);
-            }
+        for (int i = 0; i < KS * DB; ++i) {
+            const int kstep = i / DB, db = i % DB;
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vread(vt, i), pk[kstep], oacc[db], 0, 0, 0);
         }
     };
 
-    // Mask the keys a row may not see (register r of block kb holds key
+    // Mask the keys a row may not see (register r of score block kb holds key
     // kb*32 + 8(r/4) + 4hlf + r%4), then return the row maximum times c.
     auto tile_needs_mask = [&](int key0) -> bool {
-        if (MODE == KEYS_CAUSAL) return (int64_t)key0 + kTileN > a.offset + q0 + 1 || key0 + kTileN > key_end;
-        if (MODE == KEYS_DENSE) return key0 + kTileN > key_end;
+        if (MODE == KEYS_CAUSAL) return (int64_t)key0 + KT > a.offset + q0 + 1 || key0 + KT > key_end;
+        if (MODE == KEYS_DENSE) return key0 + KT > key_end;
         return false;
     };
-    auto row_max = [&](f16x& s0, f16x& s1, int key0, bool masked) -> float {
+    auto row_max = [&](f16x (&s)[NSB], int key0, bool masked) -> float {
         if (masked && tile_needs_mask(key0)) {
-            int64_t lim = (MODE == KEYS_CAUSAL) ? min((int64_t)key_last, a.offset + my_row) : (int64_t)key_last;
+            const int64_t lim = (MODE == KEYS_CAUSAL) ? min((int64_t)key_last, a.offset + my_row) : (int64_t)key_last;
+            const int64_t rel = lim - key0 - 4 * hlf;  // mask register r when 8(r/4) + r%4 + 32kb > rel
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                int kr = key0 + 8 * (r >> 2) + 4 * hlf + (r & 3);
-                if (kr > lim) s0[r] = -INFINITY;
-                if (kr + 32 > lim) s1[r] = -INFINITY;
+            for (int kb = 0; kb < NSB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (8 * (r >> 2) + (r & 3) + 32 * kb > rel) s[kb][r] = -INFINITY;
+        }
+        float mx;
+        if constexpr (NSB == 2) {
+            float t[11];
+#pragma unroll
+            for (int i = 0; i < 5; ++i) {
+                t[i] = vmax3(s[0][3 * i], s[0][3 * i + 1], s[0][3 * i + 2]);
+                t[5 + i] = vmax3(s[1][3 * i], s[1][3 * i + 1], s[1][3 * i + 2]);
             }
-        }
-        float t[11];
+            t[10] = fmaxf(s[0][15], s[1][15]);
+            float u0 = vmax3(t[0], t[1], t[2]), u1 = vmax3(t[3], t[4], t[5]), u2 = vmax3(t[6], t[7], t[8]);
+            mx = vmax3(vmax3(u0, u1, u2), t[9], t[10]);
+        } else {
+            float t[5];
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            t[i] = vmax3(s0[3 * i], s0[3 * i + 1], s0[3 * i + 2]);
-            t[5 + i] = vmax3(s1[3 * i], s1[3 * i + 1], s1[3 * i + 2]);
+            for (int i = 0; i < 5; ++i) t[i] = vmax3(s[0][3 * i], s[0][3 * i + 1], s[0][3 * i + 2]);
+            mx = vmax3(vmax3(t[0], t[1], t[2]), vmax3(t[3], t[4], s[0][15]), t[0]);
         }
-        t[10] = fmaxf(s0[15], s1[15]);
-        float u0 = vmax3(t[0], t[1], t[2]), u1 = vmax3(t[3], t[4], t[5]), u2 = vmax3(t[6], t[7], t[8]);
-        float mx = vmax3(vmax3(u0, u1, u2), t[9], t[10]);
         return wave_half_max(mx) * a.c;
     };
 
@@ -433,9 +486,10 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     auto raise_max = [&](float mc) {
         const bool raise = mc > m_run + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(raise)) {
-            const float m_new = raise ? mc : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
+            // rows that do not raise keep their state exactly (alpha = 1; also
+            // for a row whose reference is still -inf)
+            const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mc) : 1.f;
+            m_run = raise ? mc : m_run;
             l_run *= alpha;
 #pragma unroll
             for (int i = 0; i < DB; ++i)
@@ -444,43 +498,58 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         }
     };
 
-    // P = 2^(S*c - m) in FP16, in the PV operand order; l += sum of P
-    auto exp_tile = [&](const f16x& s0, const f16x& s1, h8* pk) {
+    // One exponential unit: scores r, r+1 of score block kb -> P (FP16) in the
+    // PV operand order (register r of block kb is k-step 2kb + r/8, slot r%8).
+    const h2 ones = {(_Float16)1.f, (_Float16)1.f};
+    auto exp_unit = [&](const f16x (&s)[NSB], int u, float m_use, h8* pk) {
+        const int kb = u % NSB, r = 2 * (u / NSB);
+        h2 p = {(_Float16)__builtin_amdgcn_exp2f(fmaf(s[kb][r], a.c, -m_use)),
+                (_Float16)__builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], a.c, -m_use))};
+        l_run = __builtin_amdgcn_fdot2(p, ones, l_run, false);
+        pk[2 * kb + (r >> 3)][r & 7] = p.x;
+        pk[2 * kb + (r >> 3)][(r & 7) + 1] = p.y;
+    };
+    constexpr int NU = 8 * NSB;  // exponential units per tile
+    auto exp_tile = [&](const f16x (&s)[NSB], h8* pk) {
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        const h2 ones = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            h2 p0 = {(_Float16)__builtin_amdgcn_exp2f(fmaf(s0[r], a.c, -m_use)),
-                     (_Float16)__builtin_amdgcn_exp2f(fmaf(s0[r + 1], a.c, -m_use))};
-            h2 p1 = {(_Float16)__builtin_amdgcn_exp2f(fmaf(s1[r], a.c, -m_use)),
-                     (_Float16)__builtin_amdgcn_exp2f(fmaf(s1[r + 1], a.c, -m_use))};
-            l_run = __builtin_amdgcn_fdot2(p0, ones, l_run, false);
-            l_run = __builtin_amdgcn_fdot2(p1, ones, l_run, false);
-            pk[r >> 3][r & 7] = p0.x;
-            pk[r >> 3][(r & 7) + 1] = p0.y;
-            pk[2 + (r >> 3)][r & 7] = p1.x;
-            pk[2 + (r >> 3)][(r & 7) + 1] = p1.y;
-        }
+        for (int u = 0; u < NU; ++u) exp_unit(s, u, m_use, pk);
     };
 
     // ---- pipeline --------------------------------------------------------------
-    // Invariant entering iteration it: S(it) is in scur with its maximum
-    // folded into m_run; K(it+1) and V(it) are in LDS; the loads of K(it+2) and
-    // V(it+1) are in flight (FP16) or written to LDS (E4M3, with K(it+3) and
-    // V(it+2) staged in registers).
-    auto kslot = [&](auto par) -> unsigned char* {
-        if constexpr (decltype(par)::value == 0) return kslot0; else return kslot1;
+    // K(j) and V(j) live in slot j % R. Load group g is {K(g+1), V(g)}; at the
+    // end of iteration it the slots of K(it+1) and V(it) are free and group
+    // it+R is issued into them, so every FP16 group has R-1 iterations to
+    // arrive. Invariant entering iteration it: S(it) is in scur with its
+    // maximum folded into m_run; K(it+1) and V(it) are in LDS; groups
+    // it+1 .. it+R-1 are in flight (FP16). E4M3 (R = 2) writes group it+1 to
+    // LDS and stages group it+2 in registers instead.
+    auto kslot = [&](auto p) -> unsigned char* {
+        constexpr int S = decltype(p)::value % R;
+        if constexpr (S == 0) return kslot0;
+        else if constexpr (S == 1) return kslot1;
+        else if constexpr (S == 2) return kslot2;
+        else return kslot3;
     };
-    auto vslot = [&](auto par) -> unsigned char* {
-        if constexpr (decltype(par)::value == 0) return vslot0; else return vslot1;
+    auto vslot = [&](auto p) -> unsigned char* {
+        constexpr int S = decltype(p)::value % R;
+        if constexpr (S == 0) return vslot0;
+        else if constexpr (S == 1) return vslot1;
+        else if constexpr (S == 2) return vslot2;
+        else return vslot3;
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
+    using P4 = std::integral_constant<int, 4>;
+    (void)kst;
+    (void)vst;
 
     if constexpr (SRC == KV_FP16) {
         issue_k(0, kslot0);
         issue_v(0, vslot0);
-        if (n_tiles > 1) issue_k(1, kslot1);
+        issue_k(1, kslot1);
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
     } else {
         load_k8(0, kst);
@@ -493,13 +562,22 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         }
     }
     __syncthreads();
-    f16x scur0, scur1;
-    compute_s(kslot0, scur0, scur1);
-    raise_max(row_max(scur0, scur1, tile_key0(0), true));
+    f16x scur[NSB];
+    compute_s(kslot0, scur);
+    raise_max(row_max(scur, tile_key0(0), true));
     __syncthreads();
     if constexpr (SRC == KV_FP16) {
-        if (n_tiles > 2) issue_k(2, kslot0);
-        if (n_tiles > 1) issue_v(1, vslot1);
+        // groups 1 .. R-1
+        issue_k(2, kslot(P2{}));
+        issue_v(1, vslot(P1{}));
+        if constexpr (R > 2) {
+            issue_k(3, kslot(P3{}));
+            issue_v(2, vslot(P2{}));
+        }
+        if constexpr (R > 3) {
+            issue_k(4, kslot(P4{}));
+            issue_v(3, vslot(P3{}));
+        }
     } else {
         // K(2) and V(1) are written now; K(3) and V(2) are staged in registers
         if (n_tiles > 2) {
@@ -514,42 +592,41 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         if (n_tiles > 2) load_v8(2, vst);
     }
 
-    // refill the slots after the iteration's reads: K(it+3) and V(it+2)
-    auto refill = [&](auto par, int it) {
-        using PN = std::integral_constant<int, decltype(par)::value ^ 1>;
+    // end of iteration it (phase p = it % R): wait for group it+1, then refill
+    // the slots read in this iteration with group it+R
+    auto refill = [&](auto p, int it) {
+        using PN = std::integral_constant<int, decltype(p)::value + 1>;
         if constexpr (SRC == KV_FP16) {
-            __builtin_amdgcn_s_waitcnt(kWaitVm0);
-            __syncthreads();
-            if (it + 3 < n_tiles) issue_k(it + 3, kslot(PN{}));
-            if (it + 2 < n_tiles) issue_v(it + 2, vslot(par));
+            ring_barrier<kWaitGroups>();
+            issue_k(it + R + 1, kslot(PN{}));
+            issue_v(it + R, vslot(p));
         } else {
             __syncthreads();
             if (it + 3 < n_tiles) E8::store(kslot(PN{}), kst, tid);
-            if (it + 2 < n_tiles) E8::store(vslot(par), vst, tid);
+            if (it + 2 < n_tiles) E8::store(vslot(p), vst, tid);
             if (it + 4 < n_tiles) load_k8(it + 4, kst);
             if (it + 3 < n_tiles) load_v8(it + 3, vst);
         }
     };
 
     // Steady state: tile it+1 exists and needs no mask. Written as explicit
-    // steps separated by scheduling fences: block B issues the 2*KK score
-    // MFMAs of tile it+1 with the exponentials of tile it between them, block
-    // C the 4*DB PV MFMAs of tile it with the row maximum of tile it+1 between
-    // them; every LDS operand read is issued two or three MFMAs ahead.
-    auto iteration_main = [&](auto par, int it) {
-        using PN = std::integral_constant<int, decltype(par)::value ^ 1>;
+    // steps separated by scheduling fences: block B issues the score MFMAs of
+    // tile it+1 with the exponentials of tile it between them, block C the PV
+    // MFMAs of tile it with the row maximum of tile it+1 between them; every
+    // LDS operand read is issued two or three MFMAs ahead.
+    auto iteration_main = [&](auto p, int it) {
+        using PN = std::integral_constant<int, decltype(p)::value + 1>;
         const unsigned char* kt = kslot(PN{});
-        const unsigned char* vt = vslot(par);
-        constexpr int NB = 2 * KK;  // score MFMAs
-        constexpr int NC = 4 * DB;  // PV MFMAs
-        f16x sn0, sn1;
-        h8 pk[4];
+        const unsigned char* vt = vslot(p);
+        constexpr int NB = NSB * KK;  // score MFMAs
+        constexpr int NC = KS * DB;   // PV MFMAs
+        f16x sn[NSB];
+        h8 pk[KS];
 
         // ---- block B ----
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        const h2 ones = {(_Float16)1.f, (_Float16)1.f};
         h8 kop[NB];
-        auto kread = [&](int i) { return *(const h8*)(kt + koff_s[i >> 1] + (i & 1) * 32 * ROW); };
+        auto kread = [&](int i) { return *(const h8*)(kt + koff_s[i / NSB] + (i % NSB) * 32 * ROW); };
         kop[0] = kread(0);
         kop[1] = kread(1);
         kop[2] = kread(2);
@@ -557,97 +634,88 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             if (i + 3 < NB) kop[i + 3] = kread(i + 3);
-            if (i == 0)
-                sn0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[0], qf[0], f16x{}, 0, 0, 0);
-            else if (i == 1)
-                sn1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[1], qf[0], f16x{}, 0, 0, 0);
-            else if (i & 1)
-                sn1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[i], qf[i >> 1], sn1, 0, 0, 0);
-            else
-                sn0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[i], qf[i >> 1], sn0, 0, 0, 0);
-            // exponential unit: 16 units of 2 scores cover the tile
-            constexpr int UPS = 16 / NB > 0 ? 16 / NB : 1;  // units per step
+            const int kb = i % NSB, kk = i / NSB;
+            sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[i], qf[kk], kk == 0 ? f16x{} : sn[kb], 0, 0, 0);
+            // exponential units spread evenly over the steps
 #pragma unroll
-            for (int uu = 0; uu < UPS; ++uu) {
-                const int u = i * UPS + uu;
-                if (u < 16) {
-                    const int blk = u & 1, r = 2 * (u >> 1);
-                    const f16x& sc = blk ? scur1 : scur0;
-                    h2 p = {(_Float16)__builtin_amdgcn_exp2f(fmaf(sc[r], a.c, -m_use)),
-                            (_Float16)__builtin_amdgcn_exp2f(fmaf(sc[r + 1], a.c, -m_use))};
-                    l_run = __builtin_amdgcn_fdot2(p, ones, l_run, false);
-                    pk[2 * blk + (r >> 3)][r & 7] = p.x;
-                    pk[2 * blk + (r >> 3)][(r & 7) + 1] = p.y;
-                }
-            }
+            for (int u = (i * NU) / NB; u < ((i + 1) * NU) / NB; ++u) exp_unit(scur, u, m_use, pk);
             __builtin_amdgcn_sched_barrier(0);
         }
 
         // ---- block C ----
-        auto vread = [&](int i) {
-            const int kstep = i / DB, db = i % DB;
-            s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + voff_a[db]));
-            s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + voff_b[db]));
-            return __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
         h8 vop[NC];
-        vop[0] = vread(0);
-        vop[1] = vread(1);
+        vop[0] = vread(vt, 0);
+        vop[1] = vread(vt, 1);
         __builtin_amdgcn_sched_barrier(0);
         float macc = -INFINITY;
+        constexpr int NMX = 8 * NSB;  // max3 units: two scores each
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
-            if (i + 2 < NC) vop[i + 2] = vread(i + 2);
+            if (i + 2 < NC) vop[i + 2] = vread(vt, i + 2);
             const int kstep = i / DB, db = i % DB;
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[i], pk[kstep], oacc[db], 0, 0, 0);
-            // row-maximum unit: two MFMAs in, 16 units of 2 scores
-            constexpr int MPS = 16 / (NC - 2) + 1;
+            // row-maximum units, starting two MFMAs in
+            if (i >= 2) {
 #pragma unroll
-            for (int uu = 0; uu < MPS; ++uu) {
-                const int u = (i - 2) * MPS + uu;
-                if (i >= 2 && u < 16) macc = vmax3(macc, sn0[u], sn1[u]);
+                for (int u = ((i - 2) * NMX) / (NC - 2); u < ((i - 1) * NMX) / (NC - 2); ++u) {
+                    const int e = 2 * u;  // scores e, e+1 of the flattened NSB x 16 registers
+                    macc = vmax3(macc, sn[e / 16][e % 16], sn[(e + 1) / 16][(e + 1) % 16]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         raise_max(wave_half_max(macc) * a.c);
-        refill(par, it);
-        scur0 = sn0;
-        scur1 = sn1;
+        refill(p, it);
+#pragma unroll
+        for (int kb = 0; kb < NSB; ++kb) scur[kb] = sn[kb];
     };
 
     // Any iteration, masked tiles and the last tile included.
-    auto iteration_tail = [&](auto par, int it) {
-        using PN = std::integral_constant<int, decltype(par)::value ^ 1>;
-        f16x snext0 = {}, snext1 = {};
-        h8 pk[4];
-        if (it + 1 < n_tiles) compute_s(kslot(PN{}), snext0, snext1);
-        exp_tile(scur0, scur1, pk);
-        compute_pv(vslot(par), pk);
-        if (it + 1 < n_tiles) raise_max(row_max(snext0, snext1, tile_key0(it + 1), true));
-        refill(par, it);
-        scur0 = snext0;
-        scur1 = snext1;
+    auto iteration_tail = [&](auto p, int it) {
+        using PN = std::integral_constant<int, decltype(p)::value + 1>;
+        f16x sn[NSB];
+#pragma unroll
+        for (int kb = 0; kb < NSB; ++kb) sn[kb] = f16x{};
+        h8 pk[KS];
+        if (it + 1 < n_tiles) compute_s(kslot(PN{}), sn);
+        exp_tile(scur, pk);
+        compute_pv(vslot(p), pk);
+        if (it + 1 < n_tiles) raise_max(row_max(sn, tile_key0(it + 1), true));
+        refill(p, it);
+#pragma unroll
+        for (int kb = 0; kb < NSB; ++kb) scur[kb] = sn[kb];
     };
 
     // tiles 0 .. n_plain-1 need no mask (a prefix of the tile sequence)
     int n_plain = n_tiles;
     if (MODE == KEYS_CAUSAL) {
-        int64_t lim = min(a.offset + q0 + 1, (int64_t)key_end);  // keys every row sees
-        n_plain = (int)max((int64_t)0, min((int64_t)n_tiles, (lim - (int64_t)tile_begin * kTileN) / kTileN));
+        const int64_t lim = min(a.offset + q0 + 1, (int64_t)key_end);  // keys every row of the tile sees
+        n_plain = (int)max((int64_t)0, min((int64_t)n_tiles, (lim - key_begin) / KT));
     } else if (MODE == KEYS_DENSE) {
-        n_plain = key_end / kTileN;
+        n_plain = key_end / KT;
     }
     int it = 0;
-    for (; it + 2 < n_plain; it += 2) {
+    for (; it + R < n_plain; it += R) {
         iteration_main(P0{}, it);
         iteration_main(P1{}, it + 1);
+        if constexpr (R > 2) iteration_main(P2{}, it + 2);
+        if constexpr (R > 3) iteration_main(P3{}, it + 3);
     }
     for (; it < n_tiles; ++it) {
-        if (it & 1)
-            iteration_tail(P1{}, it);
-        else
+        const int ph = it % R;
+        if (ph == 0)
             iteration_tail(P0{}, it);
+        else if (ph == 1)
+            iteration_tail(P1{}, it);
+        else if (ph == 2) {
+            if constexpr (R > 2) iteration_tail(P2{}, it);
+        } else {
+            if constexpr (R > 3) iteration_tail(P3{}, it);
+        }
     }
+
+    // no load into LDS may still be in flight when the workgroup's LDS is released
+    if constexpr (SRC == KV_FP16) __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
     // ---- epilogue ------------------------------------------------------------
     const float l_tot = l_run + __shfl_xor(l_run, 32);
