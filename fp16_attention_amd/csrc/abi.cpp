@@ -362,10 +362,18 @@ int kv_e4m3_paged_to_fp16(const uint8_t* k_cache, const uint8_t* v_cache, const 
                                              k_out, v_out, (hipStream_t)stream));
 }
 
+// Workspace of vsa_block_select: the FP32 pooled means [2][B*H*NB][D], then
+// (256-byte aligned) the FP64 block scores [B*H*NB][NB].
+static size_t vsa_pooled_bytes(int B, int H, int L, int D)
+{
+    return (((size_t)2 * B * H * (L / 64) * D * 4) + 255) & ~(size_t)255;
+}
+
 size_t vsa_block_select_workspace(int B, int H, int L, int D, int block)
 {
-    if (B < 1 || H < 1 || D != 128 || block != 64 || L < 64 || L % 64) return 0;
-    return (size_t)2 * B * H * (L / 64) * D * 4;
+    if (B < 1 || H < 1 || D != 128 || block != 64 || L < 64 || L % 64 || L / 64 > 1024) return 0;
+    const size_t nb = (size_t)(L / 64);
+    return vsa_pooled_bytes(B, H, L, D) + (size_t)B * H * nb * nb * 8;
 }
 
 int vsa_block_select(const uint16_t* q, const uint16_t* k, int B, int H, int L, int D, int block,
@@ -394,8 +402,9 @@ int vsa_block_select(const uint16_t* q, const uint16_t* k, int B, int H, int L, 
         for (int j = i + 1; j < 3; ++j)
             if (overlap(outs[i], outs[j])) return FA_ERR_ALIAS;
     }
-    return hip_status(fa::launch_vsa_select(q, k, B, H, L, D, topk, idx_out, score_out,
-                                            (float*)workspace, (hipStream_t)stream));
+    double* scores = score_out ? score_out : (double*)((char*)workspace + vsa_pooled_bytes(B, H, L, D));
+    return hip_status(fa::launch_vsa_select(q, k, B, H, L, D, topk, idx_out, scores, (float*)workspace,
+                                            (hipStream_t)stream));
 }
 
 int vsa_block_sparse_attn(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, const int32_t* idx,

@@ -81,8 +81,10 @@ hipError_t launch_e4m3_bridge(const uint8_t* kc, const uint8_t* vc, const int32_
                               int kv_len, float k_scale, float v_scale, uint16_t* k_out,
                               uint16_t* v_out, hipStream_t stream);
 
+// scores: FP64 [B*H*NB*NB] buffer the score kernel writes and the top-k kernel
+// reads; pooled: FP32 [2][B*H*NB][D] means.
 hipError_t launch_vsa_select(const uint16_t* q, const uint16_t* k, int B, int H, int L, int D,
-                             int topk, int32_t* idx_out, double* score_out, float* pooled,
+                             int topk, int32_t* idx_out, double* scores, float* pooled,
                              hipStream_t stream);
 
 }  // namespace fa

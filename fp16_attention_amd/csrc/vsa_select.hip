@@ -4,16 +4,21 @@
 // projections", key_quant.py / query_pool.py: the tile sum divided by the
 // valid count with one rounding, stored in FP32).
 //
-//   1. vsa_pool_kernel: qbar, kbar = RNE32(sum of a 64-row block / 64). The
-//      sum runs in FP64, which is exact for 64 FP16 values (all are integer
-//      multiples of 2^-24 below 2^16), so the lane/LDS summation order does
+//   1. vsa_pool_kernel: qbar, kbar = RNE32(sum of a 64-row block / 64). One
+//      wave per block; each lane sums 16 rows of 8 columns in FP64, which is
+//      exact for FP16 inputs (all are integer multiples of 2^-24 below 2^16,
+//      and 64 of them fit in 53 bits), so the order of the partial sums does
 //      not change the result. HBM-bound: Q and K are read once.
-//   2. vsa_score_topk_kernel: one workgroup per (b, h, query block):
-//      s[j] = sum over d ascending of qbar[d] * kbar[j][d] as an FP64 FMA
-//      chain (each FP32 x FP32 product is exact in FP64, so every step rounds
-//      exactly like "acc + product"), then a bitonic sort of (s, j) in LDS
-//      ordered by s descending and j ascending, and an in-order compaction of
-//      the first topk indices, which writes them ascending.
+//   2. vsa_scores_kernel: s[i][j] = sum over d ascending of qbar[i][d] *
+//      kbar[j][d], one FP64 FMA chain per (i, j) (each FP32 x FP32 product is
+//      exact in FP64, so every step rounds exactly like "acc + product").
+//      A workgroup computes a 64 x 64 tile of one (b, h) with the means staged
+//      in LDS d-major; each thread keeps a 4 x 4 block of chains.
+//   3. vsa_topk_kernel: one wave per query block. The scores are mapped to
+//      order-preserving 64-bit keys and a bitwise radix select finds the
+//      topk-th largest value T; the selection is every block with s > T plus
+//      the lowest-index blocks with s == T, written in ascending order with a
+//      ballot compaction.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -29,149 +34,183 @@ constexpr int kMaxNB = 1024;
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
-// grid: (B*H*NB, 2) — y selects Q (0) or K (1). 256 threads: thread t sums
-// rows 4*(t/16) .. +3 of d-chunk t%16 (8 values), then 16 partial sums per
-// column are combined in LDS.
+// grid: (B*H*NB / 4 rounded up, 2) — y selects Q (0) or K (1); 4 waves, one
+// block each. Lane l reads columns 8*(l%16) .. +7 of rows l/16 + 4i, i < 16.
 __global__ __launch_bounds__(256) void vsa_pool_kernel(const uint16_t* __restrict__ q,
-                                                       const uint16_t* __restrict__ k, int NB,
-                                                       int64_t n_bhb, float* __restrict__ pooled)
+                                                       const uint16_t* __restrict__ k, int64_t n_bhb,
+                                                       float* __restrict__ pooled)
 {
-    __shared__ double part[16][kD];
-    const int tid = threadIdx.x;
-    const int64_t bhb = blockIdx.x;  // (b*H + h) * NB + blk
+    const int lane = threadIdx.x & 63;
+    const int64_t bhb = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b*H + h) * NB + blk
+    if (bhb >= n_bhb) return;
     const int which = blockIdx.y;
     const uint16_t* src = (which ? k : q) + bhb * (int64_t)kBlock * kD;
-    const int col = tid & 15, rg = tid >> 4;
+    const int col = lane & 15, r0 = lane >> 4;
+    h8 x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = *(const h8*)(src + (r0 + 4 * i) * kD + col * 8);
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        h8 x = *(const h8*)(src + (rg * 4 + r) * kD + col * 8);
+    for (int i = 0; i < 16; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += (double)(float)x[e];
+        for (int e = 0; e < 8; ++e) acc[e] += (double)(float)x[i][e];
+    // lanes col, col+16, col+32, col+48 hold the four partial sums of a column
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        acc[e] += __shfl_xor(acc[e], 16);
+        acc[e] += __shfl_xor(acc[e], 32);
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) part[rg][col * 8 + e] = acc[e];
-    __syncthreads();
-    if (tid < kD) {
-        double s = 0.0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s += part[i][tid];
-        pooled[((int64_t)which * n_bhb + bhb) * kD + tid] = (float)(s * (1.0 / kBlock));
+    if (lane < 16) {
+        float* dst = pooled + ((int64_t)which * n_bhb + bhb) * kD + col * 8;
+        float4 lo = {(float)(acc[0] * (1.0 / kBlock)), (float)(acc[1] * (1.0 / kBlock)),
+                     (float)(acc[2] * (1.0 / kBlock)), (float)(acc[3] * (1.0 / kBlock))};
+        float4 hi = {(float)(acc[4] * (1.0 / kBlock)), (float)(acc[5] * (1.0 / kBlock)),
+                     (float)(acc[6] * (1.0 / kBlock)), (float)(acc[7] * (1.0 / kBlock))};
+        *(float4*)dst = lo;
+        *(float4*)(dst + 4) = hi;
     }
 }
 
-struct Entry {
-    double s;
-    int j;
-};
-
-// true when a ranks before c: larger score first, lower index on ties
-__device__ __forceinline__ bool before(double as, int aj, double cs, int cj)
+// grid: (ceil(NB/64)^2, B*H); 256 threads. Thread t owns query blocks
+// i0 + 4*(t/16) .. +3 and key blocks j0 + 4*(t%16) .. +3 of the tile.
+constexpr int kST = 64;  // score tile edge
+__global__ __launch_bounds__(256) void vsa_scores_kernel(const float* __restrict__ qbar,
+                                                         const float* __restrict__ kbar, int NB,
+                                                         double* __restrict__ scores)
 {
-    return as > cs || (as == cs && aj < cj);
-}
-
-template <int NP>  // sort length: power of two >= NB
-__global__ __launch_bounds__(256) void vsa_score_topk_kernel(const float* __restrict__ qbar,
-                                                             const float* __restrict__ kbar, int NB,
-                                                             int topk, int32_t* __restrict__ idx_out,
-                                                             double* __restrict__ score_out)
-{
-    __shared__ double ss[NP];
-    __shared__ int sj[NP];
-    __shared__ float qv[kD];
-    __shared__ unsigned char keep[NP];
+    __shared__ __attribute__((aligned(16))) float qs[kD][kST + 4];  // d-major: qs[d][i]
+    __shared__ __attribute__((aligned(16))) float ks[kD][kST + 4];
     const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x;       // (b*H + h) * NB + i
-    const int64_t bh = row / NB;
-    if (tid < kD) qv[tid] = qbar[row * kD + tid];
-    __syncthreads();
-
+    const int tiles = (NB + kST - 1) / kST;
+    const int i0 = (blockIdx.x / tiles) * kST, j0 = (blockIdx.x % tiles) * kST;
+    const int64_t bh = blockIdx.y;
+    const float* qb = qbar + bh * (int64_t)NB * kD;
     const float* kb = kbar + bh * (int64_t)NB * kD;
-    for (int j = tid; j < NP; j += 256) {
-        double acc = -INFINITY;
-        if (j < NB) {
-            const float* kr = kb + (int64_t)j * kD;
-            acc = 0.0;
-            for (int d = 0; d < kD; d += 4) {
-                float4 kv = *(const float4*)(kr + d);
-                acc = fma((double)qv[d], (double)kv.x, acc);
-                acc = fma((double)qv[d + 1], (double)kv.y, acc);
-                acc = fma((double)qv[d + 2], (double)kv.z, acc);
-                acc = fma((double)qv[d + 3], (double)kv.w, acc);
-            }
-            if (score_out) score_out[row * NB + j] = acc;
-        }
-        ss[j] = acc;
-        sj[j] = j;
-        keep[j] = 0;
+    // stage: thread reads float4 (4 consecutive d) of row tid/32 + 8m, writes transposed
+    for (int m = 0; m < kST / 8; ++m) {
+        const int r = (tid >> 5) + 8 * m, d4 = (tid & 31) * 4;
+        float4 qv = {0.f, 0.f, 0.f, 0.f}, kv = {0.f, 0.f, 0.f, 0.f};
+        if (i0 + r < NB) qv = *(const float4*)(qb + (int64_t)(i0 + r) * kD + d4);
+        if (j0 + r < NB) kv = *(const float4*)(kb + (int64_t)(j0 + r) * kD + d4);
+        qs[d4][r] = qv.x;
+        qs[d4 + 1][r] = qv.y;
+        qs[d4 + 2][r] = qv.z;
+        qs[d4 + 3][r] = qv.w;
+        ks[d4][r] = kv.x;
+        ks[d4 + 1][r] = kv.y;
+        ks[d4 + 2][r] = kv.z;
+        ks[d4 + 3][r] = kv.w;
     }
     __syncthreads();
-
-    // bitonic sort, "before" order
-    for (int size = 2; size <= NP; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int t = tid; t < NP / 2; t += 256) {
-                int lo = 2 * t - (t & (stride - 1));
-                int hi = lo + stride;
-                bool up = (lo & size) == 0;  // ascending-in-"before" segment
-                double a = ss[lo], c = ss[hi];
-                int aj = sj[lo], cj = sj[hi];
-                bool swap = up ? before(c, cj, a, aj) : before(a, aj, c, cj);
-                if (swap) {
-                    ss[lo] = c;
-                    ss[hi] = a;
-                    sj[lo] = cj;
-                    sj[hi] = aj;
-                }
-            }
-            __syncthreads();
-        }
+    const int ti = 4 * (tid >> 4), tj = 4 * (tid & 15);
+    double acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = 0.0;
+    for (int d = 0; d < kD; ++d) {
+        const float4 qv = *(const float4*)&qs[d][ti];
+        const float4 kv = *(const float4*)&ks[d][tj];
+        const double qd[4] = {qv.x, qv.y, qv.z, qv.w};
+        const double kd[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[a][c] = fma(qd[a], kd[c], acc[a][c]);
     }
-    for (int t = tid; t < topk; t += 256) keep[sj[t]] = 1;
-    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int i = i0 + ti + a;
+        if (i >= NB) continue;
+        double* row = scores + (bh * NB + i) * (int64_t)NB;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (j0 + tj + c < NB) row[j0 + tj + c] = acc[a][c];
+    }
+}
 
-    // in-order compaction by the first wave
-    if (tid < 64) {
-        int base = 0;
-        int32_t* out = idx_out + row * topk;
-        for (int j0 = 0; j0 < NB; j0 += 64) {
-            int j = j0 + tid;
-            bool f = j < NB && keep[j];
-            unsigned long long mask = __ballot(f);
-            int pos = base + __popcll(mask & ((1ull << tid) - 1ull));
-            if (f) out[pos] = j;
-            base += __popcll(mask);
+// Order-preserving map of a double to uint64 (larger value -> larger key);
+// -0 is folded into +0 first, so equal values compare equal.
+__device__ __forceinline__ uint64_t order_key(double s)
+{
+    s = s + 0.0;
+    const uint64_t u = __builtin_bit_cast(uint64_t, s);
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+constexpr int kPerLane = kMaxNB / 64;
+
+// grid: ceil(B*H*NB / 4); 4 waves, one query block (row) each.
+__global__ __launch_bounds__(256) void vsa_topk_kernel(const double* __restrict__ scores, int NB, int topk,
+                                                       int64_t rows, int32_t* __restrict__ idx_out)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const double* sr = scores + row * NB;
+    const int per = (NB + 63) / 64;  // keys per lane, key j = lane + 64 * m
+    uint64_t key[kPerLane];
+#pragma unroll
+    for (int m = 0; m < kPerLane; ++m) {
+        const int j = lane + 64 * m;
+        key[m] = (m < per && j < NB) ? order_key(sr[j]) : 0ull;  // key 0 is below every real key
+    }
+    // radix select: the largest T with at least topk keys >= T
+    uint64_t prefix = 0;
+    int need = topk;
+    for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t cand = prefix | (1ull << bit);
+        const uint64_t hi_mask = ~((1ull << bit) - 1ull);  // bits bit..63
+        int cnt = 0;
+#pragma unroll
+        for (int m = 0; m < kPerLane; ++m) {
+            if (m < per) cnt += __popcll(__ballot((key[m] & hi_mask) == cand && lane + 64 * m < NB));
         }
+        if (cnt >= need)
+            prefix = cand;
+        else
+            need -= cnt;
+    }
+    // prefix == T; keep keys > T, and the `need` lowest-index keys == T
+    int32_t* out = idx_out + row * topk;
+    int base = 0, eq_taken = 0;
+    for (int m = 0; m < per; ++m) {
+        const int j = lane + 64 * m;
+        const bool valid = j < NB;
+        const bool gt = valid && key[m] > prefix;
+        const bool eq = valid && key[m] == prefix;
+        const uint64_t eq_mask = __ballot(eq);
+        const int eq_before = __popcll(eq_mask & ((1ull << lane) - 1ull));
+        const bool take = gt || (eq && eq_taken + eq_before < need);
+        const uint64_t take_mask = __ballot(take);
+        if (take) out[base + __popcll(take_mask & ((1ull << lane) - 1ull))] = j;
+        base += __popcll(take_mask);
+        eq_taken += __popcll(eq_mask);
     }
 }
 
 hipError_t launch_vsa_select(const uint16_t* q, const uint16_t* k, int B, int H, int L, int D,
-                             int topk, int32_t* idx_out, double* score_out, float* pooled,
+                             int topk, int32_t* idx_out, double* scores, float* pooled,
                              hipStream_t stream)
 {
     if (D != kD) return hipErrorInvalidValue;
     const int NB = L / kBlock;
+    if (NB > kMaxNB) return hipErrorInvalidValue;
     const int64_t n_bhb = (int64_t)B * H * NB;
     if (n_bhb <= 0) return hipSuccess;
-    hipLaunchKernelGGL(vsa_pool_kernel, dim3((unsigned)n_bhb, 2), dim3(256), 0, stream, q, k, NB,
+    hipLaunchKernelGGL(vsa_pool_kernel, dim3((unsigned)((n_bhb + 3) / 4), 2), dim3(256), 0, stream, q, k,
                        n_bhb, pooled);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const float* qbar = pooled;
     const float* kbar = pooled + n_bhb * kD;
-    dim3 grid((unsigned)n_bhb);
-    if (NB <= 256)
-        hipLaunchKernelGGL(vsa_score_topk_kernel<256>, grid, dim3(256), 0, stream, qbar, kbar, NB,
-                           topk, idx_out, score_out);
-    else if (NB <= 512)
-        hipLaunchKernelGGL(vsa_score_topk_kernel<512>, grid, dim3(256), 0, stream, qbar, kbar, NB,
-                           topk, idx_out, score_out);
-    else if (NB <= kMaxNB)
-        hipLaunchKernelGGL(vsa_score_topk_kernel<kMaxNB>, grid, dim3(256), 0, stream, qbar, kbar, NB,
-                           topk, idx_out, score_out);
-    else
-        return hipErrorInvalidValue;
+    const int tiles = (NB + kST - 1) / kST;
+    hipLaunchKernelGGL(vsa_scores_kernel, dim3((unsigned)(tiles * tiles), (unsigned)(B * H)), dim3(256), 0,
+                       stream, qbar, kbar, NB, scores);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(vsa_topk_kernel, dim3((unsigned)((n_bhb + 3) / 4)), dim3(256), 0, stream, scores, NB,
+                       topk, n_bhb, idx_out);
     return hipGetLastError();
 }
 

@@ -170,8 +170,8 @@ int kv_e4m3_paged_to_fp16(const uint8_t* k_cache, const uint8_t* v_cache, const 
  * score_out: optional FP64 [B,H,NB,NB] (NULL to skip).
  * Domain: D == 128; block == 64; L % block == 0; 1 <= NB <= 1024;
  * 1 <= topk <= NB.
- * workspace: at least vsa_block_select_workspace(...) bytes (the pooled
- * means), 256-byte aligned.
+ * workspace: at least vsa_block_select_workspace(...) bytes (the FP32 pooled
+ * means, then the FP64 block scores when score_out is NULL), 256-byte aligned.
  */
 size_t vsa_block_select_workspace(int B, int H, int L, int D, int block);
 int vsa_block_select(const uint16_t* q, const uint16_t* k, int B, int H, int L, int D, int block,

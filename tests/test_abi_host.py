@@ -107,7 +107,8 @@ def test_workspace_queries_are_pure_functions_of_shape():
     assert lib.attn_fwd_prefix_causal_workspace(1, 6, 1, 256, 100, 128000) == 0  # invalid shape -> 0
     # a short key range needs no split and no workspace
     assert lib.attn_fwd_prefix_causal_workspace(1, 6, 1, 256, 64, 512) == 0
-    assert lib.vsa_block_select_workspace(1, 8, 36864, 128, 64) == 2 * 8 * 576 * 128 * 4
+    # pooled FP32 means (256-byte aligned) then the FP64 block scores
+    assert lib.vsa_block_select_workspace(1, 8, 36864, 128, 64) == 2 * 8 * 576 * 128 * 4 + 8 * 576 * 576 * 8
 
 
 def test_paged_and_bridge_rejections():
