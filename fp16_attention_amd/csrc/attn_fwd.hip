@@ -103,6 +103,7 @@ __device__ __forceinline__ int tile_off(int row, int chunk)
 }
 
 __device__ __forceinline__ float wave_half_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float wave_half_sum(float x) { return x + __shfl_xor(x, 32); }
 
 // Three-input maximum in one instruction (fmaxf chains are emitted with extra
 // NaN-quieting operations).
@@ -627,13 +628,13 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         h8 kop[NB];
         auto kread = [&](int i) { return *(const h8*)(kt + koff_s[i / NSB] + (i % NSB) * 32 * ROW); };
-        kop[0] = kread(0);
-        kop[1] = kread(1);
-        kop[2] = kread(2);
+        constexpr int PB = 3;  // K operand reads in flight
+#pragma unroll
+        for (int i = 0; i < PB; ++i) kop[i] = kread(i);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            if (i + 3 < NB) kop[i + 3] = kread(i + 3);
+            if (i + PB < NB) kop[i + PB] = kread(i + PB);
             const int kb = i % NSB, kk = i / NSB;
             sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[i], qf[kk], kk == 0 ? f16x{} : sn[kb], 0, 0, 0);
             // exponential units spread evenly over the steps
@@ -644,14 +645,15 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 
         // ---- block C ----
         h8 vop[NC];
-        vop[0] = vread(vt, 0);
-        vop[1] = vread(vt, 1);
+        constexpr int PC = 2;  // V operand reads in flight
+#pragma unroll
+        for (int i = 0; i < PC; ++i) vop[i] = vread(vt, i);
         __builtin_amdgcn_sched_barrier(0);
         float macc = -INFINITY;
         constexpr int NMX = 8 * NSB;  // max3 units: two scores each
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
-            if (i + 2 < NC) vop[i + 2] = vread(vt, i + 2);
+            if (i + PC < NC) vop[i + PC] = vread(vt, i + PC);
             const int kstep = i / DB, db = i % DB;
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[i], pk[kstep], oacc[db], 0, 0, 0);
             // row-maximum units, starting two MFMAs in
@@ -718,7 +720,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     if constexpr (SRC == KV_FP16) __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
     // ---- epilogue ------------------------------------------------------------
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = wave_half_sum(l_run);
     if (my_row >= a.Lq) return;
     const int64_t bh = (int64_t)b * a.Hq + h;
     if (SPLIT) {
