@@ -17,7 +17,7 @@ path, each timed with HIP events on the launch stream:
   * VSA block selection (pool, score, top-k), GB/s over Q and K read once
     plus the indices written, and VSA block-sparse attention, TFLOP/s over
     the selected pairs.
-HBM-bound kernels run after a 512 MiB buffer fill that evicts the 256 MB
+HBM-bound kernels run after a 512 MiB buffer read that evicts the 256 MB
 last-level cache, outside the timed events.
 
 "cpu_baseline" times the FP64 CPU oracle on a sample of query rows of the
@@ -275,9 +275,14 @@ def main():
     log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
     timer = Timer(torch)
     flush_buf = None
+    flush_sink = []
 
     def flush():
-        flush_buf.zero_()
+        # evict the 256 MB last-level cache by reading 512 MiB (a write-based
+        # flush would leave dirty lines whose write-back lands in the timed run)
+        flush_sink.append(flush_buf.sum(dtype=torch.int32))
+        if len(flush_sink) > 64:
+            flush_sink.clear()
 
     extra = {}
     result = None
@@ -317,7 +322,7 @@ def main():
         torch.cuda.empty_cache()
 
     if not args.no_extra or args.only not in (None, "dense"):
-        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        flush_buf = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
         if args.only in (None, "causal"):
             extra["prefix_causal"] = bench_causal(fa, torch, args.iters, timer)
             torch.cuda.empty_cache()

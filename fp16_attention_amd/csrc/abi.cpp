@@ -344,6 +344,7 @@ int kv_e4m3_paged_to_fp16(const uint8_t* k_cache, const uint8_t* v_cache, const 
     if (page_size != 32) return FA_ERR_UNSUPPORTED;
     if (D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
     if (B < 1 || Hkv < 1 || kv_len < 1 || num_phys_pages < 1) return FA_ERR_SHAPE;
+    if ((int64_t)B * Hkv * 2 > 65535 || kv_len > (1 << 26)) return FA_ERR_SHAPE;
     if (table_stride < (int64_t)((kv_len + 31) / 32)) return FA_ERR_SHAPE;
     if (!isfinite(k_scale) || !isfinite(v_scale)) return FA_ERR_SHAPE;
     if (((uintptr_t)k_cache & 15u) || ((uintptr_t)v_cache & 15u) || ((uintptr_t)page_table & 3u) ||

@@ -11,7 +11,8 @@
 // one token row and writes 32 bytes of FP16; consecutive threads cover
 // consecutive chunks of a row and then consecutive tokens, so both the page
 // reads (contiguous within a page when Hkv == 1) and the output writes are
-// coalesced.
+// coalesced. The grid's y dimension enumerates (batch, kv head, K or V), so
+// the per-thread index math is shifts and masks, no 64-bit division.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,26 +50,25 @@ __device__ __forceinline__ u2 convert4(uint32_t w, float scale)
     return r;
 }
 
+// grid: (ceil(kv_len * D/16 / 256), B * Hkv * 2); y = ((b * Hkv + g) * 2 + is_v).
+// Thread (x, tid) converts 16-code chunk c = x * 256 + tid of that row's
+// token range: token c / (D/16), column chunk c % (D/16) (shifts only).
 template <int D>
 __global__ __launch_bounds__(256) void e4m3_bridge_kernel(const uint8_t* __restrict__ kc,
                                                           const uint8_t* __restrict__ vc,
                                                           const int32_t* __restrict__ table,
                                                           int64_t table_stride, int num_pages,
-                                                          int B, int Hkv, int kv_len, float k_scale,
+                                                          int Hkv, int kv_len, float k_scale,
                                                           float v_scale, uint16_t* __restrict__ k_out,
                                                           uint16_t* __restrict__ v_out)
 {
-    constexpr int CPR = D / 16;  // 16-byte chunks per row
-    const int64_t rows = (int64_t)B * Hkv * kv_len;
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (gid >= rows * CPR) return;
-    const bool is_v = blockIdx.y != 0;
-    const int chunk = (int)(gid % CPR);
-    const int64_t row = gid / CPR;  // (b, g, t) in output order
-    const int t = (int)(row % kv_len);
-    const int64_t bg = row / kv_len;
-    const int g = (int)(bg % Hkv);
-    const int b = (int)(bg / Hkv);
+    constexpr int CPR = D / 16;  // 16-byte chunks per token row
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= kv_len * CPR) return;
+    const int is_v = blockIdx.y & 1;
+    const int bg = blockIdx.y >> 1;  // b * Hkv + g
+    const int g = bg % Hkv, b = bg / Hkv;
+    const int t = c / CPR, chunk = c % CPR;
 
     int page = table[(int64_t)b * table_stride + (t >> 5)];
     page = min(max(page, 0), num_pages - 1);
@@ -77,11 +77,9 @@ __global__ __launch_bounds__(256) void e4m3_bridge_kernel(const uint8_t* __restr
     const float scale = is_v ? v_scale : k_scale;
     const u2 c0 = convert4(w.x, scale), c1 = convert4(w.y, scale);
     const u2 c2 = convert4(w.z, scale), c3 = convert4(w.w, scale);
-    const u4 o0 = {c0.x, c0.y, c1.x, c1.y};
-    const u4 o1 = {c2.x, c2.y, c3.x, c3.y};
-    uint16_t* dst = (is_v ? v_out : k_out) + row * D + chunk * 16;
-    *(u4*)dst = o0;
-    *(u4*)(dst + 8) = o1;
+    uint16_t* dst = (is_v ? v_out : k_out) + ((int64_t)bg * kv_len + t) * D + chunk * 16;
+    *(u4*)dst = u4{c0.x, c0.y, c1.x, c1.y};
+    *(u4*)(dst + 8) = u4{c2.x, c2.y, c3.x, c3.y};
 }
 
 hipError_t launch_e4m3_bridge(const uint8_t* kc, const uint8_t* vc, const int32_t* table,
@@ -89,16 +87,17 @@ hipError_t launch_e4m3_bridge(const uint8_t* kc, const uint8_t* vc, const int32_
                               int kv_len, float k_scale, float v_scale, uint16_t* k_out,
                               uint16_t* v_out, hipStream_t stream)
 {
-    const int64_t threads = (int64_t)B * Hkv * kv_len * (D / 16);
-    const int64_t blocks = (threads + 255) / 256;
-    if (blocks <= 0) return hipSuccess;
-    dim3 grid((unsigned)blocks, 2);
+    const int64_t chunks = (int64_t)kv_len * (D / 16);
+    const int64_t ys = (int64_t)B * Hkv * 2;
+    if (chunks <= 0 || ys <= 0) return hipSuccess;
+    if (ys > 65535 || chunks > ((int64_t)1 << 31) - 256) return hipErrorInvalidValue;
+    dim3 grid((unsigned)((chunks + 255) / 256), (unsigned)ys);
     if (D == 128)
-        hipLaunchKernelGGL(e4m3_bridge_kernel<128>, grid, dim3(256), 0, stream, kc, vc, table,
-                           table_stride, num_pages, B, Hkv, kv_len, k_scale, v_scale, k_out, v_out);
+        hipLaunchKernelGGL(e4m3_bridge_kernel<128>, grid, dim3(256), 0, stream, kc, vc, table, table_stride,
+                           num_pages, Hkv, kv_len, k_scale, v_scale, k_out, v_out);
     else if (D == 256)
-        hipLaunchKernelGGL(e4m3_bridge_kernel<256>, grid, dim3(256), 0, stream, kc, vc, table,
-                           table_stride, num_pages, B, Hkv, kv_len, k_scale, v_scale, k_out, v_out);
+        hipLaunchKernelGGL(e4m3_bridge_kernel<256>, grid, dim3(256), 0, stream, kc, vc, table, table_stride,
+                           num_pages, Hkv, kv_len, k_scale, v_scale, k_out, v_out);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -149,9 +149,9 @@ int attn_fwd_paged_e4m3(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_ca
  * t/page_size]; one FP32 multiply then one FP16 conversion, both rounding to
  * nearest even; FP16 subnormals are kept. A NaN code becomes 0x7E00 with the
  * code's sign. Outputs are contiguous FP16 [B, Hkv, kv_len, D].
- * Domain: B, Hkv >= 1; D in {128, 256}; page_size == 32; kv_len >= 1;
- * table_stride >= ceil(kv_len / 32); page entries in [0, num_phys_pages)
- * (clamped otherwise); scales finite.
+ * Domain: B, Hkv >= 1 with 2 * B * Hkv <= 65535; D in {128, 256};
+ * page_size == 32; 1 <= kv_len <= 2^26; table_stride >= ceil(kv_len / 32);
+ * page entries in [0, num_phys_pages) (clamped otherwise); scales finite.
  */
 int kv_e4m3_paged_to_fp16(const uint8_t* k_cache, const uint8_t* v_cache, const int32_t* page_table,
                           int64_t table_stride, int num_phys_pages, int page_size, int B, int Hkv,

@@ -138,6 +138,7 @@ def test_paged_and_bridge_rejections():
     assert bridge(D=64) == fa.FA_ERR_UNSUPPORTED
     assert bridge(page_size=64) == fa.FA_ERR_UNSUPPORTED
     assert bridge(kv_len=0) == fa.FA_ERR_SHAPE
+    assert bridge(kv_len=(1 << 26) + 32) == fa.FA_ERR_SHAPE
     assert bridge(vo=O + 64) == fa.FA_ERR_ALIAS       # k_out and v_out overlap
     assert bridge(ko=B_) == fa.FA_ERR_ALIAS           # output over the cache
 
