@@ -78,6 +78,23 @@ def select_bytes(w):
     return 2 * 2 * w["B"] * w["H"] * w["L"] * w["D"] + 4 * w["B"] * w["H"] * nb * w["topk"]
 
 
+def dense_traffic(path):
+    """HBM bytes per launch of the dense kernel from the recorded rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs (scaled by a 1 GiB copy's readings), or None
+    when there is no record or the kernel source has changed since."""
+    if not os.path.exists(path):
+        return None
+    import hashlib
+    with open(path) as f:
+        t = json.load(f)
+    with open(os.path.join(ROOT, "fp16_attention_amd", "csrc", "attn_fwd.hip"), "rb") as f:
+        src = hashlib.sha256(f.read()).hexdigest()
+    if t.get("kernel_source_sha256") != src:
+        log("traffic record is for another version of attn_fwd.hip: reporting null")
+        return None
+    return t.get("attn_fwd_dense_video")
+
+
 # ------------------------------------------------------------------------------ timing
 
 class Timer:
@@ -249,8 +266,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--iters", type=int, default=10, help="timed launches of each extra workload")
-    ap.add_argument("--only", choices=["dense", "causal", "paged", "vsa"], default=None,
-                    help="run one workload only (for profiling)")
+    ap.add_argument("--only", choices=["dense", "causal", "paged", "vsa", "copy"], default=None,
+                    help="run one workload only (for profiling); 'copy' runs the plain 1 GiB "
+                         "device copy that calibrates the HBM byte counters")
     ap.add_argument("--no-extra", action="store_true", help="skip the non-headline workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=128, help="oracle rows per head for cpu_baseline")
@@ -280,12 +298,24 @@ def main():
     def flush():
         # evict the 256 MB last-level cache by reading 512 MiB (a write-based
         # flush would leave dirty lines whose write-back lands in the timed run)
-        flush_sink.append(flush_buf.sum(dtype=torch.int32))
+        flush_sink.append(flush_buf.view(torch.int64).sum())
         if len(flush_sink) > 64:
             flush_sink.clear()
 
     extra = {}
     result = None
+    if args.only == "copy":
+        # A plain copy of a known size: the kernel whose FETCH_SIZE / WRITE_SIZE
+        # readings scale the attention kernel's counters to bytes.
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        ms, _ = timer.run(lambda: dst.copy_(src), args.iters, 2)
+        gbs = 2 * src.numel() / (np.median(ms) * 1e-3) / 1e9
+        log(f"copy 1 GiB: {np.median(ms):.3f} ms  {gbs:.0f} GB/s")
+        print(json.dumps({"metric": "device copy", "partial": True, "only": "copy",
+                          "bytes_read": src.numel(), "bytes_written": dst.numel(), **stats(ms),
+                          "gbs": gbs}), flush=True)
+        return
     if args.only in (None, "dense"):
         w, qkv, out, ms, wall = bench_dense(fa, torch, None, args.steps, args.warmup, timer)
         flop = dense_flops(w)
@@ -294,11 +324,7 @@ def main():
         achieved = flop / (avg_ms * 1e-3) / 1e12
         log(f"dense: {avg_ms:.3f} ms/launch (events), {wall / args.steps * 1e3:.3f} ms/step (wall), "
             f"{achieved:.1f} TFLOP/s = {100 * achieved / MFMA_F16_PEAK_TFLOPS:.1f}% of peak")
-        traffic = None
-        if os.path.exists(args.traffic):
-            with open(args.traffic) as f:
-                t = json.load(f)
-            traffic = t.get("attn_fwd_dense_video", None)
+        traffic = dense_traffic(args.traffic)
         result = {
             "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
@@ -308,6 +334,7 @@ def main():
                        "inputs": "N(0,1) FP16, counter-based generator seed 2"},
             "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": traffic,
+                         "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                          "kernel": "attn_fwd_kernel (dense, D128)", "launch_ms_mean": avg_ms,
                          "algorithmic_flop_per_launch": flop},
         }
