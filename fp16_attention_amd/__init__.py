@@ -23,7 +23,7 @@ FA_ERR_HIP = 1000
 EXPORTS = ("fa_abi_version", "fa_error_string", "attn_fwd_dense", "attn_fwd_prefix_causal_workspace",
            "attn_fwd_prefix_causal", "attn_fwd_paged_e4m3_workspace", "attn_fwd_paged_e4m3",
            "kv_e4m3_paged_to_fp16", "vsa_block_select_workspace", "vsa_block_select",
-           "vsa_block_sparse_attn")
+           "vsa_block_sparse_attn_workspace", "vsa_block_sparse_attn")
 
 
 class FaTensor(ctypes.Structure):
@@ -51,7 +51,8 @@ _SIGS = {
     "kv_e4m3_paged_to_fp16": (_i, [_vp, _vp, _vp, _i64] + [_i] * 6 + [_f, _f, _vp, _vp, _vp]),
     "vsa_block_select_workspace": (_sz, [_i] * 5),
     "vsa_block_select": (_i, [_vp, _vp] + [_i] * 6 + [_vp, _vp, _vp, _sz, _vp]),
-    "vsa_block_sparse_attn": (_i, [FaTensor] * 4 + [_vp, _vp] + [_i] * 7 + [_f, _vp]),
+    "vsa_block_sparse_attn_workspace": (_sz, [_i] * 7),
+    "vsa_block_sparse_attn": (_i, [FaTensor] * 4 + [_vp, _vp] + [_i] * 7 + [_f, _vp, _sz, _vp]),
 }
 
 
@@ -223,7 +224,12 @@ def vsa_block_select(q, k, topk, block=64, scores=False, workspace=None, out=Non
     return (idx, s) if scores else idx
 
 
-def vsa_block_sparse_attn(q, k, v, idx, dense_prefix_qblocks=2, block=64, out=None, lse=None, scale=None):
+def vsa_block_sparse_attn_workspace(B, H, L, D, block, topk, dense_prefix_qblocks) -> int:
+    return int(load().vsa_block_sparse_attn_workspace(B, H, L, D, block, topk, dense_prefix_qblocks))
+
+
+def vsa_block_sparse_attn(q, k, v, idx, dense_prefix_qblocks=2, block=64, out=None, lse=None, scale=None,
+                          workspace=None):
     """Block-sparse attention over per-query-block KV block lists idx [B,H,L/block,topk]."""
     import torch
     _need_cuda(q, k, v, idx, out, lse)
@@ -234,6 +240,10 @@ def vsa_block_sparse_attn(q, k, v, idx, dense_prefix_qblocks=2, block=64, out=No
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     scale = default_scale(D) if scale is None else scale
+    ws = _workspace(vsa_block_sparse_attn_workspace(B, H, L, D, block, topk, dense_prefix_qblocks), q.device,
+                    workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().vsa_block_sparse_attn(_view(q), _view(k), _view(v), _view(out), idx.data_ptr(), _ptr(lse),
-                                        B, H, L, D, block, topk, dense_prefix_qblocks, scale, _stream(q)))
+                                        B, H, L, D, block, topk, dense_prefix_qblocks, scale, _ptr(ws), nbytes,
+                                        _stream(q)))
     return out

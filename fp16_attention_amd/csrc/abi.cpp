@@ -92,6 +92,37 @@ SplitPlan plan_split(int B, int Hq, int D, int q_rows, int kv_len)
     return p;
 }
 
+// Split of the dense-prefix query blocks of a block-sparse launch into key
+// segments of max(topk, ceil(NB / 16)) blocks, so that no work item is much
+// longer than a sparse query block's list; also a pure function of the shape.
+SplitPlan plan_vsa(int B, int H, int D, int NB, int topk, int dense_prefix)
+{
+    SplitPlan p;
+    p.n_qt = NB;
+    p.seg_tiles = std::max(topk, (NB + 15) / 16);
+    p.nseg = (NB + p.seg_tiles - 1) / p.seg_tiles;
+    if (dense_prefix == 0 || p.nseg <= 1) {
+        p.nseg = 1;
+        p.seg_tiles = NB;
+        p.workspace = 0;
+        return p;
+    }
+    size_t rows = (size_t)p.nseg * B * H * dense_prefix * fa::kTileN;
+    size_t o_bytes = rows * (size_t)D * 4;
+    o_bytes = (o_bytes + 255) & ~(size_t)255;
+    p.workspace = o_bytes + rows * 2 * 4;
+    return p;
+}
+
+int check_vsa_domain(int B, int H, int L, int D, int block, int topk, int dense_prefix)
+{
+    if (D != 128 || block != 64) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || L < block || L % block) return FA_ERR_SHAPE;
+    const int NB = L / block;
+    if (topk < 1 || topk > NB || dense_prefix < 0 || dense_prefix > NB) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
 int check_causal_domain(int B, int Hq, int Hkv, int D, int q_rows, int q_real, int kv_len)
 {
     if (D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
@@ -127,6 +158,7 @@ int run_causal(AttnArgs& a, fa::KvSource src, int D, int q_rows, int kv_len, voi
     a.n_qt = p.n_qt;
     a.nseg = p.nseg;
     a.seg_tiles = p.seg_tiles;
+    a.part_lq = q_rows;
     const bool split = p.nseg > 1;
     if (split) {
         size_t rows = (size_t)p.nseg * a.B * a.Hq * q_rows;
@@ -147,6 +179,7 @@ int run_causal(AttnArgs& a, fa::KvSource src, int D, int q_rows, int kv_len, voi
     m.o_sh = a.o_sh;
     m.o_ss = a.o_ss;
     m.lse = a.lse;
+    m.lse_sh = a.Lq;
     m.B = a.B;
     m.Hq = a.Hq;
     m.Lq = a.Lq;
@@ -408,19 +441,24 @@ int vsa_block_select(const uint16_t* q, const uint16_t* k, int B, int H, int L, 
                                             (hipStream_t)stream));
 }
 
+size_t vsa_block_sparse_attn_workspace(int B, int H, int L, int D, int block, int topk,
+                                       int dense_prefix_qblocks)
+{
+    if (check_vsa_domain(B, H, L, D, block, topk, dense_prefix_qblocks)) return 0;
+    return plan_vsa(B, H, D, L / block, topk, dense_prefix_qblocks).workspace;
+}
+
 int vsa_block_sparse_attn(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, const int32_t* idx,
                           float* lse, int B, int H, int L, int D, int block, int topk,
-                          int dense_prefix_qblocks, float scale, void* stream)
+                          int dense_prefix_qblocks, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream)
 {
     int rc;
     if ((rc = check_view(q)) || (rc = check_view(k)) || (rc = check_view(v)) || (rc = check_view(o)))
         return rc;
     if (!idx) return FA_ERR_NULL;
-    if (D != 128 || block != 64) return FA_ERR_UNSUPPORTED;
-    if (B < 1 || H < 1 || L < block || L % block) return FA_ERR_SHAPE;
+    if ((rc = check_vsa_domain(B, H, L, D, block, topk, dense_prefix_qblocks))) return rc;
     const int NB = L / block;
-    if (topk < 1 || topk > NB || dense_prefix_qblocks < 0 || dense_prefix_qblocks > NB)
-        return FA_ERR_SHAPE;
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SHAPE;
     if ((uintptr_t)idx & 3u) return FA_ERR_ALIGN;
     Span in[4] = {span_of(q.data, q.stride_b, q.stride_h, q.stride_s, B, H, L, D, 2),
@@ -434,6 +472,15 @@ int vsa_block_sparse_attn(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, co
         if (lse && overlap(sl, s)) return FA_ERR_ALIAS;
     }
     if (lse && overlap(sl, so)) return FA_ERR_ALIAS;
+    const SplitPlan p = plan_vsa(B, H, D, NB, topk, dense_prefix_qblocks);
+    if (p.workspace > 0) {
+        if (!workspace || workspace_bytes < p.workspace) return FA_ERR_WORKSPACE;
+        if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
+        Span ws = span_flat(workspace, (int64_t)p.workspace, 1);
+        for (const Span& s : in)
+            if (overlap(ws, s)) return FA_ERR_ALIAS;
+        if (overlap(ws, so) || (lse && overlap(ws, sl))) return FA_ERR_ALIAS;
+    }
 
     AttnArgs a;
     memset(&a, 0, sizeof(a));
@@ -458,9 +505,43 @@ int vsa_block_sparse_attn(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, co
     a.c = scale * 1.4426950408889634f;
     a.oscale = 1.f;
     a.n_qt = NB;
-    a.nseg = 1;
-    if ((rc = set_grid(a, (int64_t)B * H * NB, false))) return rc;
-    return hip_status(fa::launch_attn(a, D, fa::KV_FP16, fa::KEYS_BLOCKS, false, (hipStream_t)stream));
+    a.nseg = p.nseg;
+    a.seg_tiles = p.seg_tiles;
+    a.part_lq = dense_prefix_qblocks * block;
+    const bool split = p.nseg > 1;
+    if (split) {
+        size_t rows = (size_t)p.nseg * B * H * a.part_lq;
+        size_t o_bytes = ((rows * (size_t)D * 4) + 255) & ~(size_t)255;
+        a.o_part = (float*)workspace;
+        a.ml_part = (float*)((char*)workspace + o_bytes);
+    }
+    const int64_t per_bh = (int64_t)dense_prefix_qblocks * p.nseg + (NB - dense_prefix_qblocks);
+    if ((rc = set_grid(a, (int64_t)B * H * per_bh, true))) return rc;
+    hipError_t e = fa::launch_attn(a, D, fa::KV_FP16, fa::KEYS_BLOCKS, split, (hipStream_t)stream);
+    if (e != hipSuccess || !split) return hip_status(e);
+    // the dense-prefix rows: merge the key segments (every key is visible, so
+    // the causal offset is set past the last key)
+    fa::MergeArgs m;
+    memset(&m, 0, sizeof(m));
+    m.o_part = a.o_part;
+    m.ml_part = a.ml_part;
+    m.o = a.o;
+    m.o_sb = a.o_sb;
+    m.o_sh = a.o_sh;
+    m.o_ss = a.o_ss;
+    m.lse = lse;
+    m.lse_sh = L;
+    m.B = B;
+    m.Hq = H;
+    m.Lq = a.part_lq;
+    m.nseg = p.nseg;
+    m.seg_tiles = p.seg_tiles;
+    m.n_qt = dense_prefix_qblocks;
+    m.rows_per_tile = block;
+    m.offset = L;
+    m.Lkv = L;
+    m.oscale = 1.f;
+    return hip_status(fa::launch_merge(m, D, (hipStream_t)stream));
 }
 
 }  // extern "C"

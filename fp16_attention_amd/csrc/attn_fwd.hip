@@ -16,11 +16,12 @@
 // Work decomposition (MI355X-first, not the pages' SM70/SM121 designs):
 //   - A workgroup owns WAVES x 32 query rows of one (batch, head); every wave
 //     keeps its 32 query rows in registers as the MFMA B operand and streams
-//     64-key tiles of K and V through LDS.
-//   - LDS holds two K slots and two V slots. FP16 tiles move from HBM/L2 into
-//     LDS with buffer_load ... lds (no register staging; rows past the end of
-//     the key range read as zero through the buffer range check). E4M3 tiles
-//     are loaded into registers, decoded exactly to FP16 and written to LDS.
+//     32-key tiles of K and V through LDS.
+//   - LDS holds a ring of R K slots and R V slots. FP16 tiles move from
+//     HBM/L2 into LDS with buffer_load ... lds (no register staging; rows past
+//     the end of the key range read as zero through the buffer range check),
+//     R - 1 iterations ahead of their use. E4M3 tiles are loaded into
+//     registers, decoded exactly to FP16 and written to LDS.
 //     K and V are stored row-major with 16-byte chunks XOR-swizzled by the
 //     row, which keeps the K operand reads and the transposing V reads free of
 //     bank conflicts.
@@ -105,14 +106,12 @@ __device__ __forceinline__ int tile_off(int row, int chunk)
 __device__ __forceinline__ float wave_half_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ __forceinline__ float wave_half_sum(float x) { return x + __shfl_xor(x, 32); }
 
-// Three-input maximum in one instruction (fmaxf chains are emitted with extra
-// NaN-quieting operations).
-__device__ __forceinline__ float vmax3(float a, float b, float c)
-{
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
+// Three-input maximum; the compiler emits one v_max3_f32 per call. It must
+// stay compiled code (no inline asm): the scores it reads come straight from
+// MFMA accumulators, and only compiled instructions get the wait states that
+// a VALU read of a fresh MFMA result needs (there is no hardware interlock
+// for it).
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // Four E4M3 bytes -> four FP16 values, exactly (scale 1: every E4M3 value is
 // an FP16 value, so no rounding happens).
@@ -216,12 +215,14 @@ struct E4m3 {
 // D = 128, so two workgroups share a CU; 128 KB at D = 256), giving each
 // load three iterations to arrive: all workgroups on an XCD read the same
 // tiles at about the same time, so every tile costs them the latency of an
-// L2 miss together. Block lists use 64-key tiles (one block each); the paged
-// E4M3 source is staged through registers with two slots.
+// L2 miss together. Block lists (two 32-key tiles per selected block) use two
+// slots: their two-wave workgroups then take 32 KB, four per CU, which keeps
+// two waves on every SIMD. The paged E4M3 source is staged through registers
+// with two slots.
 // ---------------------------------------------------------------------------
 template <int D, int SRC, int MODE>
 struct Tiling {
-    static constexpr int KT = MODE == KEYS_BLOCKS ? 64 : 32;
+    static constexpr int KT = 32;
     static constexpr int R = (SRC == KV_FP16 && MODE != KEYS_BLOCKS) ? 4 : 2;
 };
 
@@ -237,7 +238,6 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     constexpr int DB = D / 32;    // 32-wide d blocks of O^T
     constexpr int TB = KT * D * 2;
     constexpr int ROW = 2 * D;    // bytes per LDS row
-    static_assert(MODE != KEYS_BLOCKS || KT == kTileN, "block lists need 64-key tiles");
     constexpr int R = Tiling<D, SRC, MODE>::R;
     static_assert(R >= 2 && R <= 4 && (SRC == KV_FP16 || R == 2), "ring depth");
     __shared__ __attribute__((aligned(1024))) unsigned char kslot0[TB];
@@ -279,17 +279,17 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         b = r / a.Hkv;
         h = g * a.group + j;
     } else if (MODE == KEYS_BLOCKS) {
-        // dense-prefix query blocks (the longest items) come first
-        const int n_dense = a.B * a.Hq * a.dense_prefix;
-        int bh;
-        if (item < n_dense) {
-            bh = item / a.dense_prefix;
-            qt = item % a.dense_prefix;
+        // items of one (b, h) are consecutive: the dense-prefix query blocks,
+        // each split into nseg key segments, then the sparse query blocks
+        const int n_dense = a.dense_prefix * a.nseg;
+        const int per_bh = n_dense + (a.nqb - a.dense_prefix);
+        const int bh = item / per_bh;
+        const int r = item % per_bh;
+        if (r < n_dense) {
+            qt = r / a.nseg;
+            seg = r % a.nseg;
         } else {
-            int r = item - n_dense;
-            int sparse = a.nqb - a.dense_prefix;
-            bh = r / sparse;
-            qt = a.dense_prefix + r % sparse;
+            qt = a.dense_prefix + (r - n_dense);
         }
         h = bh % a.Hq;
         b = bh / a.Hq;
@@ -314,9 +314,12 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         n_tiles = (key_stop - key_begin + KT - 1) / KT;
     } else if (MODE == KEYS_BLOCKS) {
         if (qt < a.dense_prefix) {
-            n_tiles = a.Lkv / KT;
+            key_begin = seg * a.seg_tiles * kTileN;
+            key_stop = min(a.Lkv, (seg + 1) * a.seg_tiles * kTileN);
+            if (key_begin >= key_stop) return;
+            n_tiles = (key_stop - key_begin) / KT;
         } else {
-            n_tiles = a.topk;
+            n_tiles = a.topk * (kTileN / KT);
             blist = a.idx + (((int64_t)b * a.Hq + h) * a.nqb + qt) * a.topk;
         }
     } else {
@@ -327,9 +330,10 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 
     auto tile_key0 = [&](int it) -> int {
         if (MODE == KEYS_BLOCKS && blist) {
-            int blk = blist[it];
+            constexpr int kPer = kTileN / KT;  // tiles per selected block
+            int blk = blist[it / kPer];
             blk = min(max(blk, 0), nblk - 1);
-            return blk * kTileN;
+            return blk * kTileN + (it % kPer) * KT;
         }
         return key_begin + it * KT;
     };
@@ -723,8 +727,10 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     const float l_tot = wave_half_sum(l_run);
     if (my_row >= a.Lq) return;
     const int64_t bh = (int64_t)b * a.Hq + h;
-    if (SPLIT) {
-        float* op = a.o_part + (((int64_t)seg * a.B * a.Hq + bh) * a.Lq + my_row) * D;
+    // block lists split only the dense-prefix query blocks
+    const bool to_part = SPLIT && (MODE != KEYS_BLOCKS || qt < a.dense_prefix);
+    if (to_part) {
+        float* op = a.o_part + (((int64_t)seg * a.B * a.Hq + bh) * a.part_lq + my_row) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -736,7 +742,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
             }
         if (hlf == 0) {
             float2 ml = {m_run, l_tot};
-            *(float2*)(a.ml_part + (((int64_t)seg * a.B * a.Hq + bh) * a.Lq + my_row) * 2) = ml;
+            *(float2*)(a.ml_part + (((int64_t)seg * a.B * a.Hq + bh) * a.part_lq + my_row) * 2) = ml;
         }
     } else {
         const float inv = a.oscale / l_tot;
@@ -801,7 +807,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const MergeArgs m)
     _Float16* out = m.o + (int64_t)b * m.o_sb + (int64_t)h * m.o_sh + (int64_t)i * m.o_ss + lane * PER;
 #pragma unroll
     for (int e = 0; e < PER; ++e) out[e] = (_Float16)(acc[e] * inv);
-    if (m.lse && lane == 0) m.lse[row_id] = (mmax + __log2f(den)) * 0.69314718055994530942f;
+    if (m.lse && lane == 0) m.lse[bh * m.lse_sh + i] = (mmax + __log2f(den)) * 0.69314718055994530942f;
 }
 
 // ---------------------------------------------------------------------------
@@ -834,8 +840,9 @@ hipError_t launch_attn(const AttnArgs& a, int D, KvSource src, KeyMode mode, boo
                        hipStream_t stream)
 {
     if (mode == KEYS_BLOCKS) {
-        if (D != 128 || src != KV_FP16 || split) return hipErrorInvalidValue;
-        return launch_one<128, 2, KV_FP16, KEYS_BLOCKS, false>(a, stream);
+        if (D != 128 || src != KV_FP16) return hipErrorInvalidValue;
+        return split ? launch_one<128, 2, KV_FP16, KEYS_BLOCKS, true>(a, stream)
+                     : launch_one<128, 2, KV_FP16, KEYS_BLOCKS, false>(a, stream);
     }
     if (D == 128) return launch_d<128>(a, src, mode, split, stream);
     if (D == 256) return launch_d<256>(a, src, mode, split, stream);

@@ -42,12 +42,15 @@ struct AttnArgs {
     int dense_prefix;
     int nqb;  // Lq / 64
 
-    // split-KV partial states (FP32): o_part [nseg][B*Hq][Lq][D] unnormalised,
-    // ml_part [nseg][B*Hq][Lq][2] = (running max in log2 units, running sum)
+    // split-KV partial states (FP32): o_part [nseg][B*Hq][part_lq][D]
+    // unnormalised, ml_part [nseg][B*Hq][part_lq][2] = (running max in log2
+    // units, running sum). part_lq = Lq for the causal prefill; for block
+    // lists only the dense-prefix query rows are split.
     float* o_part;
     float* ml_part;
     int nseg;
-    int seg_tiles;
+    int seg_tiles;  // segment length in 64-key units
+    int part_lq;
 
     int B, Hq, Hkv, group;
     int Lq, Lkv;
@@ -66,6 +69,7 @@ struct MergeArgs {
     _Float16* o;
     int64_t o_sb, o_sh, o_ss;
     float* lse;
+    int64_t lse_sh;  // LSE elements per (b, h)
     int B, Hq, Lq, nseg, seg_tiles, n_qt, rows_per_tile;
     int64_t offset;
     int Lkv;

@@ -187,10 +187,18 @@ int vsa_block_select(const uint16_t* q, const uint16_t* k, int B, int H, int L, 
  * lse: optional FP32 [B,H,L].
  * Domain: D == 128; block == 64; L % block == 0; 1 <= topk <= L/block;
  * 0 <= dense_prefix_qblocks <= L/block.
+ * workspace: at least vsa_block_sparse_attn_workspace(...) bytes, 256-byte
+ * aligned, not overlapping any operand (may be NULL when that size is 0).
+ * The dense-prefix query blocks are split into key segments whose FP32
+ * partial states (max, sum, unnormalised output) go to the workspace and are
+ * merged in segment order by a second kernel on the same stream.
  */
+size_t vsa_block_sparse_attn_workspace(int B, int H, int L, int D, int block, int topk,
+                                       int dense_prefix_qblocks);
 int vsa_block_sparse_attn(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, const int32_t* idx,
                           float* lse, int B, int H, int L, int D, int block, int topk,
-                          int dense_prefix_qblocks, float scale, void* stream);
+                          int dense_prefix_qblocks, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -109,6 +109,12 @@ def test_workspace_queries_are_pure_functions_of_shape():
     assert lib.attn_fwd_prefix_causal_workspace(1, 6, 1, 256, 64, 512) == 0
     # pooled FP32 means (256-byte aligned) then the FP64 block scores
     assert lib.vsa_block_select_workspace(1, 8, 36864, 128, 64) == 2 * 8 * 576 * 128 * 4 + 8 * 576 * 576 * 8
+    # 576 blocks, top-k 64: the two dense-prefix query blocks of each head split into 9 segments
+    rows = 9 * 8 * 2 * 64
+    assert lib.vsa_block_sparse_attn_workspace(1, 8, 36864, 128, 64, 64, 2) == rows * 128 * 4 + rows * 8
+    assert lib.vsa_block_sparse_attn_workspace(1, 8, 36864, 128, 64, 64, 0) == 0    # nothing dense
+    assert lib.vsa_block_sparse_attn_workspace(1, 8, 36864, 128, 64, 576, 2) == 0   # one segment
+    assert lib.vsa_block_sparse_attn_workspace(1, 8, 36864, 128, 32, 64, 2) == 0    # unsupported block
 
 
 def test_paged_and_bridge_rejections():
@@ -162,11 +168,33 @@ def test_vsa_rejections():
     assert select(idx=A) == fa.FA_ERR_ALIAS
 
     def sparse(**kw):
-        a = dict(topk=8, dp=2, L=4096, o=O)
+        a = dict(topk=8, dp=2, L=4096, o=O, ws=W, ws_bytes=1 << 30)
         a.update(kw)
         return lib.vsa_block_sparse_attn(T(A), T(B_), T(C), T(a["o"]), L, None, 1, 2, a["L"], 128, 64, a["topk"],
-                                         a["dp"], 0.088, None)
+                                         a["dp"], 0.088, a["ws"], a["ws_bytes"], None)
+    need = lib.vsa_block_sparse_attn_workspace(1, 2, 4096, 128, 64, 8, 2)
+    assert need == 8 * 2 * 2 * 64 * (128 + 2) * 4  # 8 segments of 8 blocks, 2 heads, 2 dense blocks
+    assert sparse(ws=0) == fa.FA_ERR_WORKSPACE
+    assert sparse(ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
+    assert sparse(ws=W + 16) == fa.FA_ERR_ALIGN
+    assert sparse(ws=C - 256) == fa.FA_ERR_ALIAS      # workspace runs into v
     assert sparse(topk=65) == fa.FA_ERR_SHAPE
     assert sparse(dp=65) == fa.FA_ERR_SHAPE
     assert sparse(dp=-1) == fa.FA_ERR_SHAPE
     assert sparse(o=C) == fa.FA_ERR_ALIAS
+
+
+def test_kernels_take_no_values_from_inline_asm():
+    """Inline asm in the kernels may only fence the compiler or pin a value to
+    a register class: the compiler inserts no hazard wait states before an asm
+    statement, so an asm that computes on an MFMA result can read it early."""
+    csrc = os.path.join(ROOT, "fp16_attention_amd", "csrc")
+    allowed = ('asm volatile("" ::: "memory")', 'asm volatile("; q fragment to AGPRs"',
+               'asm volatile("" : "+v"(a), "+v"(b))')
+    for name in sorted(os.listdir(csrc)):
+        if not name.endswith((".hip", ".h", ".cpp")):
+            continue
+        for n, line in enumerate(open(os.path.join(csrc, name)), 1):
+            code = line.split("//")[0]
+            if re.search(r"\basm\b", code):
+                assert any(a in code for a in allowed), f"{name}:{n}: {line.strip()}"
