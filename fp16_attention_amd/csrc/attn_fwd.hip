@@ -164,41 +164,58 @@ struct DirectLoader {
 };
 
 // ---------------------------------------------------------------------------
-// Paged E4M3 tiles: 16-code chunks loaded into registers, decoded to FP16 and
-// written to LDS as two 16-byte chunks. Thread tid handles chunks
-// tid + NT * i of the tile (row = chunk / (D/16), 16-code column chunk % (D/16)).
+// Paged E4M3 tiles. A 32-key tile is one page: its codes move into an LDS byte
+// slot with buffer_load ... lds (row-major, D bytes per row; wave w's j-th
+// load covers the 1 KB block (w + WAVES * j) of the tile), and the workgroup
+// then decodes the slot exactly into an FP16 tile, each thread one or two
+// 16-code chunks.
 // ---------------------------------------------------------------------------
-template <int D, int NT, int KT>
-struct E4m3 {
-    static constexpr int kChunks = KT * D / 16 / NT;  // per thread per K or V tile
+typedef __attribute__((address_space(4))) const int32_t const_i32;
 
-    static __device__ __forceinline__ void load(const AttnArgs& a, const uint8_t* cache,
-                                                const int32_t* table, int g, int key0, int key_last,
-                                                int tid, u4 (&dst)[kChunks])
+// p[i] through the scalar cache: a read-only, wave-uniform table entry.
+__device__ __forceinline__ int scalar_load(const int32_t* p, int i)
+{
+    return __builtin_bit_cast(const const_i32*, p)[i];
+}
+
+template <int D, int WAVES, int KT>
+struct ByteLoader {
+    static constexpr int kLoads = (KT * D / 1024) / WAVES;  // per wave per tile
+    int off[kLoads];
+
+    // row_stride: bytes between consecutive tokens of one kv head (Hkv * D)
+    __device__ __forceinline__ void init(int row_stride, int wave, int lane)
     {
-        const int pi0 = key0 >> 5;
-        const int pi1 = min(pi0 + 1, key_last >> 5);
-        const int p0 = min(max(table[pi0], 0), a.num_pages - 1);
-        const int p1 = min(max(table[pi1], 0), a.num_pages - 1);
-        const int cache_bytes = a.num_pages * 32 * a.Hkv * D;
-        __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)cache, 0, cache_bytes, kRsrcWord3);
 #pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            const int c = tid + NT * i;
-            const int row = c / (D / 16), c16 = c % (D / 16);
-            const int page = row < 32 ? p0 : p1;
-            const int off = ((page * 32 + (row & 31)) * a.Hkv + g) * D + c16 * 16;
-            dst[i] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        for (int j = 0; j < kLoads; ++j) {
+            const int pos = (wave + WAVES * j) * 1024 + lane * 16;
+            off[j] = (pos / D) * row_stride + pos % D;
         }
     }
 
-    static __device__ __forceinline__ void store(unsigned char* tile, const u4 (&src)[kChunks], int tid)
+    // base: the tile's first code of this kv head; bytes: the valid extent
+    // (rows * row_stride; the rest of the tile reads as zero, code +0)
+    __device__ __forceinline__ void issue(const uint8_t* base, int bytes, unsigned char* tile, int wave) const
+    {
+        __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kRsrcWord3);
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (lds_void_t*)(tile + (wave + WAVES * j) * 1024), 16, off[j], 0, 0, 0);
+    }
+};
+
+template <int D, int NT, int KT>
+struct ByteDecoder {
+    static constexpr int kChunks = KT * D / 16 / NT;  // 16-code chunks per thread per tile
+
+    static __device__ __forceinline__ void run(const unsigned char* bytes, unsigned char* tile, int tid)
     {
 #pragma unroll
         for (int i = 0; i < kChunks; ++i) {
             const int c = tid + NT * i;
             const int row = c / (D / 16), c16 = c % (D / 16);
-            const u4 w = src[i];
+            const u4 w = *(const u4*)(bytes + row * D + c16 * 16);
             const u2 a0 = e4m3x4_to_f16(w.x), a1 = e4m3x4_to_f16(w.y);
             const u2 a2 = e4m3x4_to_f16(w.z), a3 = e4m3x4_to_f16(w.w);
             *(u4*)(tile + tile_off<D>(row, 2 * c16)) = u4{a0.x, a0.y, a1.x, a1.y};
@@ -218,12 +235,15 @@ struct E4m3 {
 // L2 miss together. Block lists (two 32-key tiles per selected block) use two
 // slots: their two-wave workgroups then take 32 KB, four per CU, which keeps
 // two waves on every SIMD. The paged E4M3 source is staged through registers
-// with two slots.
+// with two slots, fed from a four-slot ring of E4M3 byte tiles (at D = 256:
+// 64 KB of FP16 slots and 64 KB of byte slots).
 // ---------------------------------------------------------------------------
 template <int D, int SRC, int MODE>
 struct Tiling {
     static constexpr int KT = 32;
     static constexpr int R = (SRC == KV_FP16 && MODE != KEYS_BLOCKS) ? 4 : 2;
+    static constexpr int RB = SRC == KV_E4M3_PAGED ? 4 : 1;  // E4M3 byte slots per K and V ring
+    static constexpr int PH = SRC == KV_E4M3_PAGED ? RB : R;  // phases of the unrolled loop
 };
 
 template <int D, int WAVES, int SRC, int MODE, bool SPLIT>
@@ -239,7 +259,11 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     constexpr int TB = KT * D * 2;
     constexpr int ROW = 2 * D;    // bytes per LDS row
     constexpr int R = Tiling<D, SRC, MODE>::R;
-    static_assert(R >= 2 && R <= 4 && (SRC == KV_FP16 || R == 2), "ring depth");
+    constexpr int RB = Tiling<D, SRC, MODE>::RB;
+    constexpr int PH = Tiling<D, SRC, MODE>::PH;
+    constexpr int BB = SRC == KV_E4M3_PAGED ? KT * D : 16;  // bytes per byte slot
+    static_assert(R >= 2 && R <= 4 && (SRC == KV_FP16 || (R == 2 && RB == 4)), "ring depth");
+    static_assert(SRC == KV_FP16 || KT == 32, "an E4M3 tile is one 32-token page");
     __shared__ __attribute__((aligned(1024))) unsigned char kslot0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char kslot1[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char kslot2[R > 2 ? TB : 16];
@@ -248,9 +272,18 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     __shared__ __attribute__((aligned(1024))) unsigned char vslot1[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char vslot2[R > 2 ? TB : 16];
     __shared__ __attribute__((aligned(1024))) unsigned char vslot3[R > 3 ? TB : 16];
-    // s_waitcnt that leaves the R-2 most recent load groups in flight
-    constexpr int kGroupLoads = 2 * DirectLoader<D, WAVES, KT>::kLoads;
-    constexpr int kVmLeft = (R - 2) * kGroupLoads;
+    __shared__ __attribute__((aligned(1024))) unsigned char kbyte0[BB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kbyte1[BB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kbyte2[BB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kbyte3[BB];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbyte0[BB];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbyte1[BB];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbyte2[BB];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbyte3[BB];
+    // s_waitcnt that leaves the (ring depth - 2) most recent load groups in flight
+    constexpr int kGroupLoads =
+        2 * (SRC == KV_FP16 ? DirectLoader<D, WAVES, KT>::kLoads : ByteLoader<D, WAVES, KT>::kLoads);
+    constexpr int kVmLeft = ((SRC == KV_FP16 ? R : RB) - 2) * kGroupLoads;
     static_assert(kVmLeft < 64, "vmcnt range");
     constexpr int kWaitGroups = (kVmLeft & 15) | ((kVmLeft >> 4) << 14) | 0x0070;  // and lgkmcnt(0)
 
@@ -343,14 +376,14 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     const _Float16* vbase = nullptr;
     const int32_t* table = nullptr;
     DirectLoader<D, WAVES, KT> dl;
-    using E8 = E4m3<D, NT, KT>;
-    u4 kst[E8::kChunks], vst[E8::kChunks];  // staged E4M3 tiles (paged source only)
+    ByteLoader<D, WAVES, KT> bl;
     if (SRC == KV_FP16) {
         kbase = a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh;
         vbase = a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh;
         dl.init(a.k_ss, a.v_ss, wave, lane);
     } else {
         table = a.table + (int64_t)b * a.table_stride;
+        bl.init(a.Hkv * D, wave, lane);
     }
     // Every load group issues the same number of loads, so that s_waitcnt
     // counts stay exact: a tile past the end is loaded with zero valid rows
@@ -367,11 +400,13 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         DirectLoader<D, WAVES, KT>::issue(vbase + (int64_t)key0 * a.v_ss, a.v_ss, dl.voff,
                                           ok ? min(KT, key_end - key0) : 0, slot, wave);
     };
-    auto load_k8 = [&](int it, u4 (&dst)[E8::kChunks]) {
-        E8::load(a, a.kc, table, g, tile_key0(it), key_last, tid, dst);
-    };
-    auto load_v8 = [&](int it, u4 (&dst)[E8::kChunks]) {
-        E8::load(a, a.vc, table, g, tile_key0(it), key_last, tid, dst);
+    // E4M3: tile it is page table[tile_key0(it) / 32] (tiles are page aligned)
+    auto issue_b = [&](const uint8_t* cache, int it, unsigned char* slot) {
+        const bool ok = it < n_tiles;
+        const int key0 = tile_key0(ok ? it : n_tiles - 1);
+        const int page = min(max(scalar_load(table, key0 >> 5), 0), a.num_pages - 1);
+        const int rows = ok ? min(KT, key_end - key0) : 0;
+        bl.issue(cache + ((int64_t)page * 32 * a.Hkv + g) * D, rows * a.Hkv * D, slot, wave);
     };
 
     // ---- Q fragment in registers: lane holds Q[row][16kk + 8hlf .. +7] ------
@@ -527,8 +562,13 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     // it+R is issued into them, so every FP16 group has R-1 iterations to
     // arrive. Invariant entering iteration it: S(it) is in scur with its
     // maximum folded into m_run; K(it+1) and V(it) are in LDS; groups
-    // it+1 .. it+R-1 are in flight (FP16). E4M3 (R = 2) writes group it+1 to
-    // LDS and stages group it+2 in registers instead.
+    // it+1 .. it+R-1 are in flight (FP16).
+    // E4M3: the codes of K(j) and V(j) live in byte slot j % RB and byte group
+    // g = {K(g+1), V(g)} is decoded during iteration g-1 into the FP16 slots
+    // (R = 2) that iteration does not read. Entering iteration it, byte group
+    // it+1 is in LDS and groups it+2 .. it+RB are in flight; at its end the
+    // slots of group it+1 are free and group it+RB+1 is issued into them, so
+    // every byte group has RB-1 iterations to arrive.
     auto kslot = [&](auto p) -> unsigned char* {
         constexpr int S = decltype(p)::value % R;
         if constexpr (S == 0) return kslot0;
@@ -543,13 +583,32 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         else if constexpr (S == 2) return vslot2;
         else return vslot3;
     };
+    auto kbslot = [&](auto p) -> unsigned char* {
+        constexpr int S = decltype(p)::value % RB;
+        if constexpr (S == 0) return kbyte0;
+        else if constexpr (S == 1) return kbyte1;
+        else if constexpr (S == 2) return kbyte2;
+        else return kbyte3;
+    };
+    auto vbslot = [&](auto p) -> unsigned char* {
+        constexpr int S = decltype(p)::value % RB;
+        if constexpr (S == 0) return vbyte0;
+        else if constexpr (S == 1) return vbyte1;
+        else if constexpr (S == 2) return vbyte2;
+        else return vbyte3;
+    };
+    using Dec = ByteDecoder<D, NT, KT>;
+    // byte group g -> its slots; phase p stands for g modulo RB
+    auto issue_group_b = [&](auto p, int g8) {
+        using PN = std::integral_constant<int, decltype(p)::value + 1>;
+        issue_b(a.kc, g8 + 1, kbslot(PN{}));
+        issue_b(a.vc, g8, vbslot(p));
+    };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     using P2 = std::integral_constant<int, 2>;
     using P3 = std::integral_constant<int, 3>;
     using P4 = std::integral_constant<int, 4>;
-    (void)kst;
-    (void)vst;
 
     if constexpr (SRC == KV_FP16) {
         issue_k(0, kslot0);
@@ -557,14 +616,16 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         issue_k(1, kslot1);
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
     } else {
-        load_k8(0, kst);
-        load_v8(0, vst);
-        E8::store(kslot0, kst, tid);
-        E8::store(vslot0, vst, tid);
-        if (n_tiles > 1) {
-            load_k8(1, kst);
-            E8::store(kslot1, kst, tid);
-        }
+        // byte groups -1 .. RB-2: K(0 .. RB-1), V(0 .. RB-2)
+        issue_b(a.kc, 0, kbyte0);
+        issue_group_b(P0{}, 0);
+        issue_group_b(P1{}, 1);
+        issue_group_b(P2{}, 2);
+        static_assert(RB == 4 || SRC == KV_FP16, "prologue written for four byte slots");
+        ring_barrier<(2 * kGroupLoads & 15) | (((2 * kGroupLoads) >> 4) << 14) | 0x0070>();
+        Dec::run(kbyte0, kslot0, tid);
+        Dec::run(kbyte1, kslot1, tid);
+        Dec::run(vbyte0, vslot0, tid);
     }
     __syncthreads();
     f16x scur[NSB];
@@ -584,17 +645,11 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
             issue_v(3, vslot(P3{}));
         }
     } else {
-        // K(2) and V(1) are written now; K(3) and V(2) are staged in registers
-        if (n_tiles > 2) {
-            load_k8(2, kst);
-            E8::store(kslot0, kst, tid);
-        }
-        if (n_tiles > 1) {
-            load_v8(1, vst);
-            E8::store(vslot1, vst, tid);
-        }
-        if (n_tiles > 3) load_k8(3, kst);
-        if (n_tiles > 2) load_v8(2, vst);
+        // groups -1 and 0 are decoded: issue groups 3 and 4 into their slots,
+        // then wait for group 1, which iteration 0 decodes
+        issue_group_b(P3{}, 3);
+        issue_group_b(P4{}, 4);
+        ring_barrier<((3 * kGroupLoads) & 15) | (((3 * kGroupLoads) >> 4) << 14) | 0x0070>();
     }
 
     // end of iteration it (phase p = it % R): wait for group it+1, then refill
@@ -606,11 +661,21 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
             issue_k(it + R + 1, kslot(PN{}));
             issue_v(it + R, vslot(p));
         } else {
-            __syncthreads();
-            if (it + 3 < n_tiles) E8::store(kslot(PN{}), kst, tid);
-            if (it + 2 < n_tiles) E8::store(vslot(p), vst, tid);
-            if (it + 4 < n_tiles) load_k8(it + 4, kst);
-            if (it + 3 < n_tiles) load_v8(it + 3, vst);
+            // byte group it+2 must be in LDS for the next iteration
+            using PG = std::integral_constant<int, decltype(p)::value + 1 + RB>;
+            ring_barrier<kWaitGroups>();
+            issue_group_b(PG{}, it + RB + 1);
+        }
+    };
+
+    // E4M3: decode byte group it+1 (K(it+2), V(it+1)) into the FP16 slots
+    // that iteration it does not read
+    auto decode_next = [&](auto p) {
+        if constexpr (SRC == KV_E4M3_PAGED) {
+            using Q1 = std::integral_constant<int, decltype(p)::value + 1>;
+            using Q2 = std::integral_constant<int, decltype(p)::value + 2>;
+            Dec::run(kbslot(Q2{}), kslot(Q2{}), tid);
+            Dec::run(vbslot(Q1{}), vslot(Q1{}), tid);
         }
     };
 
@@ -627,6 +692,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         constexpr int NC = KS * DB;   // PV MFMAs
         f16x sn[NSB];
         h8 pk[KS];
+        decode_next(p);
 
         // ---- block B ----
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
@@ -679,6 +745,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     // Any iteration, masked tiles and the last tile included.
     auto iteration_tail = [&](auto p, int it) {
         using PN = std::integral_constant<int, decltype(p)::value + 1>;
+        decode_next(p);
         f16x sn[NSB];
 #pragma unroll
         for (int kb = 0; kb < NSB; ++kb) sn[kb] = f16x{};
@@ -701,27 +768,27 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         n_plain = key_end / KT;
     }
     int it = 0;
-    for (; it + R < n_plain; it += R) {
+    for (; it + PH < n_plain; it += PH) {
         iteration_main(P0{}, it);
         iteration_main(P1{}, it + 1);
-        if constexpr (R > 2) iteration_main(P2{}, it + 2);
-        if constexpr (R > 3) iteration_main(P3{}, it + 3);
+        if constexpr (PH > 2) iteration_main(P2{}, it + 2);
+        if constexpr (PH > 3) iteration_main(P3{}, it + 3);
     }
     for (; it < n_tiles; ++it) {
-        const int ph = it % R;
+        const int ph = it % PH;
         if (ph == 0)
             iteration_tail(P0{}, it);
         else if (ph == 1)
             iteration_tail(P1{}, it);
         else if (ph == 2) {
-            if constexpr (R > 2) iteration_tail(P2{}, it);
+            if constexpr (PH > 2) iteration_tail(P2{}, it);
         } else {
-            if constexpr (R > 3) iteration_tail(P3{}, it);
+            if constexpr (PH > 3) iteration_tail(P3{}, it);
         }
     }
 
     // no load into LDS may still be in flight when the workgroup's LDS is released
-    if constexpr (SRC == KV_FP16) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
     // ---- epilogue ------------------------------------------------------------
     const float l_tot = wave_half_sum(l_run);
@@ -848,6 +915,22 @@ hipError_t launch_attn(const AttnArgs& a, int D, KvSource src, KeyMode mode, boo
     if (D == 256) return launch_d<256>(a, src, mode, split, stream);
     return hipErrorInvalidValue;
 }
+
+// Every kernel the launchers use, instantiated explicitly: the host compiler
+// otherwise left the launch stubs of the paged E4M3 kernels undefined (the
+// shared library then fails to load), with no diagnostic.
+template __global__ void attn_fwd_kernel<128, 4, KV_FP16, KEYS_DENSE, false>(const AttnArgs);
+template __global__ void attn_fwd_kernel<256, 4, KV_FP16, KEYS_DENSE, false>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 4, KV_FP16, KEYS_CAUSAL, false>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 4, KV_FP16, KEYS_CAUSAL, true>(const AttnArgs);
+template __global__ void attn_fwd_kernel<256, 4, KV_FP16, KEYS_CAUSAL, false>(const AttnArgs);
+template __global__ void attn_fwd_kernel<256, 4, KV_FP16, KEYS_CAUSAL, true>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 4, KV_E4M3_PAGED, KEYS_CAUSAL, false>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 4, KV_E4M3_PAGED, KEYS_CAUSAL, true>(const AttnArgs);
+template __global__ void attn_fwd_kernel<256, 4, KV_E4M3_PAGED, KEYS_CAUSAL, false>(const AttnArgs);
+template __global__ void attn_fwd_kernel<256, 4, KV_E4M3_PAGED, KEYS_CAUSAL, true>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 2, KV_FP16, KEYS_BLOCKS, false>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 2, KV_FP16, KEYS_BLOCKS, true>(const AttnArgs);
 
 hipError_t launch_merge(const MergeArgs& m, int D, hipStream_t stream)
 {

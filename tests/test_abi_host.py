@@ -37,6 +37,13 @@ def test_header_declarations_are_all_exported():
     assert lib.fa_abi_version() == 1
 
 
+def test_library_has_no_undefined_kernel_stubs():
+    """Every kernel launch stub the host code calls is defined in the library."""
+    out = subprocess.check_output(["nm", "-C", "--undefined-only", fa.LIB_PATH]).decode()
+    stubs = [line for line in out.splitlines() if "__device_stub__" in line]
+    assert not stubs, stubs
+
+
 def test_error_strings():
     for code in range(7):
         assert fa.error_string(code)
