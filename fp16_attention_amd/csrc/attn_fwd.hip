@@ -209,18 +209,25 @@ template <int D, int NT, int KT>
 struct ByteDecoder {
     static constexpr int kChunks = KT * D / 16 / NT;  // 16-code chunks per thread per tile
 
+    // chunk i of this thread: the 16 codes of row c / (D/16), columns 16 (c % (D/16)) ..
+    static __device__ __forceinline__ u4 read(const unsigned char* bytes, int tid, int i)
+    {
+        const int c = tid + NT * i;
+        return *(const u4*)(bytes + (c / (D / 16)) * D + (c % (D / 16)) * 16);
+    }
+    static __device__ __forceinline__ void store(unsigned char* tile, u4 w, int tid, int i)
+    {
+        const int c = tid + NT * i;
+        const int row = c / (D / 16), c16 = c % (D / 16);
+        const u2 a0 = e4m3x4_to_f16(w.x), a1 = e4m3x4_to_f16(w.y);
+        const u2 a2 = e4m3x4_to_f16(w.z), a3 = e4m3x4_to_f16(w.w);
+        *(u4*)(tile + tile_off<D>(row, 2 * c16)) = u4{a0.x, a0.y, a1.x, a1.y};
+        *(u4*)(tile + tile_off<D>(row, 2 * c16 + 1)) = u4{a2.x, a2.y, a3.x, a3.y};
+    }
     static __device__ __forceinline__ void run(const unsigned char* bytes, unsigned char* tile, int tid)
     {
 #pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            const int c = tid + NT * i;
-            const int row = c / (D / 16), c16 = c % (D / 16);
-            const u4 w = *(const u4*)(bytes + row * D + c16 * 16);
-            const u2 a0 = e4m3x4_to_f16(w.x), a1 = e4m3x4_to_f16(w.y);
-            const u2 a2 = e4m3x4_to_f16(w.z), a3 = e4m3x4_to_f16(w.w);
-            *(u4*)(tile + tile_off<D>(row, 2 * c16)) = u4{a0.x, a0.y, a1.x, a1.y};
-            *(u4*)(tile + tile_off<D>(row, 2 * c16 + 1)) = u4{a2.x, a2.y, a3.x, a3.y};
-        }
+        for (int i = 0; i < kChunks; ++i) store(tile, read(bytes, tid, i), tid, i);
     }
 };
 
@@ -692,7 +699,6 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         constexpr int NC = KS * DB;   // PV MFMAs
         f16x sn[NSB];
         h8 pk[KS];
-        decode_next(p);
 
         // ---- block B ----
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
@@ -714,10 +720,29 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         }
 
         // ---- block C ----
+        // E4M3: the code chunks of byte group it+1 are read with the first V
+        // operands and decoded into the free FP16 slots between later MFMAs
+        using Q1 = std::integral_constant<int, decltype(p)::value + 1>;
+        using Q2 = std::integral_constant<int, decltype(p)::value + 2>;
+        constexpr int NDC = SRC == KV_E4M3_PAGED ? 2 * Dec::kChunks : 0;  // decode units
+        u4 braw[NDC > 0 ? NDC : 1];
+        auto dec_unit = [&](int u) {
+            if (u < Dec::kChunks)
+                Dec::store(kslot(Q2{}), braw[u], tid, u);
+            else
+                Dec::store(vslot(Q1{}), braw[u], tid, u - Dec::kChunks);
+        };
         h8 vop[NC];
         constexpr int PC = 2;  // V operand reads in flight
 #pragma unroll
         for (int i = 0; i < PC; ++i) vop[i] = vread(vt, i);
+        if constexpr (NDC > 0) {
+#pragma unroll
+            for (int i = 0; i < Dec::kChunks; ++i) {
+                braw[i] = Dec::read(kbslot(Q2{}), tid, i);
+                braw[Dec::kChunks + i] = Dec::read(vbslot(Q1{}), tid, i);
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);
         float macc = -INFINITY;
         constexpr int NMX = 8 * NSB;  // max3 units: two scores each
@@ -732,6 +757,13 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
                 for (int u = ((i - 2) * NMX) / (NC - 2); u < ((i - 1) * NMX) / (NC - 2); ++u) {
                     const int e = 2 * u;  // scores e, e+1 of the flattened NSB x 16 registers
                     macc = vmax3(macc, sn[e / 16][e % 16], sn[(e + 1) / 16][(e + 1) % 16]);
+                }
+            }
+            // decode units, starting four MFMAs in
+            if constexpr (NDC > 0) {
+                if (i >= 4) {
+#pragma unroll
+                    for (int u = ((i - 4) * NDC) / (NC - 4); u < ((i - 3) * NDC) / (NC - 4); ++u) dec_unit(u);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
