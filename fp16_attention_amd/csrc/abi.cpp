@@ -20,8 +20,9 @@ namespace {
 using fa::AttnArgs;
 
 constexpr int kRowsPerTile = 128;  // query rows per workgroup (dense / causal)
-constexpr int kSplitTarget = 1536; // aimed-for work items of a split causal launch
-constexpr int kMinSegTiles = 16;   // at least 1024 keys per segment
+constexpr int kComputeUnits = 256; // MI355X
+constexpr int kMaxSeg = 16;        // key segments per query tile, at most
+constexpr int kMinSegUnits = 16;   // at least 1024 keys per segment
 
 struct Span {
     uintptr_t lo, hi;  // [lo, hi) in bytes
@@ -63,9 +64,13 @@ void fill_view(const fa_tensor& t, const _Float16*& p, int64_t& sb, int64_t& sh,
 }
 
 // Split-KV policy for the causal prefill: a pure function of the shape, so the
-// workspace query and the launch agree and results are reproducible.
+// workspace query and the launch agree and results are reproducible. Each
+// query tile's key range is cut into nseg near-equal segments; nseg is the
+// smallest count whose work items fill the resident workgroup slots of the
+// chip (one per CU at D = 256, two at D = 128) in whole rounds best, since a
+// last, partly filled round costs as much as a full one.
 struct SplitPlan {
-    int n_qt, nseg, seg_tiles;
+    int n_qt, nseg;
     size_t workspace;
 };
 
@@ -73,15 +78,25 @@ SplitPlan plan_split(int B, int Hq, int D, int q_rows, int kv_len)
 {
     SplitPlan p;
     p.n_qt = (q_rows + kRowsPerTile - 1) / kRowsPerTile;
-    const int max_tiles = (kv_len + fa::kTileN - 1) / fa::kTileN;
+    const int max_units = (kv_len + fa::kTileN - 1) / fa::kTileN;
     const int64_t items = (int64_t)B * Hq * p.n_qt;
-    int want = (int)std::min<int64_t>(16, std::max<int64_t>(1, (kSplitTarget + items - 1) / items));
-    int seg_tiles = std::max(kMinSegTiles, (max_tiles + want - 1) / want);
-    p.nseg = (max_tiles + seg_tiles - 1) / seg_tiles;
-    p.seg_tiles = seg_tiles;
+    const int64_t slots = (int64_t)kComputeUnits * (D == 128 ? 2 : 1);
+    auto fill = [&](int n) {
+        const int64_t work = items * n;
+        const int64_t rounds = (work + slots - 1) / slots;
+        return (double)work / (double)(rounds * slots);
+    };
+    p.nseg = 1;
+    double best = fill(1);
+    for (int n = 2; n <= kMaxSeg && fa::seg_units(max_units, n) >= kMinSegUnits; ++n) {
+        const double f = fill(n);
+        if (f > best * 1.01) {
+            best = f;
+            p.nseg = n;
+        }
+    }
     if (p.nseg <= 1) {
         p.nseg = 1;
-        p.seg_tiles = max_tiles;
         p.workspace = 0;
     } else {
         size_t rows = (size_t)p.nseg * B * Hq * q_rows;
@@ -99,11 +114,10 @@ SplitPlan plan_vsa(int B, int H, int D, int NB, int topk, int dense_prefix)
 {
     SplitPlan p;
     p.n_qt = NB;
-    p.seg_tiles = std::max(topk, (NB + 15) / 16);
-    p.nseg = (NB + p.seg_tiles - 1) / p.seg_tiles;
+    const int len = std::max(topk, (NB + 15) / 16);
+    p.nseg = (NB + len - 1) / len;
     if (dense_prefix == 0 || p.nseg <= 1) {
         p.nseg = 1;
-        p.seg_tiles = NB;
         p.workspace = 0;
         return p;
     }
@@ -157,7 +171,6 @@ int run_causal(AttnArgs& a, fa::KvSource src, int D, int q_rows, int kv_len, voi
     }
     a.n_qt = p.n_qt;
     a.nseg = p.nseg;
-    a.seg_tiles = p.seg_tiles;
     a.part_lq = q_rows;
     const bool split = p.nseg > 1;
     if (split) {
@@ -184,7 +197,6 @@ int run_causal(AttnArgs& a, fa::KvSource src, int D, int q_rows, int kv_len, voi
     m.Hq = a.Hq;
     m.Lq = a.Lq;
     m.nseg = p.nseg;
-    m.seg_tiles = p.seg_tiles;
     m.n_qt = p.n_qt;
     m.rows_per_tile = kRowsPerTile;
     m.offset = a.offset;
@@ -506,7 +518,6 @@ int vsa_block_sparse_attn(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, co
     a.oscale = 1.f;
     a.n_qt = NB;
     a.nseg = p.nseg;
-    a.seg_tiles = p.seg_tiles;
     a.part_lq = dense_prefix_qblocks * block;
     const bool split = p.nseg > 1;
     if (split) {
@@ -535,7 +546,6 @@ int vsa_block_sparse_attn(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, co
     m.Hq = H;
     m.Lq = a.part_lq;
     m.nseg = p.nseg;
-    m.seg_tiles = p.seg_tiles;
     m.n_qt = dense_prefix_qblocks;
     m.rows_per_tile = block;
     m.offset = L;

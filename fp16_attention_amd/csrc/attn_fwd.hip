@@ -348,14 +348,16 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     if (MODE == KEYS_CAUSAL) {
         const int last_row = min(q0 + M, a.Lq) - 1;
         key_end = (int)min((int64_t)a.Lkv, a.offset + last_row + 1);
-        key_begin = seg * a.seg_tiles * kTileN;
-        key_stop = min(key_end, (seg + 1) * a.seg_tiles * kTileN);
+        const int len = seg_units((key_end + kTileN - 1) / kTileN, a.nseg) * kTileN;
+        key_begin = seg * len;
+        key_stop = min(key_end, (seg + 1) * len);
         if (key_begin >= key_stop) return;  // the merge skips segments past the key range
         n_tiles = (key_stop - key_begin + KT - 1) / KT;
     } else if (MODE == KEYS_BLOCKS) {
         if (qt < a.dense_prefix) {
-            key_begin = seg * a.seg_tiles * kTileN;
-            key_stop = min(a.Lkv, (seg + 1) * a.seg_tiles * kTileN);
+            const int len = seg_units(a.Lkv / kTileN, a.nseg) * kTileN;
+            key_begin = seg * len;
+            key_stop = min(a.Lkv, (seg + 1) * len);
             if (key_begin >= key_stop) return;
             n_tiles = (key_stop - key_begin) / KT;
         } else {
@@ -704,7 +706,10 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         h8 kop[NB];
         auto kread = [&](int i) { return *(const h8*)(kt + koff_s[i / NSB] + (i % NSB) * 32 * ROW); };
-        constexpr int PB = 3;  // K operand reads in flight
+#ifndef FA_PB
+#define FA_PB 3
+#endif
+        constexpr int PB = FA_PB;  // K operand reads in flight
 #pragma unroll
         for (int i = 0; i < PB; ++i) kop[i] = kread(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -733,7 +738,10 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
                 Dec::store(vslot(Q1{}), braw[u], tid, u - Dec::kChunks);
         };
         h8 vop[NC];
-        constexpr int PC = 2;  // V operand reads in flight
+#ifndef FA_PC
+#define FA_PC 2
+#endif
+        constexpr int PC = FA_PC;  // V operand reads in flight
 #pragma unroll
         for (int i = 0; i < PC; ++i) vop[i] = vread(vt, i);
         if constexpr (NDC > 0) {
@@ -744,21 +752,28 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        float macc = -INFINITY;
+        float macc = -INFINITY, mpart = -INFINITY;
         constexpr int NMX = 8 * NSB;  // max3 units: two scores each
+#ifndef FA_MX0
+#define FA_MX0 2
+#define FA_MXS (NC - 2)
+#define FA_XCHG_EARLY 0
+#endif
+        constexpr int MX0 = FA_MX0, MXS = FA_MXS;  // steps carrying the max units
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             if (i + PC < NC) vop[i + PC] = vread(vt, i + PC);
             const int kstep = i / DB, db = i % DB;
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[i], pk[kstep], oacc[db], 0, 0, 0);
-            // row-maximum units, starting two MFMAs in
-            if (i >= 2) {
+            // row-maximum units
+            if (i >= MX0 && i < MX0 + MXS) {
 #pragma unroll
-                for (int u = ((i - 2) * NMX) / (NC - 2); u < ((i - 1) * NMX) / (NC - 2); ++u) {
+                for (int u = ((i - MX0) * NMX) / MXS; u < ((i - MX0 + 1) * NMX) / MXS; ++u) {
                     const int e = 2 * u;  // scores e, e+1 of the flattened NSB x 16 registers
                     macc = vmax3(macc, sn[e / 16][e % 16], sn[(e + 1) / 16][(e + 1) % 16]);
                 }
             }
+            if (FA_XCHG_EARLY && i == MX0 + MXS - 1) mpart = __shfl_xor(macc, 32);
             // decode units, starting four MFMAs in
             if constexpr (NDC > 0) {
                 if (i >= 4) {
@@ -768,7 +783,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        raise_max(wave_half_max(macc) * a.c);
+        raise_max((FA_XCHG_EARLY ? fmaxf(macc, mpart) : wave_half_max(macc)) * a.c);
         refill(p, it);
 #pragma unroll
         for (int kb = 0; kb < NSB; ++kb) scur[kb] = sn[kb];
@@ -882,7 +897,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const MergeArgs m)
     const int last_row = min((qt + 1) * m.rows_per_tile, m.Lq) - 1;
     const int key_end = (int)min((int64_t)m.Lkv, m.offset + last_row + 1);
     const int nt = (key_end + kTileN - 1) / kTileN;
-    const int nseg = min(m.nseg, (nt + m.seg_tiles - 1) / m.seg_tiles);
+    const int su = seg_units(nt, m.nseg);
+    const int nseg = (nt + su - 1) / su;
 
     const int64_t seg_stride = (int64_t)m.B * m.Hq * m.Lq;
     float mmax = -INFINITY;

@@ -45,11 +45,11 @@ struct AttnArgs {
     // split-KV partial states (FP32): o_part [nseg][B*Hq][part_lq][D]
     // unnormalised, ml_part [nseg][B*Hq][part_lq][2] = (running max in log2
     // units, running sum). part_lq = Lq for the causal prefill; for block
-    // lists only the dense-prefix query rows are split.
+    // lists only the dense-prefix query rows are split. A query tile whose
+    // keys span nt 64-key units has segments of seg_units(nt, nseg) units.
     float* o_part;
     float* ml_part;
     int nseg;
-    int seg_tiles;  // segment length in 64-key units
     int part_lq;
 
     int B, Hq, Hkv, group;
@@ -70,11 +70,16 @@ struct MergeArgs {
     int64_t o_sb, o_sh, o_ss;
     float* lse;
     int64_t lse_sh;  // LSE elements per (b, h)
-    int B, Hq, Lq, nseg, seg_tiles, n_qt, rows_per_tile;
+    int B, Hq, Lq, nseg, n_qt, rows_per_tile;
     int64_t offset;
     int Lkv;
     float oscale;
 };
+
+// Length, in 64-key units, of the key segments of a query tile whose keys span
+// nt units, when it is split into at most nseg segments; the last one may be
+// shorter, and the number that exist is ceil(nt / seg_units).
+__host__ __device__ inline int seg_units(int nt, int nseg) { return (nt + nseg - 1) / nseg; }
 
 hipError_t launch_attn(const AttnArgs& a, int D, KvSource src, KeyMode mode, bool split,
                        hipStream_t stream);

@@ -114,6 +114,11 @@ def test_workspace_queries_are_pure_functions_of_shape():
     assert lib.attn_fwd_prefix_causal_workspace(1, 6, 1, 256, 100, 128000) == 0  # invalid shape -> 0
     # a short key range needs no split and no workspace
     assert lib.attn_fwd_prefix_causal_workspace(1, 6, 1, 256, 64, 512) == 0
+    # 378 query tiles of D256 on one workgroup per CU: two key segments per tile
+    # fill three rounds of 256 slots best (756 items)
+    assert a == 2 * 6 * 8000 * (256 * 4 + 8)
+    # two query tiles: as many segments as 1024-key minimum segments allow (16)
+    assert lib.attn_fwd_prefix_causal_workspace(1, 2, 1, 256, 64, 16480) == 16 * 2 * 64 * (256 * 4 + 8)
     # pooled FP32 means (256-byte aligned) then the FP64 block scores
     assert lib.vsa_block_select_workspace(1, 8, 36864, 128, 64) == 2 * 8 * 576 * 128 * 4 + 8 * 576 * 576 * 8
     # 576 blocks, top-k 64: the two dense-prefix query blocks of each head split into 9 segments

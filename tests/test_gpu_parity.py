@@ -50,6 +50,8 @@ def test_dense_strided_views(lib):
     (6, 1, 256, 256, 200, 4096),   # split over the key range, padded rows
     (6, 1, 256, 128, 128, 160),    # one segment, KV tail not a multiple of 64
     (4, 2, 128, 192, 150, 2400),   # GQA groups of 2, D128
+    (2, 1, 256, 64, 64, 16480),    # 16 segments of 17 units, the last 3 units with a 32-key tail
+    (3, 1, 128, 64, 40, 9024),     # 9 segments at D128, padded rows
 ])
 def test_prefix_causal_parity(lib, Hq, Hkv, D, q_rows, q_real, kv_len):
     say(f"causal Hq{Hq} Hkv{Hkv} D{D} rows{q_rows} real{q_real} kv{kv_len} "
