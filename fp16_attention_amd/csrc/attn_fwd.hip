@@ -692,7 +692,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     // steps separated by scheduling fences: block B issues the score MFMAs of
     // tile it+1 with the exponentials of tile it between them, block C the PV
     // MFMAs of tile it with the row maximum of tile it+1 between them; every
-    // LDS operand read is issued two or three MFMAs ahead.
+    // LDS operand read is issued two to four MFMAs ahead.
     auto iteration_main = [&](auto p, int it) {
         using PN = std::integral_constant<int, decltype(p)::value + 1>;
         const unsigned char* kt = kslot(PN{});
@@ -706,10 +706,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         h8 kop[NB];
         auto kread = [&](int i) { return *(const h8*)(kt + koff_s[i / NSB] + (i % NSB) * 32 * ROW); };
-#ifndef FA_PB
-#define FA_PB 3
-#endif
-        constexpr int PB = FA_PB;  // K operand reads in flight
+        constexpr int PB = D == 256 ? 4 : 3;  // K operand reads in flight
 #pragma unroll
         for (int i = 0; i < PB; ++i) kop[i] = kread(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -738,10 +735,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
                 Dec::store(vslot(Q1{}), braw[u], tid, u - Dec::kChunks);
         };
         h8 vop[NC];
-#ifndef FA_PC
-#define FA_PC 2
-#endif
-        constexpr int PC = FA_PC;  // V operand reads in flight
+        constexpr int PC = D == 256 ? 3 : 2;  // V operand reads in flight
 #pragma unroll
         for (int i = 0; i < PC; ++i) vop[i] = vread(vt, i);
         if constexpr (NDC > 0) {
@@ -754,12 +748,14 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         __builtin_amdgcn_sched_barrier(0);
         float macc = -INFINITY, mpart = -INFINITY;
         constexpr int NMX = 8 * NSB;  // max3 units: two scores each
-#ifndef FA_MX0
-#define FA_MX0 2
-#define FA_MXS (NC - 2)
-#define FA_XCHG_EARLY 0
-#endif
-        constexpr int MX0 = FA_MX0, MXS = FA_MXS;  // steps carrying the max units
+        // Steps carrying the max units. With one wave per SIMD (D = 256) the
+        // maximum is finished in the first half of the block and its lane-half
+        // exchange is issued there, so the remaining MFMAs cover its latency;
+        // with two waves per SIMD (D = 128) the other wave covers it, and the
+        // units are better spread over the whole block.
+        constexpr bool XCHG_EARLY = D == 256;
+        constexpr int MX0 = XCHG_EARLY ? 1 : 2;
+        constexpr int MXS = XCHG_EARLY ? NC / 2 : NC - 2;
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             if (i + PC < NC) vop[i + PC] = vread(vt, i + PC);
@@ -773,7 +769,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
                     macc = vmax3(macc, sn[e / 16][e % 16], sn[(e + 1) / 16][(e + 1) % 16]);
                 }
             }
-            if (FA_XCHG_EARLY && i == MX0 + MXS - 1) mpart = __shfl_xor(macc, 32);
+            if (XCHG_EARLY && i == MX0 + MXS - 1) mpart = __shfl_xor(macc, 32);
             // decode units, starting four MFMAs in
             if constexpr (NDC > 0) {
                 if (i >= 4) {
@@ -783,7 +779,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        raise_max((FA_XCHG_EARLY ? fmaxf(macc, mpart) : wave_half_max(macc)) * a.c);
+        raise_max((XCHG_EARLY ? fmaxf(macc, mpart) : wave_half_max(macc)) * a.c);
         refill(p, it);
 #pragma unroll
         for (int kb = 0; kb < NSB; ++kb) scur[kb] = sn[kb];
