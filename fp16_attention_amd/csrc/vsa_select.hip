@@ -16,9 +16,10 @@
 //      in LDS d-major; each thread keeps a 4 x 4 block of chains.
 //   3. vsa_topk_kernel: one wave per query block. The scores are mapped to
 //      order-preserving 64-bit keys and a bitwise radix select finds the
-//      topk-th largest value T; the selection is every block with s > T plus
-//      the lowest-index blocks with s == T, written in ascending order with a
-//      ballot compaction.
+//      topk-th largest value T, stopping as soon as the keys that share T's
+//      leading bits are exactly the ones still needed; the selection is every
+//      block with s > T plus the lowest-index blocks with s == T, written in
+//      ascending order with a ballot compaction.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -155,9 +156,13 @@ __global__ __launch_bounds__(256) void vsa_topk_kernel(const double* __restrict_
         const int j = lane + 64 * m;
         key[m] = (m < per && j < NB) ? order_key(sr[j]) : 0ull;  // key 0 is below every real key
     }
-    // radix select: the largest T with at least topk keys >= T
+    // Radix select, most significant bit first: T is the largest value with
+    // at least topk keys >= T. After bits 63..b of T are fixed (in prefix),
+    // `need` more keys must come from the `match` keys whose bits 63..b equal
+    // prefix's; once match == need those are all taken and the lower bits of
+    // T no longer matter, so the walk stops there.
     uint64_t prefix = 0;
-    int need = topk;
+    int need = topk, match = NB, low = 0;  // low: bits below `low` are undecided
     for (int bit = 63; bit >= 0; --bit) {
         const uint64_t cand = prefix | (1ull << bit);
         const uint64_t hi_mask = ~((1ull << bit) - 1ull);  // bits bit..63
@@ -166,19 +171,27 @@ __global__ __launch_bounds__(256) void vsa_topk_kernel(const double* __restrict_
         for (int m = 0; m < kPerLane; ++m) {
             if (m < per) cnt += __popcll(__ballot((key[m] & hi_mask) == cand && lane + 64 * m < NB));
         }
-        if (cnt >= need)
+        if (cnt >= need) {
             prefix = cand;
-        else
+            match = cnt;
+        } else {
             need -= cnt;
+            match -= cnt;
+        }
+        low = bit;
+        if (match == need) break;
     }
-    // prefix == T; keep keys > T, and the `need` lowest-index keys == T
+    // keep keys whose bits 63..low exceed prefix's, and the `need` lowest-index
+    // keys whose bits 63..low equal them (all of them after an early stop)
     int32_t* out = idx_out + row * topk;
+    const uint64_t tp = prefix >> low;
     int base = 0, eq_taken = 0;
     for (int m = 0; m < per; ++m) {
         const int j = lane + 64 * m;
         const bool valid = j < NB;
-        const bool gt = valid && key[m] > prefix;
-        const bool eq = valid && key[m] == prefix;
+        const uint64_t kt = key[m] >> low;
+        const bool gt = valid && kt > tp;
+        const bool eq = valid && kt == tp;
         const uint64_t eq_mask = __ballot(eq);
         const int eq_before = __popcll(eq_mask & ((1ull << lane) - 1ull));
         const bool take = gt || (eq && eq_taken + eq_before < need);
