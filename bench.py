@@ -14,6 +14,8 @@ path, each timed with HIP events on the launch stream:
     over the visible pairs only;
   * the same prefill reading a paged E4M3 cache, KV256000, non-unit scales;
   * the exact paged E4M3 -> FP16 bridge, GB/s over the bytes it must move;
+  * decode: 16 new positions of all 6 heads against the same 256000-token
+    E4M3 cache, GB/s over the cache read once (HBM-bound);
   * VSA block selection (pool, score, top-k), GB/s over Q and K read once
     plus the indices written, and VSA block-sparse attention, TFLOP/s over
     the selected pairs.
@@ -71,6 +73,12 @@ def vsa_flops(w):
 def bridge_bytes(w):
     n = w["B"] * w["Hkv"] * w["kv_len"] * w["D"]
     return 2 * n + 2 * 2 * n + 4 * (w["kv_len"] // w["page_size"]) * w["B"]
+
+
+def decode_bytes(w):
+    """The cache codes of every key read once, the page table, q read and o written."""
+    return (2 * w["B"] * w["Hkv"] * w["kv_len"] * w["D"] + 4 * w["B"] * (w["kv_len"] // w["page_size"])
+            + 2 * 2 * w["B"] * w["Hq"] * w["q_rows"] * w["D"])
 
 
 def select_bytes(w):
@@ -194,7 +202,23 @@ def bench_paged(fa, torch, iters, timer, flush):
     log(f"bridge: {np.median(ms) * 1e3:.1f} us  {gbs:.0f} GB/s")
     bridge = {"workload": "exact paged E4M3 -> FP16 bridge, K and V, KV256000 D256 page32", "bytes": nb,
               **stats(ms), "gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS, "llc_flushed": True}
-    return fused, bridge
+    # decode: 16 new positions per head against the same cache, HBM-bound
+    wd = wl.PAGED_DECODE
+    qd = torch.from_numpy(wl.paged_inputs(wd, unit_scales=False)[0]).cuda()
+    ws_d = torch.empty(fa.load().attn_fwd_paged_e4m3_decode_workspace(wd["B"], wd["Hq"], wd["Hkv"], wd["D"],
+                                                                       wd["q_rows"], wd["kv_len"]),
+                       dtype=torch.uint8, device="cuda")
+    od = torch.empty_like(qd)
+    fn = lambda: fa.attn_fwd_paged_e4m3_decode(qd, dkc, dvc, dt, wd["kv_len"], wd["q_real"], ks, vs, out=od,
+                                               workspace=ws_d)
+    ms, _ = timer.run(fn, iters, 2, flush=flush)
+    nb = decode_bytes(wd)
+    gbs = nb / (np.median(ms) * 1e-3) / 1e9
+    log(f"paged decode: {np.median(ms) * 1e3:.1f} us  {gbs:.0f} GB/s")
+    decode = {"workload": wd["name"] + f" k_scale={ks:.6g} v_scale={vs:.6g}", "bytes": nb, **stats(ms),
+              "gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS, "llc_flushed": True,
+              "workspace_bytes": int(ws_d.numel())}
+    return fused, bridge, decode
 
 
 def bench_vsa(fa, torch, iters, timer, flush):
@@ -354,7 +378,8 @@ def main():
             extra["prefix_causal"] = bench_causal(fa, torch, args.iters, timer)
             torch.cuda.empty_cache()
         if args.only in (None, "paged"):
-            extra["paged_e4m3"], extra["e4m3_bridge"] = bench_paged(fa, torch, args.iters, timer, flush)
+            extra["paged_e4m3"], extra["e4m3_bridge"], extra["paged_e4m3_decode"] = bench_paged(
+                fa, torch, args.iters, timer, flush)
             torch.cuda.empty_cache()
         if args.only in (None, "vsa"):
             extra["vsa_select"], extra["vsa_sparse_attn"] = bench_vsa(fa, torch, args.iters, timer, flush)

@@ -22,6 +22,7 @@ FA_ERR_HIP = 1000
 # Every symbol include/fa16attn.h declares.
 EXPORTS = ("fa_abi_version", "fa_error_string", "attn_fwd_dense", "attn_fwd_prefix_causal_workspace",
            "attn_fwd_prefix_causal", "attn_fwd_paged_e4m3_workspace", "attn_fwd_paged_e4m3",
+           "attn_fwd_paged_e4m3_decode_workspace", "attn_fwd_paged_e4m3_decode",
            "kv_e4m3_paged_to_fp16", "vsa_block_select_workspace", "vsa_block_select",
            "vsa_block_sparse_attn_workspace", "vsa_block_sparse_attn")
 
@@ -48,6 +49,9 @@ _SIGS = {
     "attn_fwd_paged_e4m3_workspace": (_sz, [_i] * 6),
     "attn_fwd_paged_e4m3": (_i, [FaTensor, _vp, _vp, _vp, _i64, _i, _i, _f, _f, FaTensor, _vp]
                             + [_i] * 7 + [_f, _vp, _sz, _vp]),
+    "attn_fwd_paged_e4m3_decode_workspace": (_sz, [_i] * 6),
+    "attn_fwd_paged_e4m3_decode": (_i, [FaTensor, _vp, _vp, _vp, _i64, _i, _i, _f, _f, FaTensor, _vp]
+                                   + [_i] * 7 + [_f, _vp, _sz, _vp]),
     "kv_e4m3_paged_to_fp16": (_i, [_vp, _vp, _vp, _i64] + [_i] * 6 + [_f, _f, _vp, _vp, _vp]),
     "vsa_block_select_workspace": (_sz, [_i] * 5),
     "vsa_block_select": (_i, [_vp, _vp] + [_i] * 6 + [_vp, _vp, _vp, _sz, _vp]),
@@ -159,6 +163,19 @@ def attn_fwd_prefix_causal(q, k, v, q_real, out=None, lse=None, scale=None, work
 def attn_fwd_paged_e4m3(q, k_cache, v_cache, page_table, kv_len, q_real, k_scale=1.0, v_scale=1.0,
                         out=None, lse=None, scale=None, workspace=None):
     """Causal prefill reading an E4M3 paged cache [pages, 32, Hkv, D] (uint8) via an int32 page table."""
+    return _paged(False, q, k_cache, v_cache, page_table, kv_len, q_real, k_scale, v_scale, out, lse, scale,
+                  workspace)
+
+
+def attn_fwd_paged_e4m3_decode(q, k_cache, v_cache, page_table, kv_len, q_real=None, k_scale=1.0, v_scale=1.0,
+                               out=None, lse=None, scale=None, workspace=None):
+    """Decode: q [B,Hq,1..16,D] new positions against an E4M3 paged cache (see attn_fwd_paged_e4m3)."""
+    q_real = q.shape[2] if q_real is None else q_real
+    return _paged(True, q, k_cache, v_cache, page_table, kv_len, q_real, k_scale, v_scale, out, lse, scale,
+                  workspace)
+
+
+def _paged(decode, q, k_cache, v_cache, page_table, kv_len, q_real, k_scale, v_scale, out, lse, scale, workspace):
     import torch
     _need_cuda(q, k_cache, v_cache, page_table, out, lse)
     B, Hq, q_rows, D = q.shape
@@ -171,13 +188,14 @@ def attn_fwd_paged_e4m3(q, k_cache, v_cache, page_table, kv_len, q_real, k_scale
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     scale = default_scale(D) if scale is None else scale
-    ws = _workspace(int(load().attn_fwd_paged_e4m3_workspace(B, Hq, Hkv, D, q_rows, kv_len)), q.device,
-                    workspace)
+    lib = load()
+    wsq = lib.attn_fwd_paged_e4m3_decode_workspace if decode else lib.attn_fwd_paged_e4m3_workspace
+    fn = lib.attn_fwd_paged_e4m3_decode if decode else lib.attn_fwd_paged_e4m3
+    ws = _workspace(int(wsq(B, Hq, Hkv, D, q_rows, kv_len)), q.device, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(load().attn_fwd_paged_e4m3(_view(q), k_cache.data_ptr(), v_cache.data_ptr(), page_table.data_ptr(),
-                                      page_table.stride(0), pages, page_size, k_scale, v_scale, _view(out),
-                                      _ptr(lse), B, Hq, Hkv, D, q_rows, q_real, kv_len, scale, _ptr(ws), nbytes,
-                                      _stream(q)))
+    _check(fn(_view(q), k_cache.data_ptr(), v_cache.data_ptr(), page_table.data_ptr(), page_table.stride(0),
+              pages, page_size, k_scale, v_scale, _view(out), _ptr(lse), B, Hq, Hkv, D, q_rows, q_real, kv_len,
+              scale, _ptr(ws), nbytes, _stream(q)))
     return out
 
 

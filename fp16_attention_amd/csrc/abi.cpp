@@ -107,6 +107,35 @@ SplitPlan plan_split(int B, int Hq, int D, int q_rows, int kv_len)
     return p;
 }
 
+// Split-KV policy for decode: one work item per (b, kv head, segment), as many
+// segments (of at least 1024 keys) as it takes to give every CU its own
+// stream of the cache; a pure function of the shape.
+constexpr int kDecodeRows = 128;  // packed (head, position) rows per work item
+SplitPlan plan_decode(int B, int Hq, int Hkv, int D, int q_rows, int kv_len)
+{
+    SplitPlan p;
+    p.n_qt = 1;
+    const int max_units = (kv_len + fa::kTileN - 1) / fa::kTileN;
+    const int64_t slots = (int64_t)kComputeUnits * (D == 128 ? 2 : 1);
+    const int64_t want = (slots + (int64_t)B * Hkv - 1) / ((int64_t)B * Hkv);
+    const int cap = std::max(1, max_units / kMinSegUnits);
+    p.nseg = (int)std::min<int64_t>(std::max<int64_t>(1, want), cap);
+    size_t rows = (size_t)p.nseg * B * Hq * q_rows;
+    size_t o_bytes = ((rows * (size_t)D * 4) + 255) & ~(size_t)255;
+    p.workspace = o_bytes + rows * 2 * 4;
+    return p;
+}
+
+int check_decode_domain(int B, int Hq, int Hkv, int D, int q_rows, int q_real, int kv_len)
+{
+    if (D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || Hkv < 1 || Hq < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (q_rows < 1 || q_rows > 16 || (Hq / Hkv) * q_rows > kDecodeRows) return FA_ERR_SHAPE;
+    if (q_real < 1 || q_real > q_rows) return FA_ERR_SHAPE;
+    if (kv_len <= q_real || kv_len > 262144 || kv_len % 32 != 0) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
 // Split of the dense-prefix query blocks of a block-sparse launch into key
 // segments of max(topk, ceil(NB / 16)) blocks, so that no work item is much
 // longer than a sparse query block's list; also a pure function of the shape.
@@ -155,12 +184,11 @@ int set_grid(AttnArgs& a, int64_t items, bool xcd)
     return FA_OK;
 }
 
-// Shared body of the two causal entry points.
-int run_causal(AttnArgs& a, fa::KvSource src, int D, int q_rows, int kv_len, void* workspace,
-               size_t workspace_bytes, hipStream_t stream, const Span* inputs, int n_inputs,
-               Span out_span, Span lse_span)
+// Shared body of the causal entry points (prefill and decode).
+int run_causal(AttnArgs& a, fa::KvSource src, fa::KeyMode mode, const SplitPlan& p, int D, int q_rows,
+               void* workspace, size_t workspace_bytes, hipStream_t stream, const Span* inputs,
+               int n_inputs, Span out_span, Span lse_span)
 {
-    SplitPlan p = plan_split(a.B, a.Hq, D, q_rows, kv_len);
     if (p.workspace > 0) {
         if (!workspace || workspace_bytes < p.workspace) return FA_ERR_WORKSPACE;
         if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
@@ -172,16 +200,18 @@ int run_causal(AttnArgs& a, fa::KvSource src, int D, int q_rows, int kv_len, voi
     a.n_qt = p.n_qt;
     a.nseg = p.nseg;
     a.part_lq = q_rows;
-    const bool split = p.nseg > 1;
+    const bool decode = mode == fa::KEYS_DECODE;
+    const bool split = p.nseg > 1 || decode;
     if (split) {
         size_t rows = (size_t)p.nseg * a.B * a.Hq * q_rows;
         size_t o_bytes = ((rows * (size_t)D * 4) + 255) & ~(size_t)255;
         a.o_part = (float*)workspace;
         a.ml_part = (float*)((char*)workspace + o_bytes);
     }
-    int rc = set_grid(a, (int64_t)a.B * a.Hq * p.n_qt * p.nseg, true);
+    const int64_t items = decode ? (int64_t)a.B * a.Hkv * p.nseg : (int64_t)a.B * a.Hq * p.n_qt * p.nseg;
+    int rc = set_grid(a, items, true);
     if (rc) return rc;
-    hipError_t e = fa::launch_attn(a, D, src, fa::KEYS_CAUSAL, split, stream);
+    hipError_t e = fa::launch_attn(a, D, src, mode, split, stream);
     if (e != hipSuccess || !split) return hip_status(e);
     fa::MergeArgs m;
     memset(&m, 0, sizeof(m));
@@ -198,7 +228,7 @@ int run_causal(AttnArgs& a, fa::KvSource src, int D, int q_rows, int kv_len, voi
     m.Lq = a.Lq;
     m.nseg = p.nseg;
     m.n_qt = p.n_qt;
-    m.rows_per_tile = kRowsPerTile;
+    m.rows_per_tile = decode ? q_rows : kRowsPerTile;
     m.offset = a.offset;
     m.Lkv = a.Lkv;
     m.oscale = a.oscale;
@@ -315,8 +345,8 @@ int attn_fwd_prefix_causal(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, f
     a.offset = (int64_t)kv_len - q_real;
     a.c = scale * 1.4426950408889634f;
     a.oscale = 1.f;
-    return run_causal(a, fa::KV_FP16, D, q_rows, kv_len, workspace, workspace_bytes,
-                      (hipStream_t)stream, in, 3, so, sl);
+    return run_causal(a, fa::KV_FP16, fa::KEYS_CAUSAL, plan_split(B, Hq, D, q_rows, kv_len), D, q_rows,
+                      workspace, workspace_bytes, (hipStream_t)stream, in, 3, so, sl);
 }
 
 size_t attn_fwd_paged_e4m3_workspace(int B, int Hq, int Hkv, int D, int q_rows, int kv_len)
@@ -324,17 +354,23 @@ size_t attn_fwd_paged_e4m3_workspace(int B, int Hq, int Hkv, int D, int q_rows, 
     return attn_fwd_prefix_causal_workspace(B, Hq, Hkv, D, q_rows, kv_len);
 }
 
-int attn_fwd_paged_e4m3(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_cache,
-                        const int32_t* page_table, int64_t table_stride, int num_phys_pages,
-                        int page_size, float k_scale, float v_scale, fa_tensor o, float* lse, int B,
-                        int Hq, int Hkv, int D, int q_rows, int q_real, int kv_len, float scale,
-                        void* workspace, size_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Shared body of the paged E4M3 entry points (prefill and decode).
+int run_paged(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_cache, const int32_t* page_table,
+              int64_t table_stride, int num_phys_pages, int page_size, float k_scale, float v_scale,
+              fa_tensor o, float* lse, int B, int Hq, int Hkv, int D, int q_rows, int q_real, int kv_len,
+              float scale, void* workspace, size_t workspace_bytes, void* stream, bool decode)
 {
     int rc;
     if ((rc = check_view(q)) || (rc = check_view(o))) return rc;
     if (!k_cache || !v_cache || !page_table) return FA_ERR_NULL;
     if (page_size != 32) return FA_ERR_UNSUPPORTED;
-    if ((rc = check_causal_domain(B, Hq, Hkv, D, q_rows, q_real, kv_len))) return rc;
+    rc = decode ? check_decode_domain(B, Hq, Hkv, D, q_rows, q_real, kv_len)
+                : check_causal_domain(B, Hq, Hkv, D, q_rows, q_real, kv_len);
+    if (rc) return rc;
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SHAPE;
     if (!(k_scale > 0.f) || !isfinite(k_scale) || !(v_scale > 0.f) || !isfinite(v_scale))
         return FA_ERR_SHAPE;
@@ -376,8 +412,41 @@ int attn_fwd_paged_e4m3(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_ca
     a.offset = (int64_t)kv_len - q_real;
     a.c = scale * k_scale * 1.4426950408889634f;
     a.oscale = v_scale;
-    return run_causal(a, fa::KV_E4M3_PAGED, D, q_rows, kv_len, workspace, workspace_bytes,
-                      (hipStream_t)stream, in, 4, so, sl);
+    const SplitPlan p = decode ? plan_decode(B, Hq, Hkv, D, q_rows, kv_len) : plan_split(B, Hq, D, q_rows, kv_len);
+    return run_causal(a, fa::KV_E4M3_PAGED, decode ? fa::KEYS_DECODE : fa::KEYS_CAUSAL, p, D, q_rows,
+                      workspace, workspace_bytes, (hipStream_t)stream, in, 4, so, sl);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_paged_e4m3(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_cache,
+                        const int32_t* page_table, int64_t table_stride, int num_phys_pages,
+                        int page_size, float k_scale, float v_scale, fa_tensor o, float* lse, int B,
+                        int Hq, int Hkv, int D, int q_rows, int q_real, int kv_len, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream)
+{
+    return run_paged(q, k_cache, v_cache, page_table, table_stride, num_phys_pages, page_size, k_scale, v_scale,
+                     o, lse, B, Hq, Hkv, D, q_rows, q_real, kv_len, scale, workspace, workspace_bytes, stream,
+                     false);
+}
+
+size_t attn_fwd_paged_e4m3_decode_workspace(int B, int Hq, int Hkv, int D, int q_rows, int kv_len)
+{
+    if (check_decode_domain(B, Hq, Hkv, D, q_rows, 1, kv_len)) return 0;
+    return plan_decode(B, Hq, Hkv, D, q_rows, kv_len).workspace;
+}
+
+int attn_fwd_paged_e4m3_decode(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_cache,
+                               const int32_t* page_table, int64_t table_stride, int num_phys_pages,
+                               int page_size, float k_scale, float v_scale, fa_tensor o, float* lse, int B,
+                               int Hq, int Hkv, int D, int q_rows, int q_real, int kv_len, float scale,
+                               void* workspace, size_t workspace_bytes, void* stream)
+{
+    return run_paged(q, k_cache, v_cache, page_table, table_stride, num_phys_pages, page_size, k_scale, v_scale,
+                     o, lse, B, Hq, Hkv, D, q_rows, q_real, kv_len, scale, workspace, workspace_bytes, stream,
+                     true);
 }
 
 int kv_e4m3_paged_to_fp16(const uint8_t* k_cache, const uint8_t* v_cache, const int32_t* page_table,

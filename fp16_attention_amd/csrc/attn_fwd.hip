@@ -308,7 +308,15 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     if (item >= a.n_items) return;
 
     int b, h, qt, seg = 0;
-    if (MODE == KEYS_CAUSAL) {
+    constexpr bool CAUSAL = MODE == KEYS_CAUSAL || MODE == KEYS_DECODE;
+    if (MODE == KEYS_DECODE) {
+        // (b, kv head, key segment); h is the group's first query head
+        seg = item % a.nseg;
+        const int r = item / a.nseg;
+        b = r / a.Hkv;
+        h = (r % a.Hkv) * a.group;
+        qt = 0;
+    } else if (MODE == KEYS_CAUSAL) {
         int j = item % a.group;
         int r = item / a.group;
         qt = r % a.n_qt;
@@ -345,7 +353,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     // keys [key_begin, key_stop) are streamed; key_end bounds every row's keys
     int key_begin = 0, key_stop = a.Lkv, key_end = a.Lkv, n_tiles;
     const int32_t* blist = nullptr;
-    if (MODE == KEYS_CAUSAL) {
+    if (CAUSAL) {
         const int last_row = min(q0 + M, a.Lq) - 1;
         key_end = (int)min((int64_t)a.Lkv, a.offset + last_row + 1);
         const int len = seg_units((key_end + kTileN - 1) / kTileN, a.nseg) * kTileN;
@@ -418,12 +426,23 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         bl.issue(cache + ((int64_t)page * 32 * a.Hkv + g) * D, rows * a.Hkv * D, slot, wave);
     };
 
+    // ---- this lane's query row: head qh, position my_row ------------------------
+    // Decode packs the group's heads: tile row r is head h + r / Lq, position
+    // r % Lq; rows past the group are computed on a clamped head and dropped.
+    int my_row = q0 + wave * kRowsPerWave + l32, qh = h;
+    bool row_ok = my_row < a.Lq;
+    if (MODE == KEYS_DECODE) {
+        const int r = my_row, j = r / a.Lq;
+        my_row = r - j * a.Lq;
+        qh = h + min(j, a.group - 1);
+        row_ok = j < a.group;
+    }
+
     // ---- Q fragment in registers: lane holds Q[row][16kk + 8hlf .. +7] ------
-    const int my_row = q0 + wave * kRowsPerWave + l32;
     h8 qf[KK];
     {
         int row = min(my_row, a.Lq - 1);
-        const _Float16* qp = a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + (int64_t)row * a.q_ss;
+        const _Float16* qp = a.q + (int64_t)b * a.q_sb + (int64_t)qh * a.q_sh + (int64_t)row * a.q_ss;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const h8*)(qp + 16 * kk + 8 * hlf);
         // With D = 256 the FP32 output accumulators take half the register
@@ -496,13 +515,13 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     // Mask the keys a row may not see (register r of score block kb holds key
     // kb*32 + 8(r/4) + 4hlf + r%4), then return the row maximum times c.
     auto tile_needs_mask = [&](int key0) -> bool {
-        if (MODE == KEYS_CAUSAL) return (int64_t)key0 + KT > a.offset + q0 + 1 || key0 + KT > key_end;
+        if (CAUSAL) return (int64_t)key0 + KT > a.offset + q0 + 1 || key0 + KT > key_end;
         if (MODE == KEYS_DENSE) return key0 + KT > key_end;
         return false;
     };
     auto row_max = [&](f16x (&s)[NSB], int key0, bool masked) -> float {
         if (masked && tile_needs_mask(key0)) {
-            const int64_t lim = (MODE == KEYS_CAUSAL) ? min((int64_t)key_last, a.offset + my_row) : (int64_t)key_last;
+            const int64_t lim = CAUSAL ? min((int64_t)key_last, a.offset + my_row) : (int64_t)key_last;
             const int64_t rel = lim - key0 - 4 * hlf;  // mask register r when 8(r/4) + r%4 + 32kb > rel
 #pragma unroll
             for (int kb = 0; kb < NSB; ++kb)
@@ -804,7 +823,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 
     // tiles 0 .. n_plain-1 need no mask (a prefix of the tile sequence)
     int n_plain = n_tiles;
-    if (MODE == KEYS_CAUSAL) {
+    if (CAUSAL) {
         const int64_t lim = min(a.offset + q0 + 1, (int64_t)key_end);  // keys every row of the tile sees
         n_plain = (int)max((int64_t)0, min((int64_t)n_tiles, (lim - key_begin) / KT));
     } else if (MODE == KEYS_DENSE) {
@@ -835,8 +854,8 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 
     // ---- epilogue ------------------------------------------------------------
     const float l_tot = wave_half_sum(l_run);
-    if (my_row >= a.Lq) return;
-    const int64_t bh = (int64_t)b * a.Hq + h;
+    if (!row_ok) return;
+    const int64_t bh = (int64_t)b * a.Hq + qh;
     // block lists split only the dense-prefix query blocks
     const bool to_part = SPLIT && (MODE != KEYS_BLOCKS || qt < a.dense_prefix);
     if (to_part) {
@@ -856,7 +875,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         }
     } else {
         const float inv = a.oscale / l_tot;
-        _Float16* op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)my_row * a.o_ss;
+        _Float16* op = a.o + (int64_t)b * a.o_sb + (int64_t)qh * a.o_sh + (int64_t)my_row * a.o_ss;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -921,6 +940,72 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const MergeArgs m)
     if (m.lse && lane == 0) m.lse[bh * m.lse_sh + i] = (mmax + __log2f(den)) * 0.69314718055994530942f;
 }
 
+// The same merge for splits with many segments (decode): one workgroup per
+// (query row, 64 output columns). The segment weights 2^(m_s - M) are formed
+// once in LDS; wave w then sums segments w, w + 4, ... for its lane's column,
+// and the four partial sums are added in wave order, so the result is still
+// fixed run to run.
+constexpr int kWideMaxSeg = 1024;
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_wide_kernel(const MergeArgs m)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int NCH = D / 64;
+    const int64_t row_id = blockIdx.x / NCH;
+    const int col = (blockIdx.x % NCH) * 64 + lane;
+    const int i = (int)(row_id % m.Lq);
+    const int64_t bh = row_id / m.Lq;
+    const int b = (int)(bh / m.Hq), h = (int)(bh % m.Hq);
+    const int qt = i / m.rows_per_tile;
+    const int last_row = min((qt + 1) * m.rows_per_tile, m.Lq) - 1;
+    const int key_end = (int)min((int64_t)m.Lkv, m.offset + last_row + 1);
+    const int nt = (key_end + kTileN - 1) / kTileN;
+    const int su = seg_units(nt, m.nseg);
+    const int nseg = (nt + su - 1) / su;  // <= kWideMaxSeg (checked at launch)
+    const int64_t seg_stride = (int64_t)m.B * m.Hq * m.Lq;
+
+    __shared__ float wgt[kWideMaxSeg];
+    __shared__ float red[4];
+    __shared__ float part[4][64];
+    // M = max of the segment maxima
+    float mx = -INFINITY;
+    for (int s = tid; s < nseg; s += 256) {
+        const float ms = m.ml_part[(s * seg_stride + row_id) * 2];
+        wgt[s] = ms;
+        mx = fmaxf(mx, ms);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    const float mmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    // weights, and sum w_s l_s (each thread its segments, then in wave order)
+    float den = 0.f;
+    for (int s = tid; s < nseg; s += 256) {
+        const float ls = m.ml_part[(s * seg_stride + row_id) * 2 + 1];
+        const float w = ls == 0.f ? 0.f : __builtin_amdgcn_exp2f(wgt[s] - mmax);  // no visible key: no weight
+        wgt[s] = w;
+        den += w * ls;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
+    if (lane == 0) red[wave] = den;
+    __syncthreads();
+    const float dsum = ((red[0] + red[1]) + red[2]) + red[3];
+
+    float acc = 0.f;
+    const float* op = m.o_part + row_id * D + col;
+#pragma unroll 8
+    for (int s = wave; s < nseg; s += 4) acc += wgt[s] * op[s * seg_stride * D];
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    const float sum = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+    m.o[(int64_t)b * m.o_sb + (int64_t)h * m.o_sh + (int64_t)i * m.o_ss + col] = (_Float16)(sum * (m.oscale / dsum));
+    if (m.lse && col == 0) m.lse[bh * m.lse_sh + i] = (mmax + __log2f(dsum)) * 0.69314718055994530942f;
+}
+
 // ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
@@ -950,6 +1035,13 @@ static hipError_t launch_d(const AttnArgs& a, KvSource src, KeyMode mode, bool s
 hipError_t launch_attn(const AttnArgs& a, int D, KvSource src, KeyMode mode, bool split,
                        hipStream_t stream)
 {
+    if (mode == KEYS_DECODE) {
+        // always split: the merge writes the output
+        if (src != KV_E4M3_PAGED || !split) return hipErrorInvalidValue;
+        if (D == 128) return launch_one<128, 4, KV_E4M3_PAGED, KEYS_DECODE, true>(a, stream);
+        if (D == 256) return launch_one<256, 4, KV_E4M3_PAGED, KEYS_DECODE, true>(a, stream);
+        return hipErrorInvalidValue;
+    }
     if (mode == KEYS_BLOCKS) {
         if (D != 128 || src != KV_FP16) return hipErrorInvalidValue;
         return split ? launch_one<128, 2, KV_FP16, KEYS_BLOCKS, true>(a, stream)
@@ -975,10 +1067,24 @@ template __global__ void attn_fwd_kernel<256, 4, KV_E4M3_PAGED, KEYS_CAUSAL, fal
 template __global__ void attn_fwd_kernel<256, 4, KV_E4M3_PAGED, KEYS_CAUSAL, true>(const AttnArgs);
 template __global__ void attn_fwd_kernel<128, 2, KV_FP16, KEYS_BLOCKS, false>(const AttnArgs);
 template __global__ void attn_fwd_kernel<128, 2, KV_FP16, KEYS_BLOCKS, true>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 4, KV_E4M3_PAGED, KEYS_DECODE, true>(const AttnArgs);
+template __global__ void attn_fwd_kernel<256, 4, KV_E4M3_PAGED, KEYS_DECODE, true>(const AttnArgs);
 
 hipError_t launch_merge(const MergeArgs& m, int D, hipStream_t stream)
 {
     int64_t rows = (int64_t)m.B * m.Hq * m.Lq;
+    if (m.nseg >= 16) {
+        // many segments per row: a workgroup per (row, 64 columns)
+        if (rows <= 0) return hipSuccess;
+        if (m.nseg > kWideMaxSeg || rows * (D / 64) > 0x7fffffff) return hipErrorInvalidValue;
+        if (D == 128)
+            hipLaunchKernelGGL(attn_merge_wide_kernel<128>, dim3((unsigned)(rows * 2)), dim3(256), 0, stream, m);
+        else if (D == 256)
+            hipLaunchKernelGGL(attn_merge_wide_kernel<256>, dim3((unsigned)(rows * 4)), dim3(256), 0, stream, m);
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     int grid = (int)((rows + 3) / 4);
     if (grid <= 0) return hipSuccess;
     if (D == 128)

@@ -13,7 +13,10 @@ constexpr int kTileN = 64;
 constexpr int kRowsPerWave = 32;
 
 enum KvSource { KV_FP16 = 0, KV_E4M3_PAGED = 1 };
-enum KeyMode { KEYS_DENSE = 0, KEYS_CAUSAL = 1, KEYS_BLOCKS = 2 };
+// KEYS_DECODE: causal rows of a few query positions (Lq <= 16), with the
+// rows of every query head of a kv-head group packed into one tile, so each
+// K/V byte is read once per group.
+enum KeyMode { KEYS_DENSE = 0, KEYS_CAUSAL = 1, KEYS_BLOCKS = 2, KEYS_DECODE = 3 };
 
 // Everything one attention launch needs; passed by value as the kernel
 // argument. Strides are in elements.

@@ -142,6 +142,29 @@ int attn_fwd_paged_e4m3(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_ca
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode-phase attention against a paged E4M3 cache ([P4] Purpose: the
+ * E4M3 decode kernels; Test plan and results: decode replays at 256000 input
+ * tokens): q_rows (1..16) new positions per sequence against kv_len cached
+ * tokens, causal with the rule of attn_fwd_prefix_causal (position i sees keys
+ * j <= kv_len - q_real + i). The rows of all Hq / Hkv query heads of a kv head
+ * are computed together, so each cache byte is read once per kv head; the key
+ * range is split into segments whose FP32 states are merged by a second
+ * kernel. Arguments, layouts and scales as attn_fwd_paged_e4m3.
+ * Domain: B >= 1, Hkv >= 1, Hq % Hkv == 0; D in {128, 256};
+ * 1 <= q_rows <= 16 with (Hq / Hkv) * q_rows <= 128; 1 <= q_real <= q_rows;
+ * q_real < kv_len <= 262144; kv_len % 32 == 0; page_size == 32;
+ * table_stride >= kv_len / 32; num_phys_pages >= 1; finite scales > 0.
+ * workspace: at least attn_fwd_paged_e4m3_decode_workspace(...) bytes (never
+ * 0 for a valid shape), 256-byte aligned.
+ */
+size_t attn_fwd_paged_e4m3_decode_workspace(int B, int Hq, int Hkv, int D, int q_rows, int kv_len);
+int attn_fwd_paged_e4m3_decode(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_cache,
+                               const int32_t* page_table, int64_t table_stride, int num_phys_pages,
+                               int page_size, float k_scale, float v_scale, fa_tensor o, float* lse, int B,
+                               int Hq, int Hkv, int D, int q_rows, int q_real, int kv_len, float scale,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Exact paged E4M3 -> FP16 conversion ([P4] Implementation, the "exact E4M3
  * bridge"). For every logical token t < kv_len of row b and kv head g:
  *   k_out[b,g,t,:] = RNE16(RNE32(decode(k_cache[page][t % page_size][g][:]) * k_scale))

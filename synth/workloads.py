@@ -27,6 +27,8 @@ PREFIX_CAUSAL = dict(name="causal prefill B1 Hq6 Hkv1 D256 Q8000 KV128000 (prefi
                      Hq=6, Hkv=1, D=256, q_rows=8000, q_real=8000, kv_len=128000)
 PAGED_E4M3 = dict(name="paged E4M3 causal prefill B1 Hq6 Hkv1 D256 Q8000 KV256000 page32", seed=4, B=1,
                   Hq=6, Hkv=1, D=256, q_rows=8000, q_real=8000, kv_len=256000, page_size=32)
+PAGED_DECODE = dict(name="paged E4M3 decode B1 Hq6 Hkv1 D256 Q16 KV256000 page32", seed=4, B=1, Hq=6, Hkv=1,
+                    D=256, q_rows=16, q_real=16, kv_len=256000, page_size=32)
 VSA = dict(name="VSA block-sparse attention B1 H8 D128 L36864 block64 top-k 64 dense-prefix 2", seed=5,
            B=1, H=8, D=128, L=36864, block=64, topk=64, dense_prefix=2)
 

@@ -106,6 +106,35 @@ def test_causal_domain_rejections():
     assert causal(q=q, ws=A) == fa.FA_ERR_ALIAS             # workspace over q
 
 
+def test_decode_rejections_and_workspace():
+    lib = fa.load()
+
+    def decode(**kw):
+        a = dict(q_rows=16, q_real=16, Hq=6, Hkv=1, D=256, kv_len=4096, page_size=32, ws=W, ws_bytes=1 << 30,
+                 ks=1.0, stride=4096 // 32)
+        a.update(kw)
+        return lib.attn_fwd_paged_e4m3_decode(T(A), B_, C, L, a["stride"], 200, a["page_size"], a["ks"], 1.0,
+                                              T(O), None, 1, a["Hq"], a["Hkv"], a["D"], a["q_rows"], a["q_real"],
+                                              a["kv_len"], 0.0625, a["ws"], a["ws_bytes"], None)
+    assert decode(q_rows=17, q_real=17) == fa.FA_ERR_SHAPE
+    assert decode(Hq=16) == fa.FA_ERR_SHAPE           # 16 heads x 16 rows exceed one 128-row tile
+    assert decode(q_real=0) == fa.FA_ERR_SHAPE
+    assert decode(q_real=17) == fa.FA_ERR_SHAPE
+    assert decode(kv_len=4100) == fa.FA_ERR_SHAPE
+    assert decode(page_size=16) == fa.FA_ERR_UNSUPPORTED
+    assert decode(D=64) == fa.FA_ERR_UNSUPPORTED
+    assert decode(ks=0.0) == fa.FA_ERR_SHAPE
+    assert decode(stride=10) == fa.FA_ERR_SHAPE
+    assert decode(ws=0) == fa.FA_ERR_WORKSPACE
+    need = lib.attn_fwd_paged_e4m3_decode_workspace(1, 6, 1, 256, 16, 4096)
+    assert decode(ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
+    # 64 key units of 64 allow 4 segments of 1024 keys; 96 packed rows each
+    assert need == 4 * 6 * 16 * (256 * 4 + 8)
+    # 256000 keys: one segment per CU (256), capped at 1024-key segments (250)
+    assert lib.attn_fwd_paged_e4m3_decode_workspace(1, 6, 1, 256, 16, 256000) == 250 * 96 * (256 * 4 + 8)
+    assert lib.attn_fwd_paged_e4m3_decode_workspace(1, 6, 1, 256, 17, 256000) == 0   # invalid shape
+
+
 def test_workspace_queries_are_pure_functions_of_shape():
     lib = fa.load()
     a = lib.attn_fwd_prefix_causal_workspace(1, 6, 1, 256, 8000, 128000)

@@ -71,6 +71,23 @@ def test_paged_e4m3_full(lib, unit_scales):
     assert_close(_rows_of(out.cpu().numpy(), rows), ref, f"O ({len(rows)} rows)")
 
 
+def test_paged_decode_full(lib):
+    """Every one of the 96 (head, position) rows of the decode workload, non-unit scales."""
+    w = wl.PAGED_DECODE
+    q, kc, vc, table, ks, vs = wl.paged_inputs(w, unit_scales=False)
+    say("full paged decode", w["name"], "scales", ks, vs)
+    lse = torch.empty((w["B"], w["Hq"], w["q_rows"]), dtype=torch.float32, device="cuda")
+    out = lib.attn_fwd_paged_e4m3_decode(dev(q), dev(kc), dev(vc), dev(table), w["kv_len"], w["q_real"], ks, vs,
+                                         lse=lse)
+    torch.cuda.synchronize()
+    kf = oracle.e4m3_to_f16(oracle.paged_gather(kc, table, w["kv_len"]), ks).view(np.float16)
+    vf = oracle.e4m3_to_f16(oracle.paged_gather(vc, table, w["kv_len"]), vs).view(np.float16)
+    ref, ref_lse = oracle.attention(q, kf, vf, lib.default_scale(w["D"]), mode=oracle.MODE_CAUSAL,
+                                    offset=w["kv_len"] - w["q_real"])
+    assert_close(out.cpu().numpy().reshape(-1, w["D"]), ref, "O (all rows)")
+    assert np.abs(lse.cpu().numpy().ravel() - ref_lse).max() < LSE_ABS
+
+
 def test_vsa_full(lib):
     w = wl.VSA
     say("full vsa", w["name"])

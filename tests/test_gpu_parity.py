@@ -106,6 +106,30 @@ def test_paged_e4m3_parity(lib, ks, vs):
     assert_close(out.cpu().numpy().reshape(-1, D), ref, "O")
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,q_rows,q_real,kv_len,pages,ks,vs", [
+    (6, 1, 256, 16, 16, 4096, 130, 1.0, 1.0),          # the decode shape, short cache
+    (6, 1, 256, 5, 3, 2080, 70, 0.0625, 0.03125),      # padded rows, 32-key tail
+    (4, 2, 128, 1, 1, 1024, 40, 0.0371, 0.0815),       # one position, two kv heads
+    (8, 1, 128, 16, 16, 8192, 260, 1.0, 1.0),          # 8 heads x 16 rows fill the 128-row tile
+    (4, 2, 128, 2, 2, 16416, 520, 0.0625, 1.0),        # 16 segments: the workgroup-per-row merge
+])
+def test_paged_decode_parity(lib, Hq, Hkv, D, q_rows, q_real, kv_len, pages, ks, vs):
+    say(f"paged decode Hq{Hq} Hkv{Hkv} D{D} q{q_rows} real{q_real} kv{kv_len} scales {ks} {vs}")
+    ks, vs = float(np.float32(ks)), float(np.float32(vs))
+    q = synth.normal_f16(9, synth.TID_Q, (1, Hq, q_rows, D))
+    kc, vc, table = _paged_inputs(9, Hkv, D, kv_len, pages, ks, vs)
+    scale = lib.default_scale(D)
+    lse = torch.empty((1, Hq, q_rows), dtype=torch.float32, device="cuda")
+    out = lib.attn_fwd_paged_e4m3_decode(dev(q), dev(kc), dev(vc), dev(table), kv_len, q_real, ks, vs, lse=lse,
+                                         scale=scale)
+    torch.cuda.synchronize()
+    kf = oracle.e4m3_to_f16(oracle.paged_gather(kc, table, kv_len), ks).view(np.float16)
+    vf = oracle.e4m3_to_f16(oracle.paged_gather(vc, table, kv_len), vs).view(np.float16)
+    ref, ref_lse = oracle.attention(q, kf, vf, scale, mode=oracle.MODE_CAUSAL, offset=kv_len - q_real)
+    assert_close(out.cpu().numpy().reshape(-1, D), ref, "O")
+    assert np.abs(lse.cpu().numpy().ravel() - ref_lse).max() < LSE_ABS
+
+
 def _bits_equal(got, want, codes, what):
     got = np.asarray(got).view(np.uint16).ravel()
     want = np.asarray(want).ravel()
