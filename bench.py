@@ -12,6 +12,7 @@ The same JSON line carries, under "extra", the other workloads of the hot
 path, each timed with HIP events on the launch stream:
   * causal prefill D256 Hq6/Hkv1 Q8000 KV128000 (split-KV + merge), TFLOP/s
     over the visible pairs only;
+  * the dense D128 shape of the GB10 page, H56 Lq15360 Lkv29678 with LSE;
   * the same prefill reading a paged E4M3 cache, KV256000, non-unit scales;
   * the exact paged E4M3 -> FP16 bridge, GB/s over the bytes it must move;
   * decode: 16 new positions of all 6 heads against the same 256000-token
@@ -154,6 +155,23 @@ def bench_dense(fa, torch, W, steps, warmup, timer):
     return w, (q, k, v), out, ms, wall
 
 
+def bench_ragged(fa, torch, iters, timer):
+    import synth.workloads as wl
+    w = wl.RAGGED_DENSE
+    log("generating", w["name"])
+    q, k, v = wl.dense_inputs(w)
+    dq, dk, dv = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    del q, k, v
+    out = torch.empty_like(dq)
+    lse = torch.empty((w["B"], w["H"], w["Lq"]), dtype=torch.float32, device="cuda")
+    ms, _ = timer.run(lambda: fa.attn_fwd_dense(dq, dk, dv, out=out, lse=lse), iters, 2)
+    f = dense_flops(w)
+    tf = f / (np.median(ms) * 1e-3) / 1e12
+    log(f"ragged dense: {np.median(ms):.3f} ms  {tf:.1f} TFLOP/s")
+    return {"workload": w["name"] + ", FP32 LSE", "flop": f, **stats(ms), "tflops": tf,
+            "frac_mfma_peak": tf / MFMA_F16_PEAK_TFLOPS}
+
+
 def bench_causal(fa, torch, iters, timer):
     import synth.workloads as wl
     w = wl.PREFIX_CAUSAL
@@ -290,7 +308,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--iters", type=int, default=10, help="timed launches of each extra workload")
-    ap.add_argument("--only", choices=["dense", "causal", "paged", "vsa", "copy"], default=None,
+    ap.add_argument("--only", choices=["dense", "causal", "ragged", "paged", "vsa", "copy"], default=None,
                     help="run one workload only (for profiling); 'copy' runs the plain 1 GiB "
                          "device copy that calibrates the HBM byte counters")
     ap.add_argument("--no-extra", action="store_true", help="skip the non-headline workloads")
@@ -376,6 +394,9 @@ def main():
         flush_buf = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
         if args.only in (None, "causal"):
             extra["prefix_causal"] = bench_causal(fa, torch, args.iters, timer)
+            torch.cuda.empty_cache()
+        if args.only in (None, "ragged"):
+            extra["ragged_dense"] = bench_ragged(fa, torch, args.iters, timer)
             torch.cuda.empty_cache()
         if args.only in (None, "paged"):
             extra["paged_e4m3"], extra["e4m3_bridge"], extra["paged_e4m3_decode"] = bench_paged(

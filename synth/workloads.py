@@ -23,6 +23,9 @@ TINY_DENSE = dict(name="tiny dense attention B1 H2 D128 L256 non-causal", seed=1
                   Lq=256, Lkv=256)
 VIDEO_DENSE = dict(name="video-DiT dense attention B1 H8 D128 L36864 non-causal", seed=2, B=1, H=8,
                    D=128, Lq=36864, Lkv=36864)
+# the dense shape of the GB10 page: 56 heads, a key length that is not a multiple of 32 or 64
+RAGGED_DENSE = dict(name="ragged dense D128 B1 H56 Lq15360 Lkv29678 non-causal", seed=6, B=1, H=56, D=128,
+                    Lq=15360, Lkv=29678)
 PREFIX_CAUSAL = dict(name="causal prefill B1 Hq6 Hkv1 D256 Q8000 KV128000 (prefix 120000)", seed=3, B=1,
                      Hq=6, Hkv=1, D=256, q_rows=8000, q_real=8000, kv_len=128000)
 PAGED_E4M3 = dict(name="paged E4M3 causal prefill B1 Hq6 Hkv1 D256 Q8000 KV256000 page32", seed=4, B=1,

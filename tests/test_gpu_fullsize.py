@@ -35,6 +35,21 @@ def test_video_dense_full(lib):
     assert np.abs(got_lse - ref_lse).max() < LSE_ABS
 
 
+def test_ragged_dense_full(lib):
+    """The GB10 page's dense shape: 56 heads, Lq 15360 against Lkv 29678 (a 14-key tail)."""
+    w = wl.RAGGED_DENSE
+    say("full ragged dense", w["name"])
+    q, k, v = wl.dense_inputs(w)
+    lse = torch.empty((w["B"], w["H"], w["Lq"]), dtype=torch.float32, device="cuda")
+    out = lib.attn_fwd_dense(dev(q), dev(k), dev(v), lse=lse)
+    torch.cuda.synchronize()
+    rows = sample_rows(w["B"], w["H"], w["Lq"], 8, seed=6)
+    ref, ref_lse = oracle.attention(q, k, v, lib.default_scale(w["D"]), rows=rows)
+    assert_close(_rows_of(out.cpu().numpy(), rows), ref, f"O ({len(rows)} rows)")
+    got_lse = lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert np.abs(got_lse - ref_lse).max() < LSE_ABS
+
+
 def test_prefix_causal_full(lib):
     w = wl.PREFIX_CAUSAL
     say("full causal", w["name"])
