@@ -12,7 +12,8 @@ The same JSON line carries, under "extra", the other workloads of the hot
 path, each timed with HIP events on the launch stream:
   * causal prefill D256 Hq6/Hkv1 Q8000 KV128000 (split-KV + merge), TFLOP/s
     over the visible pairs only;
-  * the dense D128 shape of the GB10 page, H56 Lq15360 Lkv29678 with LSE;
+  * the dense D128 shape of the GB10 page, H56 Lq15360 Lkv29678 with LSE,
+    on FP16 and on BF16 operands;
   * the same prefill reading a paged E4M3 cache, KV256000, non-unit scales;
   * the exact paged E4M3 -> FP16 bridge, GB/s over the bytes it must move;
   * decode: 16 new positions of all 6 heads against the same 256000-token
@@ -168,8 +169,19 @@ def bench_ragged(fa, torch, iters, timer):
     f = dense_flops(w)
     tf = f / (np.median(ms) * 1e-3) / 1e12
     log(f"ragged dense: {np.median(ms):.3f} ms  {tf:.1f} TFLOP/s")
-    return {"workload": w["name"] + ", FP32 LSE", "flop": f, **stats(ms), "tflops": tf,
-            "frac_mfma_peak": tf / MFMA_F16_PEAK_TFLOPS}
+    res = {"workload": w["name"] + ", FP32 LSE", "flop": f, **stats(ms), "tflops": tf,
+           "frac_mfma_peak": tf / MFMA_F16_PEAK_TFLOPS}
+    # the same shape on BF16 operands (BF16 MFMA; same dense peak)
+    for t in (dq, dk, dv):
+        t.copy_(t.to(torch.bfloat16).view(torch.float16))
+    dq, dk, dv = (t.view(torch.bfloat16) for t in (dq, dk, dv))
+    outb = out.view(torch.bfloat16)
+    ms, _ = timer.run(lambda: fa.attn_fwd_dense(dq, dk, dv, out=outb, lse=lse), iters, 2)
+    tf = f / (np.median(ms) * 1e-3) / 1e12
+    log(f"ragged dense bf16: {np.median(ms):.3f} ms  {tf:.1f} TFLOP/s")
+    bf = {"workload": w["name"] + ", BF16 operands, FP32 LSE", "flop": f, **stats(ms), "tflops": tf,
+          "frac_mfma_peak": tf / MFMA_F16_PEAK_TFLOPS}
+    return res, bf
 
 
 def bench_causal(fa, torch, iters, timer):
@@ -396,7 +408,7 @@ def main():
             extra["prefix_causal"] = bench_causal(fa, torch, args.iters, timer)
             torch.cuda.empty_cache()
         if args.only in (None, "ragged"):
-            extra["ragged_dense"] = bench_ragged(fa, torch, args.iters, timer)
+            extra["ragged_dense"], extra["ragged_dense_bf16"] = bench_ragged(fa, torch, args.iters, timer)
             torch.cuda.empty_cache()
         if args.only in (None, "paged"):
             extra["paged_e4m3"], extra["e4m3_bridge"], extra["paged_e4m3_decode"] = bench_paged(

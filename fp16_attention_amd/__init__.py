@@ -20,7 +20,8 @@ FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_WORKS
 FA_ERR_HIP = 1000
 
 # Every symbol include/fa16attn.h declares.
-EXPORTS = ("fa_abi_version", "fa_error_string", "attn_fwd_dense", "attn_fwd_prefix_causal_workspace",
+EXPORTS = ("fa_abi_version", "fa_error_string", "attn_fwd_dense", "attn_fwd_dense_bf16",
+           "attn_fwd_prefix_causal_workspace",
            "attn_fwd_prefix_causal", "attn_fwd_paged_e4m3_workspace", "attn_fwd_paged_e4m3",
            "attn_fwd_paged_e4m3_decode_workspace", "attn_fwd_paged_e4m3_decode",
            "kv_e4m3_paged_to_fp16", "vsa_block_select_workspace", "vsa_block_select",
@@ -44,6 +45,7 @@ _SIGS = {
     "fa_abi_version": (_i, []),
     "fa_error_string": (ctypes.c_char_p, [_i]),
     "attn_fwd_dense": (_i, [FaTensor] * 4 + [_vp] + [_i] * 5 + [_f, _vp]),
+    "attn_fwd_dense_bf16": (_i, [FaTensor] * 4 + [_vp] + [_i] * 5 + [_f, _vp]),
     "attn_fwd_prefix_causal_workspace": (_sz, [_i] * 6),
     "attn_fwd_prefix_causal": (_i, [FaTensor] * 4 + [_vp] + [_i] * 7 + [_f, _vp, _sz, _vp]),
     "attn_fwd_paged_e4m3_workspace": (_sz, [_i] * 6),
@@ -118,16 +120,22 @@ def default_scale(D: int) -> float:
 # --------------------------------------------------------------------------- attention
 
 def attn_fwd_dense(q, k, v, out=None, lse=None, scale=None):
-    """Dense non-causal attention. q [B,H,Lq,D], k/v [B,H,Lkv,D] FP16 -> out [B,H,Lq,D] FP16."""
+    """Dense non-causal attention. q [B,H,Lq,D], k/v [B,H,Lkv,D] FP16 or BF16 -> out of the same type.
+    BF16 operands go to attn_fwd_dense_bf16."""
     import torch
     _need_cuda(q, k, v, out, lse)
+    dt = q.dtype
+    if dt not in (torch.float16, torch.bfloat16) or k.dtype != dt or v.dtype != dt:
+        raise ValueError("q, k, v must all be float16 or all bfloat16")
     B, H, Lq, D = q.shape
     Lkv = k.shape[2]
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    elif out.dtype != dt:
+        raise ValueError("out must have the dtype of q")
     scale = default_scale(D) if scale is None else scale
-    _check(load().attn_fwd_dense(_view(q), _view(k), _view(v), _view(out), _ptr(lse), B, H, Lq, Lkv, D,
-                                 scale, _stream(q)))
+    fn = load().attn_fwd_dense_bf16 if dt == torch.bfloat16 else load().attn_fwd_dense
+    _check(fn(_view(q), _view(k), _view(v), _view(out), _ptr(lse), B, H, Lq, Lkv, D, scale, _stream(q)))
     return out
 
 

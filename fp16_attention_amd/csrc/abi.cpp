@@ -257,8 +257,13 @@ const char* fa_error_string(int code)
     return "fa16attn: unknown error code";
 }
 
-int attn_fwd_dense(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse, int B, int H,
-                   int Lq, int Lkv, int D, float scale, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Shared body of the dense entry points (FP16 and BF16 operands).
+int run_dense(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse, int B, int H, int Lq, int Lkv,
+              int D, float scale, void* stream, fa::KvSource src)
 {
     int rc;
     if ((rc = check_view(q)) || (rc = check_view(k)) || (rc = check_view(v)) || (rc = check_view(o)))
@@ -297,7 +302,23 @@ int attn_fwd_dense(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* ls
     a.n_qt = (Lq + kRowsPerTile - 1) / kRowsPerTile;
     a.nseg = 1;
     if ((rc = set_grid(a, (int64_t)B * H * a.n_qt, true))) return rc;
-    return hip_status(fa::launch_attn(a, D, fa::KV_FP16, fa::KEYS_DENSE, false, (hipStream_t)stream));
+    return hip_status(fa::launch_attn(a, D, src, fa::KEYS_DENSE, false, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_dense(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse, int B, int H,
+                   int Lq, int Lkv, int D, float scale, void* stream)
+{
+    return run_dense(q, k, v, o, lse, B, H, Lq, Lkv, D, scale, stream, fa::KV_FP16);
+}
+
+int attn_fwd_dense_bf16(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse, int B, int H,
+                        int Lq, int Lkv, int D, float scale, void* stream)
+{
+    return run_dense(q, k, v, o, lse, B, H, Lq, Lkv, D, scale, stream, fa::KV_BF16);
 }
 
 size_t attn_fwd_prefix_causal_workspace(int B, int Hq, int Hkv, int D, int q_rows, int kv_len)

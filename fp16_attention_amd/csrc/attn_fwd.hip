@@ -61,6 +61,31 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s4 lds_s4_t;
 
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+
+// D(32x32, FP32) += A(32x16) B(16x32) on FP16 or BF16 operands, both carried
+// as eight 16-bit values per lane.
+template <bool BF>
+__device__ __forceinline__ f16x mma(h8 a, h8 b, f16x c)
+{
+    if constexpr (BF)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8, a), __builtin_bit_cast(bf8, b), c, 0,
+                                                       0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// FP32 -> the 16-bit output format, rounding to nearest even.
+template <bool BF>
+__device__ __forceinline__ _Float16 to_out(float x)
+{
+    if constexpr (BF)
+        return __builtin_bit_cast(_Float16, (__bf16)x);
+    else
+        return (_Float16)x;
+}
+
 // Word 3 of a raw buffer resource (32-bit data, no swizzle) on the gfx9 family.
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 // The running maximum (log2 units) is raised only when exceeded by this much.
@@ -248,7 +273,7 @@ struct ByteDecoder {
 template <int D, int SRC, int MODE>
 struct Tiling {
     static constexpr int KT = 32;
-    static constexpr int R = (SRC == KV_FP16 && MODE != KEYS_BLOCKS) ? 4 : 2;
+    static constexpr int R = (SRC != KV_E4M3_PAGED && MODE != KEYS_BLOCKS) ? 4 : 2;
     static constexpr int RB = SRC == KV_E4M3_PAGED ? 4 : 1;  // E4M3 byte slots per K and V ring
     static constexpr int PH = SRC == KV_E4M3_PAGED ? RB : R;  // phases of the unrolled loop
 };
@@ -267,10 +292,12 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     constexpr int ROW = 2 * D;    // bytes per LDS row
     constexpr int R = Tiling<D, SRC, MODE>::R;
     constexpr int RB = Tiling<D, SRC, MODE>::RB;
+    constexpr bool DIRECT = SRC != KV_E4M3_PAGED;  // 16-bit K/V loaded straight into LDS
+    constexpr bool BF = SRC == KV_BF16;
     constexpr int PH = Tiling<D, SRC, MODE>::PH;
     constexpr int BB = SRC == KV_E4M3_PAGED ? KT * D : 16;  // bytes per byte slot
-    static_assert(R >= 2 && R <= 4 && (SRC == KV_FP16 || (R == 2 && RB == 4)), "ring depth");
-    static_assert(SRC == KV_FP16 || KT == 32, "an E4M3 tile is one 32-token page");
+    static_assert(R >= 2 && R <= 4 && (DIRECT || (R == 2 && RB == 4)), "ring depth");
+    static_assert(DIRECT || KT == 32, "an E4M3 tile is one 32-token page");
     __shared__ __attribute__((aligned(1024))) unsigned char kslot0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char kslot1[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char kslot2[R > 2 ? TB : 16];
@@ -289,8 +316,8 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     __shared__ __attribute__((aligned(1024))) unsigned char vbyte3[BB];
     // s_waitcnt that leaves the (ring depth - 2) most recent load groups in flight
     constexpr int kGroupLoads =
-        2 * (SRC == KV_FP16 ? DirectLoader<D, WAVES, KT>::kLoads : ByteLoader<D, WAVES, KT>::kLoads);
-    constexpr int kVmLeft = ((SRC == KV_FP16 ? R : RB) - 2) * kGroupLoads;
+        2 * (DIRECT ? DirectLoader<D, WAVES, KT>::kLoads : ByteLoader<D, WAVES, KT>::kLoads);
+    constexpr int kVmLeft = ((DIRECT ? R : RB) - 2) * kGroupLoads;
     static_assert(kVmLeft < 64, "vmcnt range");
     constexpr int kWaitGroups = (kVmLeft & 15) | ((kVmLeft >> 4) << 14) | 0x0070;  // and lgkmcnt(0)
 
@@ -394,7 +421,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     const int32_t* table = nullptr;
     DirectLoader<D, WAVES, KT> dl;
     ByteLoader<D, WAVES, KT> bl;
-    if (SRC == KV_FP16) {
+    if (DIRECT) {
         kbase = a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh;
         vbase = a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh;
         dl.init(a.k_ss, a.v_ss, wave, lane);
@@ -493,7 +520,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 #pragma unroll
             for (int kb = 0; kb < NSB; ++kb) {
                 h8 k = *(const h8*)(kt + koff_s[kk] + kb * 32 * ROW);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k, qf[kk], s[kb], 0, 0, 0);
+                s[kb] = mma<BF>(k, qf[kk], s[kb]);
             }
     };
 
@@ -508,7 +535,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 #pragma unroll
         for (int i = 0; i < KS * DB; ++i) {
             const int kstep = i / DB, db = i % DB;
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vread(vt, i), pk[kstep], oacc[db], 0, 0, 0);
+            oacc[db] = mma<BF>(vread(vt, i), pk[kstep], oacc[db]);
         }
     };
 
@@ -569,11 +596,20 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     // One exponential unit: scores r, r+1 of score block kb -> P (FP16) in the
     // PV operand order (register r of block kb is k-step 2kb + r/8, slot r%8).
     const h2 ones = {(_Float16)1.f, (_Float16)1.f};
+    const bf2 ones_bf = {(__bf16)1.f, (__bf16)1.f};
     auto exp_unit = [&](const f16x (&s)[NSB], int u, float m_use, h8* pk) {
         const int kb = u % NSB, r = 2 * (u / NSB);
-        h2 p = {(_Float16)__builtin_amdgcn_exp2f(fmaf(s[kb][r], a.c, -m_use)),
-                (_Float16)__builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], a.c, -m_use))};
-        l_run = __builtin_amdgcn_fdot2(p, ones, l_run, false);
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], a.c, -m_use));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], a.c, -m_use));
+        h2 p;
+        if constexpr (BF) {
+            const bf2 pb = {(__bf16)e0, (__bf16)e1};
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(pb, ones_bf, l_run, false);
+            p = __builtin_bit_cast(h2, pb);
+        } else {
+            p = h2{(_Float16)e0, (_Float16)e1};
+            l_run = __builtin_amdgcn_fdot2(p, ones, l_run, false);
+        }
         pk[2 * kb + (r >> 3)][r & 7] = p.x;
         pk[2 * kb + (r >> 3)][(r & 7) + 1] = p.y;
     };
@@ -638,7 +674,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     using P3 = std::integral_constant<int, 3>;
     using P4 = std::integral_constant<int, 4>;
 
-    if constexpr (SRC == KV_FP16) {
+    if constexpr (DIRECT) {
         issue_k(0, kslot0);
         issue_v(0, vslot0);
         issue_k(1, kslot1);
@@ -649,7 +685,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         issue_group_b(P0{}, 0);
         issue_group_b(P1{}, 1);
         issue_group_b(P2{}, 2);
-        static_assert(RB == 4 || SRC == KV_FP16, "prologue written for four byte slots");
+        static_assert(RB == 4, "prologue written for four byte slots");
         ring_barrier<(2 * kGroupLoads & 15) | (((2 * kGroupLoads) >> 4) << 14) | 0x0070>();
         Dec::run(kbyte0, kslot0, tid);
         Dec::run(kbyte1, kslot1, tid);
@@ -660,7 +696,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     compute_s(kslot0, scur);
     raise_max(row_max(scur, tile_key0(0), true));
     __syncthreads();
-    if constexpr (SRC == KV_FP16) {
+    if constexpr (DIRECT) {
         // groups 1 .. R-1
         issue_k(2, kslot(P2{}));
         issue_v(1, vslot(P1{}));
@@ -684,7 +720,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     // the slots read in this iteration with group it+R
     auto refill = [&](auto p, int it) {
         using PN = std::integral_constant<int, decltype(p)::value + 1>;
-        if constexpr (SRC == KV_FP16) {
+        if constexpr (DIRECT) {
             ring_barrier<kWaitGroups>();
             issue_k(it + R + 1, kslot(PN{}));
             issue_v(it + R, vslot(p));
@@ -733,7 +769,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         for (int i = 0; i < NB; ++i) {
             if (i + PB < NB) kop[i + PB] = kread(i + PB);
             const int kb = i % NSB, kk = i / NSB;
-            sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[i], qf[kk], kk == 0 ? f16x{} : sn[kb], 0, 0, 0);
+            sn[kb] = mma<BF>(kop[i], qf[kk], kk == 0 ? f16x{} : sn[kb]);
             // exponential units spread evenly over the steps
 #pragma unroll
             for (int u = (i * NU) / NB; u < ((i + 1) * NU) / NB; ++u) exp_unit(scur, u, m_use, pk);
@@ -779,7 +815,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         for (int i = 0; i < NC; ++i) {
             if (i + PC < NC) vop[i + PC] = vread(vt, i + PC);
             const int kstep = i / DB, db = i % DB;
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[i], pk[kstep], oacc[db], 0, 0, 0);
+            oacc[db] = mma<BF>(vop[i], pk[kstep], oacc[db]);
             // row-maximum units
             if (i >= MX0 && i < MX0 + MXS) {
 #pragma unroll
@@ -883,7 +919,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
                 int d = db * 32 + 8 * g4 + 4 * hlf;
                 h4 v4;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v4[e] = (_Float16)(oacc[db][4 * g4 + e] * inv);
+                for (int e = 0; e < 4; ++e) v4[e] = to_out<BF>(oacc[db][4 * g4 + e] * inv);
                 *(h4*)(op + d) = v4;
             }
         if (a.lse && hlf == 0)
@@ -1023,7 +1059,10 @@ template <int D>
 static hipError_t launch_d(const AttnArgs& a, KvSource src, KeyMode mode, bool split,
                            hipStream_t stream)
 {
-    if (mode == KEYS_DENSE) return launch_one<D, 4, KV_FP16, KEYS_DENSE, false>(a, stream);
+    if (mode == KEYS_DENSE)
+        return src == KV_BF16 ? launch_one<D, 4, KV_BF16, KEYS_DENSE, false>(a, stream)
+                              : launch_one<D, 4, KV_FP16, KEYS_DENSE, false>(a, stream);
+    if (src == KV_BF16) return hipErrorInvalidValue;
     if (mode == KEYS_BLOCKS) return hipErrorInvalidValue;
     if (src == KV_FP16)
         return split ? launch_one<D, 4, KV_FP16, KEYS_CAUSAL, true>(a, stream)
@@ -1057,6 +1096,8 @@ hipError_t launch_attn(const AttnArgs& a, int D, KvSource src, KeyMode mode, boo
 // shared library then fails to load), with no diagnostic.
 template __global__ void attn_fwd_kernel<128, 4, KV_FP16, KEYS_DENSE, false>(const AttnArgs);
 template __global__ void attn_fwd_kernel<256, 4, KV_FP16, KEYS_DENSE, false>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 4, KV_BF16, KEYS_DENSE, false>(const AttnArgs);
+template __global__ void attn_fwd_kernel<256, 4, KV_BF16, KEYS_DENSE, false>(const AttnArgs);
 template __global__ void attn_fwd_kernel<128, 4, KV_FP16, KEYS_CAUSAL, false>(const AttnArgs);
 template __global__ void attn_fwd_kernel<128, 4, KV_FP16, KEYS_CAUSAL, true>(const AttnArgs);
 template __global__ void attn_fwd_kernel<256, 4, KV_FP16, KEYS_CAUSAL, false>(const AttnArgs);

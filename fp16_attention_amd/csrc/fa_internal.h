@@ -12,7 +12,9 @@ constexpr int kTileN = 64;
 // Query rows per wave (one 32-wide MFMA column block).
 constexpr int kRowsPerWave = 32;
 
-enum KvSource { KV_FP16 = 0, KV_E4M3_PAGED = 1 };
+// KV_BF16: Q, K, V and O are BF16 (dense attention only); it streams like
+// KV_FP16 and differs in the MFMA type and the rounding of P and O.
+enum KvSource { KV_FP16 = 0, KV_E4M3_PAGED = 1, KV_BF16 = 2 };
 // KEYS_DECODE: causal rows of a few query positions (Lq <= 16), with the
 // rows of every query head of a kv-head group packed into one tile, so each
 // K/V byte is read once per group.

@@ -99,6 +99,15 @@ int attn_fwd_dense(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* ls
                    int Lq, int Lkv, int D, float scale, void* stream);
 
 /*
+ * attn_fwd_dense on BF16 operands ([P5] the BF16 dense attention of the GB10
+ * shape, minimax_h3_prefix.cu): q, k, v and o hold BF16 values; QK^T and PV
+ * accumulate in FP32, P is rounded to BF16 before the PV product and O to BF16
+ * (nearest even). Arguments, domain and errors as attn_fwd_dense.
+ */
+int attn_fwd_dense_bf16(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse, int B, int H,
+                        int Lq, int Lkv, int D, float scale, void* stream);
+
+/*
  * Causal prefill against a prefix KV with grouped-query heads ([P4]
  * Implementation). Query row i (0 <= i < q_rows) of query head h sees keys
  * j <= (kv_len - q_real) + i of kv head h / (Hq / Hkv). Rows i >= q_real are

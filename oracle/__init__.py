@@ -38,6 +38,8 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         lib.or_f16_to_f64.restype = ctypes.c_double
         lib.or_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.or_bf16_to_f64.restype = ctypes.c_double
+        lib.or_bf16_to_f64.argtypes = [ctypes.c_uint16]
         lib.or_f64_to_f16.restype = ctypes.c_uint16
         lib.or_f64_to_f16.argtypes = [ctypes.c_double]
         lib.or_e4m3_decode.restype = ctypes.c_double
@@ -56,7 +58,7 @@ def _load():
                                      _i64p] + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int,
                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                     ctypes.c_void_p, ctypes.c_int]
+                                     ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
         lib.or_merge.restype = None
         lib.or_merge.argtypes = [ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 5
         lib.or_vsa_pool.restype = None
@@ -91,6 +93,12 @@ def f16_to_f64(bits) -> np.ndarray:
     lib = _load()
     b = np.asarray(bits, dtype=np.uint16).ravel()
     return np.array([lib.or_f16_to_f64(int(x)) for x in b], dtype=np.float64)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    lib = _load()
+    b = np.asarray(bits, dtype=np.uint16).ravel()
+    return np.array([lib.or_bf16_to_f64(int(x)) for x in b], dtype=np.float64)
 
 
 def f64_to_f16(values) -> np.ndarray:
@@ -141,9 +149,10 @@ def all_rows(B: int, H: int, L: int) -> np.ndarray:
 
 
 def attention(q, k, v, scale: float, mode: int = MODE_DENSE, offset: int = 0, idx=None,
-              block: int = 64, dense_prefix: int = 0, rows=None, threads: int = 0):
+              block: int = 64, dense_prefix: int = 0, rows=None, threads: int = 0, bf16: bool = False):
     """FP64 attention of FP16 q [B,Hq,Lq,D], k/v [B,Hkv,Lkv,D] (any D-contiguous strides).
 
+    bf16: the arrays are uint16 bit patterns of bfloat16 values instead.
     rows: int32 [n,3] (b, h, i) triples to compute (default: all rows).
     Returns (out float64 [n, D], lse float64 [n]) in the order of rows.
     """
@@ -151,9 +160,10 @@ def attention(q, k, v, scale: float, mode: int = MODE_DENSE, offset: int = 0, id
     q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
+    want = np.uint16 if bf16 else np.float16
     for name, a in (("q", q), ("k", k), ("v", v)):
-        if a.dtype != np.float16 or a.ndim != 4:
-            raise TypeError(f"{name} must be a 4-D float16 array")
+        if a.dtype != want or a.ndim != 4:
+            raise TypeError(f"{name} must be a 4-D {np.dtype(want).name} array")
     B, Hq, Lq, D = q.shape
     _, Hkv, Lkv, _ = k.shape
     if rows is None:
@@ -171,7 +181,7 @@ def attention(q, k, v, scale: float, mode: int = MODE_DENSE, offset: int = 0, id
     rc = lib.or_attention(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), B, Hq, Hkv,
                           Lq, Lkv, D, float(scale), mode, int(offset),
                           _ptr(idx_arr) if idx_arr is not None else None, block, topk, dense_prefix,
-                          _ptr(rows), n, _ptr(out), _ptr(lse), _threads(threads))
+                          _ptr(rows), n, _ptr(out), _ptr(lse), _threads(threads), int(bool(bf16)))
     if rc:
         raise ValueError("invalid oracle arguments")
     return out, lse

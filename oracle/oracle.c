@@ -44,6 +44,24 @@ double or_f16_to_f64(uint16_t h)
     return s ? -mag : mag;
 }
 
+/* bfloat16, from its definition: the upper 16 bits of an IEEE binary32 (1    */
+/* sign bit, 8 exponent bits with bias 127, 7 fraction bits). [P5] uses it    */
+/* for the BF16 dense attention of the GB10 shape.                            */
+double or_bf16_to_f64(uint16_t h)
+{
+    int s = (h >> 15) & 1;
+    int e = (h >> 7) & 255;
+    int f = h & 127;
+    double mag;
+    if (e == 255)
+        mag = f ? NAN : INFINITY;
+    else if (e == 0)
+        mag = ldexp((double)f, -133);
+    else
+        mag = ldexp(128.0 + f, e - 134);
+    return s ? -mag : mag;
+}
+
 /* Round a double to the nearest FP16 value, ties to even; overflow to inf. */
 uint16_t or_f64_to_f16(double x)
 {
@@ -181,6 +199,7 @@ typedef struct {
     int64_t n_rows;
     double* out; /* [n_rows, D] */
     double* lse; /* [n_rows] */
+    double (*elem)(uint16_t); /* q, k, v element format: FP16 or BF16 */
     int64_t next;
     pthread_mutex_t lock;
 } attn_job;
@@ -236,14 +255,14 @@ static void* attn_worker(void* arg)
         int g = h / group;
         const uint16_t* qrow = J->q + b * J->qs[0] + h * J->qs[1] + (int64_t)i * J->qs[2];
         for (int d = 0; d < D; ++d)
-            qd[d] = or_f16_to_f64(qrow[d]);
+            qd[d] = J->elem(qrow[d]);
         int64_t n = keys_of_row(J, b, h, i, keys);
         double m = -INFINITY;
         for (int64_t t = 0; t < n; ++t) {
             const uint16_t* krow = J->k + b * J->ks[0] + g * J->ks[1] + keys[t] * J->ks[2];
             double dot = 0.0;
             for (int d = 0; d < D; ++d)
-                dot += qd[d] * or_f16_to_f64(krow[d]);
+                dot += qd[d] * J->elem(krow[d]);
             s[t] = J->scale * dot;
             if (s[t] > m)
                 m = s[t];
@@ -256,7 +275,7 @@ static void* attn_worker(void* arg)
             denom += p;
             const uint16_t* vrow = J->v + b * J->vs[0] + g * J->vs[1] + keys[t] * J->vs[2];
             for (int d = 0; d < D; ++d)
-                acc[d] += p * or_f16_to_f64(vrow[d]);
+                acc[d] += p * J->elem(vrow[d]);
         }
         for (int d = 0; d < D; ++d)
             J->out[r * D + d] = acc[d] / denom;
@@ -269,12 +288,13 @@ static void* attn_worker(void* arg)
     return NULL;
 }
 
-/* Returns 0, or -1 for an invalid argument. */
+/* Returns 0, or -1 for an invalid argument. bf16: q, k, v hold bfloat16
+   values instead of FP16. */
 int or_attention(const uint16_t* q, const int64_t* qs, const uint16_t* k, const int64_t* ks,
                  const uint16_t* v, const int64_t* vs, int B, int Hq, int Hkv, int Lq, int Lkv,
                  int D, double scale, int mode, int64_t offset, const int32_t* idx, int block,
                  int topk, int dense_prefix, const int32_t* rows, int64_t n_rows, double* out,
-                 double* lse, int threads)
+                 double* lse, int threads, int bf16)
 {
     if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || (mode == 2 && (block <= 0 || !idx)))
         return -1;
@@ -303,6 +323,7 @@ int or_attention(const uint16_t* q, const int64_t* qs, const uint16_t* k, const 
     J.n_rows = n_rows;
     J.out = out;
     J.lse = lse;
+    J.elem = bf16 ? or_bf16_to_f64 : or_f16_to_f64;
     J.next = 0;
     pthread_mutex_init(&J.lock, NULL);
     if (threads < 1)

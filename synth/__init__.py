@@ -105,6 +105,25 @@ def normal_f16(seed: int, tensor_id: int, shape) -> np.ndarray:
     return out.reshape(shape)
 
 
+def normal_bf16(seed: int, tensor_id: int, shape) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of the same N(0,1) draws: float64 -> float32
+    (numpy, nearest even) -> the upper 16 bits, nearest even."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    shape = tuple(int(s) for s in shape)
+    n = int(np.prod(shape)) if shape else 1
+    out = np.empty(n, dtype=np.uint16)
+
+    def fill(span):
+        lo, hi = span
+        u = normal_f64_block(seed, tensor_id, lo, hi).astype(np.float32).view(np.uint32)
+        out[lo:hi] = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+    with ThreadPoolExecutor(_threads()) as pool:
+        list(pool.map(fill, _blocks(n)))
+    return out.reshape(shape)
+
+
 def normal_f64_block(seed: int, tensor_id: int, lo: int, hi: int) -> np.ndarray:
     """Elements lo..hi-1 of the normal stream; lo must be even."""
     assert lo % 2 == 0

@@ -12,6 +12,10 @@ MAX_ABS = 2e-3
 REL_L2 = 1e-3
 # LSE is FP32: compare it with an absolute bound
 LSE_ABS = 1e-3
+# BF16 outputs (and BF16 P): the same bounds in units of the format's unit
+# roundoff, which is 2^-8 for BF16 against 2^-11 for FP16, i.e. 8x
+BF16_MAX_ABS = 8 * MAX_ABS
+BF16_REL_L2 = 8 * REL_L2
 
 
 def say(*msg):
@@ -30,6 +34,14 @@ def assert_close(out, ref, what="", max_abs=MAX_ABS, rel_l2=REL_L2):
     say(f"  {what}: max_abs={ma:.3e} rel_l2={rl:.3e}")
     assert ma <= max_abs, f"{what}: max-abs {ma} > {max_abs}"
     assert rl <= rel_l2, f"{what}: rel-L2 {rl} > {rel_l2}"
+
+
+def qkv_bf16(seed, B, H, Lq, Lkv, D):
+    """bfloat16 bit patterns (uint16) of the seeded N(0,1) draws."""
+    q = synth.normal_bf16(seed, synth.TID_Q, (B, H, Lq, D))
+    k = synth.normal_bf16(seed, synth.TID_K, (B, H, Lkv, D))
+    v = synth.normal_bf16(seed, synth.TID_V, (B, H, Lkv, D))
+    return q, k, v
 
 
 def qkv(seed, B, Hq, Hkv, Lq, Lkv, D):

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import synth.workloads as wl
-from parity_util import LSE_ABS, assert_close, sample_rows, say
+from parity_util import BF16_MAX_ABS, BF16_REL_L2, LSE_ABS, assert_close, sample_rows, say
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -46,6 +46,27 @@ def test_ragged_dense_full(lib):
     rows = sample_rows(w["B"], w["H"], w["Lq"], 8, seed=6)
     ref, ref_lse = oracle.attention(q, k, v, lib.default_scale(w["D"]), rows=rows)
     assert_close(_rows_of(out.cpu().numpy(), rows), ref, f"O ({len(rows)} rows)")
+    got_lse = lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert np.abs(got_lse - ref_lse).max() < LSE_ABS
+
+
+def test_ragged_dense_bf16_full(lib):
+    """The GB10 page's BF16 variant of the same ragged dense shape."""
+    import synth
+    w = wl.RAGGED_DENSE
+    say("full ragged dense bf16", w["name"])
+    shape_q, shape_kv = (w["B"], w["H"], w["Lq"], w["D"]), (w["B"], w["H"], w["Lkv"], w["D"])
+    q = synth.normal_bf16(w["seed"], synth.TID_Q, shape_q)
+    k = synth.normal_bf16(w["seed"], synth.TID_K, shape_kv)
+    v = synth.normal_bf16(w["seed"], synth.TID_V, shape_kv)
+    dq, dk, dv = (dev(x.view(np.int16)).view(torch.bfloat16) for x in (q, k, v))
+    lse = torch.empty((w["B"], w["H"], w["Lq"]), dtype=torch.float32, device="cuda")
+    out = lib.attn_fwd_dense(dq, dk, dv, lse=lse)
+    torch.cuda.synchronize()
+    rows = sample_rows(w["B"], w["H"], w["Lq"], 8, seed=7)
+    ref, ref_lse = oracle.attention(q, k, v, lib.default_scale(w["D"]), rows=rows, bf16=True)
+    got = out.double().cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert_close(got, ref, f"O bf16 ({len(rows)} rows)", BF16_MAX_ABS, BF16_REL_L2)
     got_lse = lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
     assert np.abs(got_lse - ref_lse).max() < LSE_ABS
 

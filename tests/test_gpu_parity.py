@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import synth
-from parity_util import LSE_ABS, assert_close, qkv, say
+from parity_util import BF16_MAX_ABS, BF16_REL_L2, LSE_ABS, assert_close, qkv, qkv_bf16, say
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -28,6 +28,21 @@ def test_dense_parity(lib, B, H, Lq, Lkv, D):
     torch.cuda.synchronize()
     ref, ref_lse = oracle.attention(q, k, v, scale)
     assert_close(out.cpu().numpy().reshape(-1, D), ref, "O")
+    assert np.abs(lse.cpu().numpy().ravel() - ref_lse).max() < LSE_ABS
+
+
+@pytest.mark.parametrize("B,H,Lq,Lkv,D", [(1, 2, 256, 256, 128), (2, 3, 300, 1000, 128), (1, 2, 129, 65, 256)])
+def test_dense_bf16_parity(lib, B, H, Lq, Lkv, D):
+    say(f"dense bf16 B{B} H{H} Lq{Lq} Lkv{Lkv} D{D}")
+    q, k, v = qkv_bf16(12, B, H, Lq, Lkv, D)
+    dq, dk, dv = (dev(x.view(np.int16)).view(torch.bfloat16) for x in (q, k, v))
+    scale = lib.default_scale(D)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device="cuda")
+    out = lib.attn_fwd_dense(dq, dk, dv, lse=lse, scale=scale)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.bfloat16
+    ref, ref_lse = oracle.attention(q, k, v, scale, bf16=True)
+    assert_close(out.double().cpu().numpy().reshape(-1, D), ref, "O bf16", BF16_MAX_ABS, BF16_REL_L2)
     assert np.abs(lse.cpu().numpy().ravel() - ref_lse).max() < LSE_ABS
 
 

@@ -45,6 +45,21 @@ def test_dense_matches_torch_sdpa(B, Hq, Hkv, Lq, Lkv, D):
     assert np.abs(lse - torch.logsumexp(s, -1).numpy().ravel()).max() < 1e-12
 
 
+def test_bf16_operands_match_torch_sdpa():
+    """bfloat16 operands (as bit patterns) against torch float64 SDPA of the same values."""
+    rng = np.random.default_rng(11)
+    B, H, Lq, Lkv, D = 1, 3, 29, 47, 16
+    tq, tk, tv = (torch.from_numpy(rng.standard_normal(s)).to(torch.bfloat16) for s in
+                  ((B, H, Lq, D), (B, H, Lkv, D), (B, H, Lkv, D)))
+    bits = [t.view(torch.int16).numpy().view(np.uint16) for t in (tq, tk, tv)]
+    scale = float(np.float32(1 / np.sqrt(D)))
+    out, lse = oracle.attention(*bits, scale, bf16=True)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq.double(), tk.double(), tv.double(), scale=scale)
+    assert np.abs(out - ref.numpy().reshape(-1, D)).max() < 1e-12
+    s = tq.double() @ tk.double().transpose(-1, -2) * scale
+    assert np.abs(lse - torch.logsumexp(s, -1).numpy().ravel()).max() < 1e-12
+
+
 @pytest.mark.parametrize("q_rows,q_real,kv_len", [(64, 64, 96), (64, 40, 100), (128, 100, 101)])
 def test_causal_offset_matches_torch_masked_sdpa(q_rows, q_real, kv_len):
     rng = np.random.default_rng(q_real)

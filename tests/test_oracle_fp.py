@@ -25,6 +25,17 @@ def test_f16_decode_exhaustive_matches_numpy():
     assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
 
 
+def test_bf16_decode_exhaustive_matches_torch():
+    """All 65536 bfloat16 codes against torch's own bfloat16 -> float64 conversion."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.bf16_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
 def test_f64_to_f16_rounding_matches_numpy():
     rng = np.random.default_rng(7)
     h = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16)  # all finite positive halves
