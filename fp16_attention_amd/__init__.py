@@ -236,7 +236,7 @@ def vsa_block_select(q, k, topk, block=64, scores=False, workspace=None, out=Non
     if not (q.is_contiguous() and k.is_contiguous()):
         raise ValueError("q and k must be contiguous")
     B, H, L, D = q.shape
-    NB = L // block
+    NB = (L + block - 1) // block  # the last block may be partial
     idx = out
     if idx is None:
         idx = torch.empty((B, H, NB, topk), dtype=torch.int32, device=q.device)

@@ -160,8 +160,8 @@ SplitPlan plan_vsa(int B, int H, int D, int NB, int topk, int dense_prefix)
 int check_vsa_domain(int B, int H, int L, int D, int block, int topk, int dense_prefix)
 {
     if (D != 128 || block != 64) return FA_ERR_UNSUPPORTED;
-    if (B < 1 || H < 1 || L < block || L % block) return FA_ERR_SHAPE;
-    const int NB = L / block;
+    if (B < 1 || H < 1 || L < 1) return FA_ERR_SHAPE;
+    const int NB = (L + block - 1) / block;  // the last block may be partial
     if (topk < 1 || topk > NB || dense_prefix < 0 || dense_prefix > NB) return FA_ERR_SHAPE;
     return FA_OK;
 }
@@ -502,13 +502,13 @@ int kv_e4m3_paged_to_fp16(const uint8_t* k_cache, const uint8_t* v_cache, const 
 // (256-byte aligned) the FP64 block scores [B*H*NB][NB].
 static size_t vsa_pooled_bytes(int B, int H, int L, int D)
 {
-    return (((size_t)2 * B * H * (L / 64) * D * 4) + 255) & ~(size_t)255;
+    return (((size_t)2 * B * H * ((L + 63) / 64) * D * 4) + 255) & ~(size_t)255;
 }
 
 size_t vsa_block_select_workspace(int B, int H, int L, int D, int block)
 {
-    if (B < 1 || H < 1 || D != 128 || block != 64 || L < 64 || L % 64 || L / 64 > 1024) return 0;
-    const size_t nb = (size_t)(L / 64);
+    if (B < 1 || H < 1 || D != 128 || block != 64 || L < 1 || (L + 63) / 64 > 1024) return 0;
+    const size_t nb = (size_t)((L + 63) / 64);
     return vsa_pooled_bytes(B, H, L, D) + (size_t)B * H * nb * nb * 8;
 }
 
@@ -518,8 +518,8 @@ int vsa_block_select(const uint16_t* q, const uint16_t* k, int B, int H, int L, 
 {
     if (!q || !k || !idx_out) return FA_ERR_NULL;
     if (D != 128 || block != 64) return FA_ERR_UNSUPPORTED;
-    if (B < 1 || H < 1 || L < block || L % block) return FA_ERR_SHAPE;
-    const int NB = L / block;
+    if (B < 1 || H < 1 || L < 1) return FA_ERR_SHAPE;
+    const int NB = (L + block - 1) / block;  // the last block may be partial
     if (NB > 1024 || topk < 1 || topk > NB) return FA_ERR_SHAPE;
     if (((uintptr_t)q & 15u) || ((uintptr_t)k & 15u) || ((uintptr_t)idx_out & 3u) ||
         ((uintptr_t)score_out & 7u))
@@ -547,7 +547,7 @@ size_t vsa_block_sparse_attn_workspace(int B, int H, int L, int D, int block, in
                                        int dense_prefix_qblocks)
 {
     if (check_vsa_domain(B, H, L, D, block, topk, dense_prefix_qblocks)) return 0;
-    return plan_vsa(B, H, D, L / block, topk, dense_prefix_qblocks).workspace;
+    return plan_vsa(B, H, D, (L + block - 1) / block, topk, dense_prefix_qblocks).workspace;
 }
 
 int vsa_block_sparse_attn(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, const int32_t* idx,
@@ -560,7 +560,7 @@ int vsa_block_sparse_attn(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, co
         return rc;
     if (!idx) return FA_ERR_NULL;
     if ((rc = check_vsa_domain(B, H, L, D, block, topk, dense_prefix_qblocks))) return rc;
-    const int NB = L / block;
+    const int NB = (L + block - 1) / block;
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SHAPE;
     if ((uintptr_t)idx & 3u) return FA_ERR_ALIGN;
     Span in[4] = {span_of(q.data, q.stride_b, q.stride_h, q.stride_s, B, H, L, D, 2),
@@ -608,7 +608,7 @@ int vsa_block_sparse_attn(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, co
     a.oscale = 1.f;
     a.n_qt = NB;
     a.nseg = p.nseg;
-    a.part_lq = dense_prefix_qblocks * block;
+    a.part_lq = std::min(dense_prefix_qblocks * block, L);  // rows past L do not exist
     const bool split = p.nseg > 1;
     if (split) {
         size_t rows = (size_t)p.nseg * B * H * a.part_lq;

@@ -390,11 +390,11 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         n_tiles = (key_stop - key_begin + KT - 1) / KT;
     } else if (MODE == KEYS_BLOCKS) {
         if (qt < a.dense_prefix) {
-            const int len = seg_units(a.Lkv / kTileN, a.nseg) * kTileN;
+            const int len = seg_units((a.Lkv + kTileN - 1) / kTileN, a.nseg) * kTileN;
             key_begin = seg * len;
             key_stop = min(a.Lkv, (seg + 1) * len);
             if (key_begin >= key_stop) return;
-            n_tiles = (key_stop - key_begin) / KT;
+            n_tiles = (key_stop - key_begin + KT - 1) / KT;
         } else {
             n_tiles = a.topk * (kTileN / KT);
             blist = a.idx + (((int64_t)b * a.Hq + h) * a.nqb + qt) * a.topk;
@@ -403,12 +403,12 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         n_tiles = (a.Lkv + KT - 1) / KT;
     }
     const int key_last = key_end - 1;
-    const int nblk = a.Lkv / kTileN;
+    const int nblk = (a.Lkv + kTileN - 1) / kTileN;  // the last block may be partial
 
     auto tile_key0 = [&](int it) -> int {
         if (MODE == KEYS_BLOCKS && blist) {
             constexpr int kPer = kTileN / KT;  // tiles per selected block
-            int blk = blist[it / kPer];
+            int blk = scalar_load(blist, it / kPer);  // wave-uniform: keeps the load addresses scalar
             blk = min(max(blk, 0), nblk - 1);
             return blk * kTileN + (it % kPer) * KT;
         }
@@ -432,17 +432,22 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     // Every load group issues the same number of loads, so that s_waitcnt
     // counts stay exact: a tile past the end is loaded with zero valid rows
     // (the buffer range check returns zeros) into its free slot.
+    // rows of the tile at key0 that exist (a block list's partial last block
+    // can leave none); wave-uniform, so the buffer descriptor stays scalar
+    auto valid_rows = [&](bool ok, int key0) {
+        return __builtin_amdgcn_readfirstlane(ok ? max(0, min(KT, key_end - key0)) : 0);
+    };
     auto issue_k = [&](int it, unsigned char* slot) {
         const bool ok = it < n_tiles;
         const int key0 = tile_key0(ok ? it : n_tiles - 1);
         DirectLoader<D, WAVES, KT>::issue(kbase + (int64_t)key0 * a.k_ss, a.k_ss, dl.koff,
-                                          ok ? min(KT, key_end - key0) : 0, slot, wave);
+                                          valid_rows(ok, key0), slot, wave);
     };
     auto issue_v = [&](int it, unsigned char* slot) {
         const bool ok = it < n_tiles;
         const int key0 = tile_key0(ok ? it : n_tiles - 1);
         DirectLoader<D, WAVES, KT>::issue(vbase + (int64_t)key0 * a.v_ss, a.v_ss, dl.voff,
-                                          ok ? min(KT, key_end - key0) : 0, slot, wave);
+                                          valid_rows(ok, key0), slot, wave);
     };
     // E4M3: tile it is page table[tile_key0(it) / 32] (tiles are page aligned)
     auto issue_b = [&](const uint8_t* cache, int it, unsigned char* slot) {
@@ -543,8 +548,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     // kb*32 + 8(r/4) + 4hlf + r%4), then return the row maximum times c.
     auto tile_needs_mask = [&](int key0) -> bool {
         if (CAUSAL) return (int64_t)key0 + KT > a.offset + q0 + 1 || key0 + KT > key_end;
-        if (MODE == KEYS_DENSE) return key0 + KT > key_end;
-        return false;
+        return key0 + KT > key_end;  // dense, block lists: the key tail
     };
     auto row_max = [&](f16x (&s)[NSB], int key0, bool masked) -> float {
         if (masked && tile_needs_mask(key0)) {
@@ -864,6 +868,11 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         n_plain = (int)max((int64_t)0, min((int64_t)n_tiles, (lim - key_begin) / KT));
     } else if (MODE == KEYS_DENSE) {
         n_plain = key_end / KT;
+    } else if (MODE == KEYS_BLOCKS && a.Lkv % kTileN != 0) {
+        // a partial last block: a dense-prefix item's keys ascend, so only its
+        // last tiles need the tail mask; a list may hold the partial block at
+        // any position, so every one of its tiles is checked
+        n_plain = blist ? 0 : (key_stop - key_begin) / KT;
     }
     int it = 0;
     for (; it + PH < n_plain; it += PH) {

@@ -4,11 +4,13 @@
 // projections", key_quant.py / query_pool.py: the tile sum divided by the
 // valid count with one rounding, stored in FP32).
 //
-//   1. vsa_pool_kernel: qbar, kbar = RNE32(sum of a 64-row block / 64). One
-//      wave per block; each lane sums 16 rows of 8 columns in FP64, which is
-//      exact for FP16 inputs (all are integer multiples of 2^-24 below 2^16,
-//      and 64 of them fit in 53 bits), so the order of the partial sums does
-//      not change the result. HBM-bound: Q and K are read once.
+//   1. vsa_pool_kernel: qbar, kbar = RNE32(sum of a block's rows / their
+//      count); blocks hold 64 rows, the last one of a sequence whose length is
+//      not a multiple of 64 fewer. One wave per block; each lane sums 16 rows
+//      of 8 columns in FP64, which is exact for FP16 inputs (all are integer
+//      multiples of 2^-24 below 2^16, and 64 of them fit in 53 bits), so the
+//      order of the partial sums does not change the result. HBM-bound: Q and
+//      K are read once.
 //   2. vsa_scores_kernel: s[i][j] = sum over d ascending of qbar[i][d] *
 //      kbar[j][d], one FP64 FMA chain per (i, j) (each FP32 x FP32 product is
 //      exact in FP64, so every step rounds exactly like "acc + product").
@@ -35,21 +37,49 @@ constexpr int kMaxNB = 1024;
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
+// The FP32 value nearest to sum / count, ties to even, for an exact FP64 sum
+// of FP16 values and a count of at most 64: the FP64 quotient rounded to FP32
+// is the answer or one of its neighbours, and their distances |c * count -
+// sum| are exact in FP64 (a 24-bit c times a 7-bit count).
+__device__ __forceinline__ float mean_rn(double sum, int count)
+{
+    const float c0 = (float)(sum / count);
+    const float cand[2] = {nextafterf(c0, -INFINITY), nextafterf(c0, INFINITY)};
+    float best = c0;
+    double err = fabs((double)c0 * count - sum);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const double e = fabs((double)cand[i] * count - sum);
+        if (e < err || (e == err && (__float_as_uint(cand[i]) & 1u) == 0)) {
+            best = cand[i];
+            err = e;
+        }
+    }
+    return best;
+}
+
 // grid: (B*H*NB / 4 rounded up, 2) — y selects Q (0) or K (1); 4 waves, one
-// block each. Lane l reads columns 8*(l%16) .. +7 of rows l/16 + 4i, i < 16.
+// block each. Lane l reads columns 8*(l%16) .. +7 of rows l/16 + 4i, i < 16,
+// of the block's valid rows.
 __global__ __launch_bounds__(256) void vsa_pool_kernel(const uint16_t* __restrict__ q,
-                                                       const uint16_t* __restrict__ k, int64_t n_bhb,
-                                                       float* __restrict__ pooled)
+                                                       const uint16_t* __restrict__ k, int64_t n_bhb, int L,
+                                                       int NB, float* __restrict__ pooled)
 {
     const int lane = threadIdx.x & 63;
     const int64_t bhb = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b*H + h) * NB + blk
     if (bhb >= n_bhb) return;
     const int which = blockIdx.y;
-    const uint16_t* src = (which ? k : q) + bhb * (int64_t)kBlock * kD;
+    const int64_t bh = bhb / NB;
+    const int blk = (int)(bhb - bh * NB);
+    const int count = min(kBlock, L - blk * kBlock);
+    const uint16_t* src = (which ? k : q) + (bh * L + (int64_t)blk * kBlock) * kD;
     const int col = lane & 15, r0 = lane >> 4;
     h8 x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = *(const h8*)(src + (r0 + 4 * i) * kD + col * 8);
+    for (int i = 0; i < 16; ++i) {
+        const int row = r0 + 4 * i;
+        x[i] = row < count ? *(const h8*)(src + row * kD + col * 8) : h8{};
+    }
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -63,10 +93,10 @@ __global__ __launch_bounds__(256) void vsa_pool_kernel(const uint16_t* __restric
     }
     if (lane < 16) {
         float* dst = pooled + ((int64_t)which * n_bhb + bhb) * kD + col * 8;
-        float4 lo = {(float)(acc[0] * (1.0 / kBlock)), (float)(acc[1] * (1.0 / kBlock)),
-                     (float)(acc[2] * (1.0 / kBlock)), (float)(acc[3] * (1.0 / kBlock))};
-        float4 hi = {(float)(acc[4] * (1.0 / kBlock)), (float)(acc[5] * (1.0 / kBlock)),
-                     (float)(acc[6] * (1.0 / kBlock)), (float)(acc[7] * (1.0 / kBlock))};
+        float4 lo = {mean_rn(acc[0], count), mean_rn(acc[1], count), mean_rn(acc[2], count),
+                     mean_rn(acc[3], count)};
+        float4 hi = {mean_rn(acc[4], count), mean_rn(acc[5], count), mean_rn(acc[6], count),
+                     mean_rn(acc[7], count)};
         *(float4*)dst = lo;
         *(float4*)(dst + 4) = hi;
     }
@@ -207,12 +237,12 @@ hipError_t launch_vsa_select(const uint16_t* q, const uint16_t* k, int B, int H,
                              hipStream_t stream)
 {
     if (D != kD) return hipErrorInvalidValue;
-    const int NB = L / kBlock;
+    const int NB = (L + kBlock - 1) / kBlock;
     if (NB > kMaxNB) return hipErrorInvalidValue;
     const int64_t n_bhb = (int64_t)B * H * NB;
     if (n_bhb <= 0) return hipSuccess;
     hipLaunchKernelGGL(vsa_pool_kernel, dim3((unsigned)((n_bhb + 3) / 4), 2), dim3(256), 0, stream, q, k,
-                       n_bhb, pooled);
+                       n_bhb, L, NB, pooled);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const float* qbar = pooled;

@@ -192,16 +192,16 @@ int kv_e4m3_paged_to_fp16(const uint8_t* k_cache, const uint8_t* v_cache, const 
 
 /*
  * VSA block selection ([P3] Purpose; [P5] key_quant.py and query_pool.py for
- * the tile means). With NB = L / block:
- *   qbar[b,h,t,:] = RNE32(sum of the block's FP16 query rows / block),
+ * the tile means). With NB = ceil(L / block) (the last block may hold fewer
+ * than block rows when L is not a multiple of block):
+ *   qbar[b,h,t,:] = RNE32(sum of the block's FP16 query rows / their count),
  *   kbar likewise from k,
  *   s[b,h,i,j]    = sum over d ascending of qbar[b,h,i,d] * kbar[b,h,j,d] in FP64,
  * and idx_out[b,h,i,:] = the topk block indices j with the largest s[b,h,i,j]
  * (equal scores ranked by the lower j), written in ascending order.
  * q, k: FP16 [B,H,L,D] contiguous. idx_out: int32 [B,H,NB,topk] contiguous.
  * score_out: optional FP64 [B,H,NB,NB] (NULL to skip).
- * Domain: D == 128; block == 64; L % block == 0; 1 <= NB <= 1024;
- * 1 <= topk <= NB.
+ * Domain: D == 128; block == 64; L >= 1; 1 <= NB <= 1024; 1 <= topk <= NB.
  * workspace: at least vsa_block_select_workspace(...) bytes (the FP32 pooled
  * means, then the FP64 block scores when score_out is NULL), 256-byte aligned.
  */
@@ -214,11 +214,13 @@ int vsa_block_select(const uint16_t* q, const uint16_t* k, int B, int H, int L, 
  * VSA block-sparse attention ([P3] Purpose). Query block bq = i / block of
  * head h attends to the keys of the blocks idx[b,h,bq,0..topk) when
  * bq >= dense_prefix_qblocks, and to every key when bq < dense_prefix_qblocks.
- * q, k, v, o: FP16 [B,H,L,D] views; idx: int32 [B,H,L/block,topk] contiguous,
- * entries distinct and in [0, L/block) (out-of-range entries are clamped);
+ * With NB = ceil(L / block), the last block may be partial; keys past L are
+ * never attended to and rows past L are not written.
+ * q, k, v, o: FP16 [B,H,L,D] views; idx: int32 [B,H,NB,topk] contiguous,
+ * entries distinct and in [0, NB) (out-of-range entries are clamped);
  * lse: optional FP32 [B,H,L].
- * Domain: D == 128; block == 64; L % block == 0; 1 <= topk <= L/block;
- * 0 <= dense_prefix_qblocks <= L/block.
+ * Domain: D == 128; block == 64; L >= 1; 1 <= topk <= NB;
+ * 0 <= dense_prefix_qblocks <= NB.
  * workspace: at least vsa_block_sparse_attn_workspace(...) bytes, 256-byte
  * aligned, not overlapping any operand (may be NULL when that size is 0).
  * The dense-prefix query blocks are split into key segments whose FP32

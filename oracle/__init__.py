@@ -206,7 +206,7 @@ def vsa_pool(x: np.ndarray, block: int) -> np.ndarray:
     lib = _load()
     x = np.ascontiguousarray(x, dtype=np.float16)
     B, H, L, D = x.shape
-    out = np.empty((B, H, L // block, D), dtype=np.float32)
+    out = np.empty((B, H, (L + block - 1) // block, D), dtype=np.float32)
     lib.or_vsa_pool(_ptr(x), B, H, L, D, block, _ptr(out))
     return out
 

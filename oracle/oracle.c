@@ -180,7 +180,8 @@ int or_paged_gather(const uint8_t* cache, int64_t num_pages, int page_size, cons
 /*   mode 1  causal with offset: j <= offset + i, offset = kv_len - q_real,   */
 /*           the same rule for padded rows i >= q_real                        */
 /*   mode 2  block list: query block bq = i / block; bq < dense_prefix sees   */
-/*           all keys, otherwise the keys of blocks idx[b][h][bq][0..topk)    */
+/*           all keys, otherwise the keys (below Lkv: the last block may be   */
+/*           partial) of blocks idx[b][h][bq][0..topk)                        */
 /* GQA: query head h reads kv head h / (Hq / Hkv).                            */
 /* ------------------------------------------------------------------------ */
 
@@ -228,11 +229,14 @@ static int64_t keys_of_row(const attn_job* J, int b, int h, int i, int64_t* keys
             for (int64_t j = 0; j < J->Lkv; ++j)
                 keys[n++] = j;
         } else {
-            int nqb = J->Lq / J->block;
+            int nqb = (J->Lq + J->block - 1) / J->block;
             const int32_t* list = J->idx + (((int64_t)b * J->Hq + h) * nqb + bq) * J->topk;
             for (int t = 0; t < J->topk; ++t)
-                for (int u = 0; u < J->block; ++u)
-                    keys[n++] = (int64_t)list[t] * J->block + u;
+                for (int u = 0; u < J->block; ++u) {
+                    int64_t j = (int64_t)list[t] * J->block + u;
+                    if (j < J->Lkv) /* the last block may be partial */
+                        keys[n++] = j;
+                }
         }
     }
     return n;
@@ -372,22 +376,46 @@ void or_merge(int nseg, int D, const double* m, const double* l, const double* o
 /* the tile sum divided by the valid count with one rounding, stored FP32).   */
 /* ------------------------------------------------------------------------ */
 
-/* x [B,H,L,D] FP16 contiguous -> out [B,H,L/block,D] FP32 = RNE32(sum / block).
- * The FP64 sum of <= 2^10 FP16 values is exact (all are multiples of 2^-24
- * below 2^16), so the order of the sum does not matter. */
+/* The FP32 value nearest to sum / count (ties to even), for an exact FP64 sum
+ * of FP16 values and 1 <= count <= 1024: the FP64 quotient is within one FP32
+ * step of it, and each neighbour's distance |c * count - sum| is computed
+ * exactly (24-bit c times an 11-bit count fits in 53 bits). */
+static float or_div_rn_f32(double sum, int count)
+{
+    float best = (float)(sum / count);
+    double err = fabs((double)best * count - sum);
+    float nb[2] = {nextafterf(best, -INFINITY), nextafterf(best, INFINITY)};
+    for (int i = 0; i < 2; ++i) {
+        double e = fabs((double)nb[i] * count - sum);
+        uint32_t u;
+        memcpy(&u, &nb[i], 4);
+        if (e < err || (e == err && (u & 1u) == 0)) {
+            best = nb[i];
+            err = e;
+        }
+    }
+    return best;
+}
+
+/* x [B,H,L,D] FP16 contiguous -> out [B,H,ceil(L/block),D] FP32: the sum of the
+ * block's valid rows (the last block may be partial) divided by their count,
+ * rounded once. The FP64 sum of <= 2^10 FP16 values is exact (all are multiples
+ * of 2^-24 below 2^16), so the order of the sum does not matter. */
 void or_vsa_pool(const uint16_t* x, int B, int H, int L, int D, int block, float* out)
 {
-    int nb = L / block;
+    int nb = (L + block - 1) / block;
     for (int b = 0; b < B; ++b)
         for (int h = 0; h < H; ++h)
-            for (int t = 0; t < nb; ++t)
+            for (int t = 0; t < nb; ++t) {
+                int count = L - t * block < block ? L - t * block : block;
                 for (int d = 0; d < D; ++d) {
                     double sum = 0.0;
-                    for (int u = 0; u < block; ++u)
+                    for (int u = 0; u < count; ++u)
                         sum += or_f16_to_f64(
                             x[(((int64_t)b * H + h) * L + (int64_t)t * block + u) * D + d]);
-                    out[(((int64_t)b * H + h) * nb + t) * D + d] = (float)(sum / block);
+                    out[(((int64_t)b * H + h) * nb + t) * D + d] = or_div_rn_f32(sum, count);
                 }
+            }
 }
 
 /* s[b,h,i,j] = sum_{d ascending} qbar[b,h,i,d] * kbar[b,h,j,d] in FP64. Each

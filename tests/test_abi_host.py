@@ -200,7 +200,9 @@ def test_vsa_rejections():
                                     a["ws_bytes"], None)
     assert select(block=128) == fa.FA_ERR_UNSUPPORTED
     assert select(D=256) == fa.FA_ERR_UNSUPPORTED
-    assert select(L=4000) == fa.FA_ERR_SHAPE
+    assert select(L=0) == fa.FA_ERR_SHAPE
+    # a length that is not a multiple of the block: the last block is partial
+    assert lib.vsa_block_select_workspace(1, 2, 4000, 128, 64) == 2 * 2 * 63 * 128 * 4 + 2 * 63 * 63 * 8
     assert select(topk=0) == fa.FA_ERR_SHAPE
     assert select(topk=65) == fa.FA_ERR_SHAPE         # more than NB = 64
     assert select(L=64 * 1025, topk=4) == fa.FA_ERR_SHAPE

@@ -193,7 +193,8 @@ def test_bridge_paged_layout_bit_exact(lib):
                               oracle.e4m3_to_f16(g, float(np.float32(0.07))))
 
 
-@pytest.mark.parametrize("B,H,L,topk", [(1, 2, 4096, 8), (2, 1, 64 * 300, 64), (1, 1, 128, 2)])
+@pytest.mark.parametrize("B,H,L,topk", [(1, 2, 4096, 8), (2, 1, 64 * 300, 64), (1, 1, 128, 2),
+                                         (1, 2, 64 * 20 + 37, 6), (1, 1, 50, 1)])  # partial last blocks
 def test_vsa_select_bit_exact(lib, B, H, L, topk):
     say(f"vsa select B{B} H{H} L{L} k{topk}")
     q = synth.normal_f16(8, synth.TID_Q, (B, H, L, 128))
@@ -215,7 +216,8 @@ def test_vsa_select_ties_take_lower_index(lib):
     assert np.array_equal(idx.cpu().numpy()[0, 0], np.broadcast_to(np.arange(5), (40, 5)))
 
 
-@pytest.mark.parametrize("L,topk,dp", [(2048, 8, 2), (64 * 20, 20, 0), (1024, 3, 16)])
+@pytest.mark.parametrize("L,topk,dp", [(2048, 8, 2), (64 * 20, 20, 0), (1024, 3, 16),
+                                       (64 * 30 + 37, 7, 2), (64 * 6 + 1, 7, 7)])  # partial last blocks
 def test_vsa_sparse_attn_parity(lib, L, topk, dp):
     say(f"vsa sparse L{L} k{topk} dp{dp}")
     B, H, D = 1, 2, 128

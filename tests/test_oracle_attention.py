@@ -173,6 +173,23 @@ def test_full_block_list_equals_dense_and_prefix_rows_are_dense():
     assert np.abs(o1[:, : 2 * blk] - dense.reshape(H, L, D)[:, : 2 * blk]).max() < 1e-14
 
 
+def test_partial_last_block_list_equals_dense():
+    """L not a multiple of the block: a full list still equals dense attention,
+    and a list holding only the partial last block sees only its valid keys."""
+    rng = np.random.default_rng(12)
+    B, H, L, D, blk = 1, 2, 200, 16, 32  # 7 blocks, the last one of 8 keys
+    nb = (L + blk - 1) // blk
+    q, k, v = (rng.standard_normal((B, H, L, D)).astype(np.float16) for _ in range(3))
+    dense, _ = oracle.attention(q, k, v, 0.25)
+    full = np.broadcast_to(np.arange(nb, dtype=np.int32), (B, H, nb, nb)).copy()
+    sparse, _ = oracle.attention(q, k, v, 0.25, mode=oracle.MODE_BLOCKS, idx=full, block=blk)
+    assert np.abs(dense - sparse).max() < 1e-14
+    last = np.full((B, H, nb, 1), nb - 1, np.int32)
+    o1, _ = oracle.attention(q, k, v, 0.25, mode=oracle.MODE_BLOCKS, idx=last, block=blk)
+    sub, _ = oracle.attention(q, k[:, :, (nb - 1) * blk:], v[:, :, (nb - 1) * blk:], 0.25)
+    assert np.abs(o1 - sub).max() < 1e-14
+
+
 def test_merge_over_any_split_equals_whole():
     rng = np.random.default_rng(10)
     D, L = 24, 300

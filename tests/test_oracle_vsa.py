@@ -25,6 +25,31 @@ def test_pool_equals_exact_fixed_point_mean():
     assert np.array_equal(ours, tm)
 
 
+def _nearest_f32(fr):
+    """The float32 nearest to a Fraction, ties to even, by exact rational comparison."""
+    from fractions import Fraction
+    f = np.float32(float(fr))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - fr), int(np.array(c).view(np.uint32)) & 1))
+    return best
+
+
+def test_pool_partial_tile_is_the_exact_mean_rounded_once():
+    """A last block of 37 valid rows: every mean equals the exactly computed
+    rational sum / 37 rounded once to FP32 (not twice)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(3)
+    L, D = 64 + 37, 24
+    x = (rng.standard_normal((1, 1, L, D)) * 100).astype(np.float16)
+    ours = oracle.vsa_pool(x, 64)
+    assert ours.shape == (1, 1, 2, D)
+    ints = (x.astype(np.float64) * 2.0 ** 24).astype(np.int64)[0, 0]
+    for t, (lo, hi) in enumerate([(0, 64), (64, L)]):
+        for d in range(D):
+            exact = Fraction(int(ints[lo:hi, d].sum()), 2 ** 24 * (hi - lo))
+            assert ours[0, 0, t, d] == _nearest_f32(exact), (t, d)
+
+
 def test_scores_exact_on_integer_vectors_and_within_bound_otherwise():
     rng = np.random.default_rng(1)
     qi = rng.integers(-50, 50, (1, 2, 10, 128)).astype(np.float32)
