@@ -18,6 +18,8 @@ path, each timed with HIP events on the launch stream:
   * the exact paged E4M3 -> FP16 bridge, GB/s over the bytes it must move;
   * decode: 16 new positions of all 6 heads against the same 256000-token
     E4M3 cache, GB/s over the cache read once (HBM-bound);
+  * the FP8 round trip of prefix keys with the valid-row gather (B1 N36864
+    H8, 32768 rows), GB/s over K and V rows read and written;
   * VSA block selection (pool, score, top-k), GB/s over Q and K read once
     plus the indices written, and VSA block-sparse attention, TFLOP/s over
     the selected pairs.
@@ -251,6 +253,24 @@ def bench_paged(fa, torch, iters, timer, flush):
     return fused, bridge, decode
 
 
+def bench_prefix_fp8(fa, torch, iters, timer, flush):
+    import synth.workloads as wl
+    w = wl.PREFIX_FP8
+    log("generating", w["name"])
+    k, v, index = wl.prefix_fp8_inputs(w)
+    dk, dv = (torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16) for x in (k, v))
+    di = torch.from_numpy(index).cuda()
+    del k, v
+    ko = torch.empty((w["B"], w["rows"], w["H"], w["D"]), dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty_like(ko)
+    ms, _ = timer.run(lambda: fa.kv_prefix_fp8_gather(dk, dv, di, k_out=ko, v_out=vo), iters, 2, flush=flush)
+    nb = 4 * w["B"] * w["rows"] * w["H"] * w["D"] * 2 + 4 * w["rows"]
+    gbs = nb / (np.median(ms) * 1e-3) / 1e9
+    log(f"prefix fp8 gather: {np.median(ms) * 1e3:.1f} us  {gbs:.0f} GB/s")
+    return {"workload": w["name"], "bytes": nb, **stats(ms), "gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+            "llc_flushed": True}
+
+
 def bench_vsa(fa, torch, iters, timer, flush):
     import synth.workloads as wl
     w = wl.VSA
@@ -320,7 +340,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--iters", type=int, default=10, help="timed launches of each extra workload")
-    ap.add_argument("--only", choices=["dense", "causal", "ragged", "paged", "vsa", "copy"], default=None,
+    ap.add_argument("--only", choices=["dense", "causal", "ragged", "paged", "prefix", "vsa", "copy"], default=None,
                     help="run one workload only (for profiling); 'copy' runs the plain 1 GiB "
                          "device copy that calibrates the HBM byte counters")
     ap.add_argument("--no-extra", action="store_true", help="skip the non-headline workloads")
@@ -413,6 +433,9 @@ def main():
         if args.only in (None, "paged"):
             extra["paged_e4m3"], extra["e4m3_bridge"], extra["paged_e4m3_decode"] = bench_paged(
                 fa, torch, args.iters, timer, flush)
+            torch.cuda.empty_cache()
+        if args.only in (None, "prefix"):
+            extra["prefix_fp8_gather"] = bench_prefix_fp8(fa, torch, args.iters, timer, flush)
             torch.cuda.empty_cache()
         if args.only in (None, "vsa"):
             extra["vsa_select"], extra["vsa_sparse_attn"] = bench_vsa(fa, torch, args.iters, timer, flush)

@@ -24,7 +24,7 @@ EXPORTS = ("fa_abi_version", "fa_error_string", "attn_fwd_dense", "attn_fwd_dens
            "attn_fwd_prefix_causal_workspace",
            "attn_fwd_prefix_causal", "attn_fwd_paged_e4m3_workspace", "attn_fwd_paged_e4m3",
            "attn_fwd_paged_e4m3_decode_workspace", "attn_fwd_paged_e4m3_decode",
-           "kv_e4m3_paged_to_fp16", "vsa_block_select_workspace", "vsa_block_select",
+           "kv_e4m3_paged_to_fp16", "kv_prefix_fp8_gather", "vsa_block_select_workspace", "vsa_block_select",
            "vsa_block_sparse_attn_workspace", "vsa_block_sparse_attn")
 
 
@@ -55,6 +55,7 @@ _SIGS = {
     "attn_fwd_paged_e4m3_decode": (_i, [FaTensor, _vp, _vp, _vp, _i64, _i, _i, _f, _f, FaTensor, _vp]
                                    + [_i] * 7 + [_f, _vp, _sz, _vp]),
     "kv_e4m3_paged_to_fp16": (_i, [_vp, _vp, _vp, _i64] + [_i] * 6 + [_f, _f, _vp, _vp, _vp]),
+    "kv_prefix_fp8_gather": (_i, [_vp, _vp] + [_i] * 4 + [_vp, _i, _vp, _vp, _vp]),
     "vsa_block_select_workspace": (_sz, [_i] * 5),
     "vsa_block_select": (_i, [_vp, _vp] + [_i] * 6 + [_vp, _vp, _vp, _sz, _vp]),
     "vsa_block_sparse_attn_workspace": (_sz, [_i] * 7),
@@ -228,6 +229,26 @@ def kv_e4m3_paged_to_fp16(k_cache, v_cache, page_table, B, kv_len, k_scale=1.0, 
 
 
 # ---------------------------------------------------------------------------------- VSA
+
+def kv_prefix_fp8_gather(k, v, index, k_out=None, v_out=None):
+    """FP8 round trip of K per (row, head) with the row gather. k, v: bfloat16 [B, N, H, 128]
+    contiguous; index: int32 [rows]. Returns (k_out, v_out) bfloat16 [B, rows, H, 128]."""
+    import torch
+    _need_cuda(k, v, index, k_out, v_out)
+    if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16 or not k.is_contiguous() or not v.is_contiguous():
+        raise ValueError("k and v must be contiguous bfloat16 [B, N, H, D]")
+    if index.dtype != torch.int32 or not index.is_contiguous():
+        raise ValueError("index must be contiguous int32")
+    B, N, H, D = k.shape
+    rows = index.numel()
+    if k_out is None:
+        k_out = torch.empty((B, rows, H, D), dtype=torch.bfloat16, device=k.device)
+    if v_out is None:
+        v_out = torch.empty_like(k_out)
+    _check(load().kv_prefix_fp8_gather(k.data_ptr(), v.data_ptr(), B, N, H, D, index.data_ptr(), rows,
+                                       k_out.data_ptr(), v_out.data_ptr(), _stream(k)))
+    return k_out, v_out
+
 
 def vsa_block_select(q, k, topk, block=64, scores=False, workspace=None, out=None):
     """Top-k KV blocks per query block. Returns idx int32 [B,H,NB,topk] (and FP64 scores if asked)."""

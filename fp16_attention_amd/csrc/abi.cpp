@@ -498,6 +498,26 @@ int kv_e4m3_paged_to_fp16(const uint8_t* k_cache, const uint8_t* v_cache, const 
                                              k_out, v_out, (hipStream_t)stream));
 }
 
+int kv_prefix_fp8_gather(const uint16_t* k, const uint16_t* v, int B, int N, int H, int D,
+                         const int32_t* index, int rows, uint16_t* k_out, uint16_t* v_out, void* stream)
+{
+    if (!k || !v || !index || !k_out || !v_out) return FA_ERR_NULL;
+    if (D != 128) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || N < 1 || H < 1 || rows < 0) return FA_ERR_SHAPE;
+    if (rows == 0) return FA_OK;
+    if (((uintptr_t)k & 15u) || ((uintptr_t)v & 15u) || ((uintptr_t)k_out & 15u) || ((uintptr_t)v_out & 15u) ||
+        ((uintptr_t)index & 3u))
+        return FA_ERR_ALIGN;
+    const int64_t in_elems = (int64_t)B * N * H * D, out_elems = (int64_t)B * rows * H * D;
+    Span in[3] = {span_flat(k, in_elems, 2), span_flat(v, in_elems, 2), span_flat(index, rows, 4)};
+    Span out[2] = {span_flat(k_out, out_elems, 2), span_flat(v_out, out_elems, 2)};
+    if (overlap(out[0], out[1])) return FA_ERR_ALIAS;
+    for (const Span& o : out)
+        for (const Span& s : in)
+            if (overlap(o, s)) return FA_ERR_ALIAS;
+    return hip_status(fa::launch_prefix_fp8_gather(k, v, B, N, H, index, rows, k_out, v_out, (hipStream_t)stream));
+}
+
 // Workspace of vsa_block_select: the FP32 pooled means [2][B*H*NB][D], then
 // (256-byte aligned) the FP64 block scores [B*H*NB][NB].
 static size_t vsa_pooled_bytes(int B, int H, int L, int D)

@@ -95,6 +95,11 @@ hipError_t launch_e4m3_bridge(const uint8_t* kc, const uint8_t* vc, const int32_
                               int kv_len, float k_scale, float v_scale, uint16_t* k_out,
                               uint16_t* v_out, hipStream_t stream);
 
+// K: FP8 round trip per (row, head) with the row gather; V: the gather.
+hipError_t launch_prefix_fp8_gather(const uint16_t* k, const uint16_t* v, int B, int N, int H,
+                                    const int32_t* index, int rows, uint16_t* k_out, uint16_t* v_out,
+                                    hipStream_t stream);
+
 // scores: FP64 [B*H*NB*NB] buffer the score kernel writes and the top-k kernel
 // reads; pooled: FP32 [2][B*H*NB][D] means.
 hipError_t launch_vsa_select(const uint16_t* q, const uint16_t* k, int B, int H, int L, int D,

@@ -191,6 +191,22 @@ int kv_e4m3_paged_to_fp16(const uint8_t* k_cache, const uint8_t* v_cache, const 
                           uint16_t* v_out, void* stream);
 
 /*
+ * FP8 round trip of prefix keys with the valid-row gather ([P5]
+ * prefix_quant.py, quantize_gather_prefix_kv; qknorm_rope.py, the PREFIX_FP8
+ * path). k, v: bfloat16 [B, N, H, D] contiguous; index: int32 [rows], the
+ * source token of each output row (clamped into [0, N)). For every (b, r, h),
+ * with x the FP32 values of k[b, index[r], h, :]:
+ *   scale = max |x| / 448, inv = (scale == 0 ? 0 : 1 / scale),
+ *   k_out[b, r, h, :] = RNE_bf16(decode(RNE_e4m3(clamp(x * inv, -448, 448))) * scale),
+ * every step rounding once in FP32 (OCP E4M3FN); v_out[b, r, h, :] =
+ * v[b, index[r], h, :]. Outputs are bfloat16 [B, rows, H, D] contiguous and
+ * must not overlap the inputs or each other.
+ * Domain: D == 128; B, N, H >= 1; rows >= 0 (0 is a no-op).
+ */
+int kv_prefix_fp8_gather(const uint16_t* k, const uint16_t* v, int B, int N, int H, int D,
+                         const int32_t* index, int rows, uint16_t* k_out, uint16_t* v_out, void* stream);
+
+/*
  * VSA block selection ([P3] Purpose; [P5] key_quant.py and query_pool.py for
  * the tile means). With NB = ceil(L / block) (the last block may hold fewer
  * than block rows when L is not a multiple of block):

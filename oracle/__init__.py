@@ -38,6 +38,13 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         lib.or_f16_to_f64.restype = ctypes.c_double
         lib.or_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.or_f32_to_e4m3.restype = ctypes.c_uint8
+        lib.or_f32_to_e4m3.argtypes = [ctypes.c_float]
+        lib.or_f32_to_bf16.restype = ctypes.c_uint16
+        lib.or_f32_to_bf16.argtypes = [ctypes.c_float]
+        lib.or_prefix_fp8_gather.restype = None
+        lib.or_prefix_fp8_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 4 + [
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         lib.or_bf16_to_f64.restype = ctypes.c_double
         lib.or_bf16_to_f64.argtypes = [ctypes.c_uint16]
         lib.or_f64_to_f16.restype = ctypes.c_uint16
@@ -120,6 +127,34 @@ def e4m3_to_f16(codes: np.ndarray, scale: float) -> np.ndarray:
     out = np.empty(c.shape, dtype=np.uint16)
     lib.or_e4m3_to_f16_array(_ptr(c), c.size, ctypes.c_float(np.float32(scale)), _ptr(out))
     return out
+
+
+def f32_to_e4m3(x) -> np.ndarray:
+    lib = _load()
+    a = np.asarray(x, dtype=np.float32).ravel()
+    return np.array([lib.or_f32_to_e4m3(float(v)) for v in a], dtype=np.uint8)
+
+
+def f32_to_bf16(x) -> np.ndarray:
+    lib = _load()
+    a = np.asarray(x, dtype=np.float32).ravel()
+    return np.array([lib.or_f32_to_bf16(float(v)) for v in a], dtype=np.uint16)
+
+
+def prefix_fp8_gather(k: np.ndarray, v: np.ndarray, index: np.ndarray):
+    """k, v: bfloat16 bit patterns (uint16) [B, N, H, D]; index: int32 source rows.
+    Returns (ko, vo) uint16 [B, rows, H, D]: K's FP8 round trip with a per-(row, head)
+    amax / 448 scale, and V, both gathered."""
+    lib = _load()
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    index = np.ascontiguousarray(index, dtype=np.int32)
+    B, N, H, D = k.shape
+    rows = index.size
+    ko = np.empty((B, rows, H, D), dtype=np.uint16)
+    vo = np.empty_like(ko)
+    lib.or_prefix_fp8_gather(_ptr(k), _ptr(v), B, N, H, D, _ptr(index), rows, _ptr(ko), _ptr(vo))
+    return ko, vo
 
 
 def paged_gather(cache: np.ndarray, table: np.ndarray, kv_len: int) -> np.ndarray:

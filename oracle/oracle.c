@@ -144,6 +144,78 @@ void or_e4m3_to_f16_array(const uint8_t* c, int64_t n, float scale, uint16_t* ou
 }
 
 /*
+ * The E4M3FN code nearest to a finite float x in [-448, 448], ties to the code
+ * with an even mantissa (round to nearest even); the sign of x is kept (a
+ * negative value that rounds to zero gives -0). Plain search over the codes of
+ * x's sign.
+ */
+uint8_t or_f32_to_e4m3(float x)
+{
+    pthread_once(&g_e4m3_once, e4m3_table_init);
+    int base = signbit(x) ? 0x80 : 0x00;
+    int best = base;
+    double err = INFINITY;
+    for (int m = 0; m < 127; ++m) { /* 0x7F / 0xFF are NaN */
+        double e = fabs(g_e4m3[base + m] - (double)x);
+        if (e < err || (e == err && ((base + m) & 1) == 0 && (best & 1) == 1)) {
+            best = base + m;
+            err = e;
+        }
+    }
+    return (uint8_t)best;
+}
+
+/* bfloat16 bits of the value nearest to a finite float, ties to even: the two
+   candidates are the truncation and the next bfloat16 away from zero. */
+uint16_t or_f32_to_bf16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    uint16_t lo = (uint16_t)(u >> 16), hi = (uint16_t)(lo + 1);
+    double dlo = or_bf16_to_f64(lo), dhi = or_bf16_to_f64(hi);
+    double elo = fabs((double)x - dlo), ehi = isfinite(dhi) ? fabs(dhi - (double)x) : INFINITY;
+    if (elo < ehi || (elo == ehi && (lo & 1) == 0))
+        return lo;
+    return hi;
+}
+
+/*
+ * FP8 round trip of prefix keys with the valid-row gather ([P5]
+ * prefix_quant.py, quantize_gather_prefix_kv). k, v: bfloat16 [B, N, H, D]
+ * contiguous; index: the `rows` source tokens. For every (b, r, h), with x
+ * the FP32 values of K's row index[r], head h:
+ *   scale = max |x| / 448 (FP32), inv = scale == 0 ? 0 : 1 / scale,
+ *   ko = RNE_bf16( decode( RNE_e4m3( clamp(x * inv, +-448) ) ) * scale ),
+ * each operation rounding once in FP32; vo is V's row copied. Outputs are
+ * [B, rows, H, D] bfloat16.
+ */
+void or_prefix_fp8_gather(const uint16_t* k, const uint16_t* v, int B, int N, int H, int D,
+                          const int32_t* index, int rows, uint16_t* ko, uint16_t* vo)
+{
+    for (int b = 0; b < B; ++b)
+        for (int r = 0; r < rows; ++r)
+            for (int h = 0; h < H; ++h) {
+                const int64_t src = (((int64_t)b * N + index[r]) * H + h) * D;
+                const int64_t dst = (((int64_t)b * rows + r) * H + h) * D;
+                volatile float amax = 0.0f;
+                for (int d = 0; d < D; ++d) {
+                    float a = fabsf((float)or_bf16_to_f64(k[src + d]));
+                    if (a > amax)
+                        amax = a;
+                }
+                volatile float scale = amax / 448.0f;
+                volatile float inv = scale == 0.0f ? 0.0f : 1.0f / scale;
+                for (int d = 0; d < D; ++d) {
+                    volatile float x = (float)or_bf16_to_f64(k[src + d]) * inv;
+                    float c = x < -448.0f ? -448.0f : (x > 448.0f ? 448.0f : x);
+                    volatile float y = (float)or_e4m3_decode(or_f32_to_e4m3(c)) * scale;
+                    ko[dst + d] = or_f32_to_bf16(y);
+                    vo[dst + d] = v[src + d];
+                }
+            }
+}
+
+/*
  * Paged cache gather (reading of [P4] "Implementation", paged E4M3 KV):
  * cache [num_pages, page_size, Hkv, D] bytes, table [B, pages_per_seq] int32,
  * logical token t of sequence b lives in page table[b][t / page_size], slot

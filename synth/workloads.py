@@ -17,7 +17,10 @@ seed = workload number and tensor ids Q=1, K=2, V=3, page table=4, scales=5.
 """
 from __future__ import annotations
 
-from . import TID_K, TID_Q, TID_SCALES, TID_TABLE, TID_V, e4m3_codes, normal_f16, permutation, uniform_f32
+import numpy as np
+
+from . import (TID_K, TID_Q, TID_SCALES, TID_TABLE, TID_V, e4m3_codes, normal_bf16, normal_f16, permutation,
+               uniform, uniform_f32)
 
 TINY_DENSE = dict(name="tiny dense attention B1 H2 D128 L256 non-causal", seed=1, B=1, H=2, D=128,
                   Lq=256, Lkv=256)
@@ -32,6 +35,9 @@ PAGED_E4M3 = dict(name="paged E4M3 causal prefill B1 Hq6 Hkv1 D256 Q8000 KV25600
                   Hq=6, Hkv=1, D=256, q_rows=8000, q_real=8000, kv_len=256000, page_size=32)
 PAGED_DECODE = dict(name="paged E4M3 decode B1 Hq6 Hkv1 D256 Q16 KV256000 page32", seed=4, B=1, Hq=6, Hkv=1,
                     D=256, q_rows=16, q_real=16, kv_len=256000, page_size=32)
+# valid-row gather with the FP8 round trip of the prefix keys, at the video shape
+PREFIX_FP8 = dict(name="FP8 prefix-key round trip + gather B1 N36864 H8 D128, 32768 valid rows", seed=8, B=1,
+                  N=36864, H=8, D=128, rows=32768)
 VSA = dict(name="VSA block-sparse attention B1 H8 D128 L36864 block64 top-k 64 dense-prefix 2", seed=5,
            B=1, H=8, D=128, L=36864, block=64, topk=64, dense_prefix=2)
 
@@ -78,3 +84,20 @@ def vsa_inputs(w):
     s = w["seed"]
     shape = (w["B"], w["H"], w["L"], w["D"])
     return normal_f16(s, TID_Q, shape), normal_f16(s, TID_K, shape), normal_f16(s, TID_V, shape)
+
+
+def prefix_fp8_inputs(w):
+    """k, v: bfloat16 bit patterns [B, N, H, D] of N(0,1) draws times a per-(token, head)
+    magnitude spread over 2^-8 .. 2^8; index: the sorted valid rows (a seeded subset)."""
+    s = w["seed"]
+    shape = (w["B"], w["N"], w["H"], w["D"])
+    k = normal_bf16(s, TID_K, shape)
+    v = normal_bf16(s, TID_V, shape)
+    # spread K's per-row magnitude: add a per-(token, head) exponent offset in [-8, 8] to the bfloat16 bits
+    e = (uniform(s, TID_SCALES, w["B"] * w["N"] * w["H"]) * 17).astype(np.int32) - 8
+    e = np.repeat(e.reshape(w["B"], w["N"], w["H"], 1), w["D"], axis=3)
+    expo = ((k >> 7) & 0xFF).astype(np.int32)
+    nz = expo > 0
+    k = np.where(nz, (k & 0x807F) | (np.clip(expo + e, 1, 254).astype(np.uint16) << 7), k).astype(np.uint16)
+    index = np.sort(permutation(s, TID_TABLE, w["N"])[: w["rows"]]).astype(np.int32)
+    return k, v, index

@@ -124,6 +124,24 @@ def test_paged_decode_full(lib):
     assert np.abs(lse.cpu().numpy().ravel() - ref_lse).max() < LSE_ABS
 
 
+def test_prefix_fp8_gather_full(lib):
+    """The video-shape gather (32768 of 36864 rows, 8 heads): V exactly everywhere, K bit-exact
+    on a seeded sample of output rows (the oracle computes those rows' index entries only)."""
+    w = wl.PREFIX_FP8
+    say("full prefix fp8", w["name"])
+    k, v, index = wl.prefix_fp8_inputs(w)
+    dk, dv = (dev(x.view(np.int16)).view(torch.bfloat16) for x in (k, v))
+    ko, vo = lib.kv_prefix_fp8_gather(dk, dv, dev(index))
+    torch.cuda.synchronize()
+    got_v = vo.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got_v, v[:, index]), "V gather differs"
+    rng = np.random.default_rng(8)
+    sample = np.unique(np.concatenate([[0, w["rows"] - 1], rng.integers(0, w["rows"], 1024)])).astype(np.int64)
+    rk, _ = oracle.prefix_fp8_gather(k, v, index[sample])
+    got_k = ko.view(torch.int16).cpu().numpy().view(np.uint16)[:, sample]
+    assert np.array_equal(got_k, rk), f"{int((got_k != rk).sum())} K mismatches on {sample.size} rows"
+
+
 def test_vsa_full(lib):
     w = wl.VSA
     say("full vsa", w["name"])

@@ -145,6 +145,46 @@ def test_paged_decode_parity(lib, Hq, Hkv, D, q_rows, q_real, kv_len, pages, ks,
     assert np.abs(lse.cpu().numpy().ravel() - ref_lse).max() < LSE_ABS
 
 
+@pytest.mark.parametrize("B,N,H,rows", [(2, 300, 3, 200), (1, 64, 1, 64), (1, 5, 2, 9)])
+def test_prefix_fp8_gather_bit_exact(lib, B, N, H, rows):
+    import synth.workloads as wl
+    say(f"prefix fp8 gather B{B} N{N} H{H} rows{rows}")
+    w = dict(wl.PREFIX_FP8, B=B, N=N, H=H, rows=min(rows, N))
+    k, v, index = wl.prefix_fp8_inputs(w)
+    if rows > N:  # repeated rows
+        index = np.resize(index, rows).astype(np.int32)
+    k[0, 0, 0] = 0                      # an all-zero (row, head): scale 0
+    k[0, 1 % N, 0, :5] = 0x8000          # negative zeros
+    k[0, 1 % N, 0, 5:9] = 0x0001         # tiny values: subnormal E4M3 codes after scaling
+    dk, dv = (dev(x.view(np.int16)).view(torch.bfloat16) for x in (k, v))
+    ko, vo = lib.kv_prefix_fp8_gather(dk, dv, dev(index))
+    torch.cuda.synchronize()
+    rk, rv = oracle.prefix_fp8_gather(k, v, index)
+    got_k = ko.view(torch.int16).cpu().numpy().view(np.uint16)
+    got_v = vo.view(torch.int16).cpu().numpy().view(np.uint16)
+    bad = np.nonzero(got_k != rk)
+    assert bad[0].size == 0, f"{bad[0].size} K mismatches, first {[hex(got_k[t]) for t in zip(*bad)][:4]} vs {[hex(rk[t]) for t in zip(*bad)][:4]}"
+    assert np.array_equal(got_v, rv)
+
+
+def test_prefix_fp8_then_bf16_attention(lib):
+    """The pages' use: attention of BF16 queries over the FP8-round-tripped prefix keys."""
+    import synth.workloads as wl
+    say("prefix fp8 + attention")
+    w = dict(wl.PREFIX_FP8, N=500, H=2, rows=300)
+    k, v, index = wl.prefix_fp8_inputs(w)
+    q = synth.normal_bf16(9, synth.TID_Q, (1, 2, 200, 128))
+    dk, dv = (dev(x.view(np.int16)).view(torch.bfloat16) for x in (k, v))
+    ko, vo = lib.kv_prefix_fp8_gather(dk, dv, dev(index))
+    dq = dev(q.view(np.int16)).view(torch.bfloat16)
+    scale = lib.default_scale(128)
+    out = lib.attn_fwd_dense(dq, ko.transpose(1, 2), vo.transpose(1, 2), scale=scale)
+    torch.cuda.synchronize()
+    rk, rv = oracle.prefix_fp8_gather(k, v, index)
+    ref, _ = oracle.attention(q, rk.transpose(0, 2, 1, 3), rv.transpose(0, 2, 1, 3), scale, bf16=True)
+    assert_close(out.double().cpu().numpy().reshape(-1, 128), ref, "O", BF16_MAX_ABS, BF16_REL_L2)
+
+
 def _bits_equal(got, want, codes, what):
     got = np.asarray(got).view(np.uint16).ravel()
     want = np.asarray(want).ravel()

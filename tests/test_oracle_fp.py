@@ -139,3 +139,50 @@ def test_paged_gather_identity_and_permutation():
     assert np.array_equal(oracle.paged_gather(moved, np.arange(pages, dtype=np.int32)[None], kv_len), g2)
     with pytest.raises(ValueError):
         oracle.paged_gather(cache, np.full((1, pages), pages, dtype=np.int32), kv_len)
+
+
+def test_f32_to_e4m3_matches_torch_float8():
+    """Every finite code value, every midpoint between neighbours (the ties) and
+    random values in [-448, 448], against torch's float32 -> float8_e4m3fn cast."""
+    vals = oracle.e4m3_decode_table()
+    fin = np.sort(vals[np.isfinite(vals)])
+    mids = (fin[:-1] + fin[1:]) / 2  # exact in FP32: E4M3 values have 4 significant bits
+    rng = np.random.default_rng(21)
+    rand = np.concatenate([rng.uniform(-448, 448, 4000), rng.uniform(-1, 1, 2000) * 2.0 ** -6])
+    x = np.concatenate([fin, mids, rand, [0.0, -0.0]]).astype(np.float32)
+    ours = oracle.f32_to_e4m3(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_f32_to_bf16_matches_torch():
+    """Random FP32 values and exact ties (low 16 bits 0x8000) against torch's bfloat16 cast."""
+    rng = np.random.default_rng(22)
+    u = rng.integers(0, 0x7F7F0000, 6000, dtype=np.uint64).astype(np.uint32)
+    ties = (u & 0xFFFF0000) | 0x8000
+    bits = np.concatenate([u, ties, u | 0x80000000]).astype(np.uint32)
+    x = bits.view(np.float32)
+    ours = oracle.f32_to_bf16(x)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_prefix_fp8_gather_matches_torch_dtype_casts():
+    """The round trip against torch float32 arithmetic with its float8_e4m3fn and
+    bfloat16 casts (independent conversion routines), plus the gather of V."""
+    rng = np.random.default_rng(23)
+    B, N, H, D = 2, 40, 3, 128
+    tk = torch.from_numpy(rng.standard_normal((B, N, H, D)) * rng.uniform(0.01, 30, (B, N, H, 1))).to(torch.bfloat16)
+    tv = torch.from_numpy(rng.standard_normal((B, N, H, D))).to(torch.bfloat16)
+    tk[0, 5, 1] = 0  # an all-zero row: scale 0
+    index = rng.permutation(N)[:25].astype(np.int32)
+    kb = tk.view(torch.int16).numpy().view(np.uint16)
+    vb = tv.view(torch.int16).numpy().view(np.uint16)
+    ko, vo = oracle.prefix_fp8_gather(kb, vb, index)
+    kg = tk.float()[:, torch.from_numpy(index).long()]
+    scale = kg.abs().amax(-1, keepdim=True) / 448.0
+    inv = torch.where(scale == 0, torch.zeros_like(scale), 1.0 / scale)
+    q8 = torch.clamp(kg * inv, -448.0, 448.0).to(torch.float8_e4m3fn).float()
+    ref = (q8 * scale).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ko, ref)
+    assert np.array_equal(vo, vb[:, index])
