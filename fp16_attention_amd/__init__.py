@@ -24,7 +24,8 @@ EXPORTS = ("fa_abi_version", "fa_error_string", "attn_fwd_dense", "attn_fwd_dens
            "attn_fwd_prefix_causal_workspace",
            "attn_fwd_prefix_causal", "attn_fwd_paged_e4m3_workspace", "attn_fwd_paged_e4m3",
            "attn_fwd_paged_e4m3_decode_workspace", "attn_fwd_paged_e4m3_decode",
-           "kv_e4m3_paged_to_fp16", "kv_prefix_fp8_gather", "vsa_block_select_workspace", "vsa_block_select",
+           "kv_e4m3_paged_to_fp16", "kv_prefix_fp8_gather", "vsa_topk_for_sparsity", "vsa_block_select_workspace",
+           "vsa_block_select",
            "vsa_block_sparse_attn_workspace", "vsa_block_sparse_attn")
 
 
@@ -56,6 +57,7 @@ _SIGS = {
                                    + [_i] * 7 + [_f, _vp, _sz, _vp]),
     "kv_e4m3_paged_to_fp16": (_i, [_vp, _vp, _vp, _i64] + [_i] * 6 + [_f, _f, _vp, _vp, _vp]),
     "kv_prefix_fp8_gather": (_i, [_vp, _vp] + [_i] * 4 + [_vp, _i, _vp, _vp, _vp]),
+    "vsa_topk_for_sparsity": (_i, [_i, _i, ctypes.c_double]),
     "vsa_block_select_workspace": (_sz, [_i] * 5),
     "vsa_block_select": (_i, [_vp, _vp] + [_i] * 6 + [_vp, _vp, _vp, _sz, _vp]),
     "vsa_block_sparse_attn_workspace": (_sz, [_i] * 7),
@@ -248,6 +250,14 @@ def kv_prefix_fp8_gather(k, v, index, k_out=None, v_out=None):
     _check(load().kv_prefix_fp8_gather(k.data_ptr(), v.data_ptr(), B, N, H, D, index.data_ptr(), rows,
                                        k_out.data_ptr(), v_out.data_ptr(), _stream(k)))
     return k_out, v_out
+
+
+def vsa_topk_for_sparsity(L: int, sparsity: float, block: int = 64) -> int:
+    """Blocks kept per query block for a VSA keep ratio (1 - sparsity)."""
+    k = int(load().vsa_topk_for_sparsity(L, block, sparsity))
+    if k < 0:
+        raise FaError(-k, error_string(-k))
+    return k
 
 
 def vsa_block_select(q, k, topk, block=64, scores=False, workspace=None, out=None):

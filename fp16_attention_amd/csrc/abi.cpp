@@ -518,6 +518,17 @@ int kv_prefix_fp8_gather(const uint16_t* k, const uint16_t* v, int B, int N, int
     return hip_status(fa::launch_prefix_fp8_gather(k, v, B, N, H, index, rows, k_out, v_out, (hipStream_t)stream));
 }
 
+int vsa_topk_for_sparsity(int L, int block, double sparsity)
+{
+    if (block < 1 || L < 1 || !(sparsity >= 0.0) || !(sparsity < 1.0)) return -FA_ERR_SHAPE;
+    const int NB = (L + block - 1) / block;
+    // a product within 1e-9 of an integer is that integer: 1 - 0.7 is not 0.3 in binary
+    const double x = (1.0 - sparsity) * NB;
+    const double n = nearbyint(x);
+    const int keep = fabs(x - n) <= 1e-9 * NB ? (int)n : (int)ceil(x);
+    return keep < 1 ? 1 : keep;
+}
+
 // Workspace of vsa_block_select: the FP32 pooled means [2][B*H*NB][D], then
 // (256-byte aligned) the FP64 block scores [B*H*NB][NB].
 static size_t vsa_pooled_bytes(int B, int H, int L, int D)

@@ -207,6 +207,16 @@ int kv_prefix_fp8_gather(const uint16_t* k, const uint16_t* v, int B, int N, int
                          const int32_t* index, int rows, uint16_t* k_out, uint16_t* v_out, void* stream);
 
 /*
+ * The top-k of a VSA keep ratio ([P5] the VSA_sparsity setting, 0.8 with
+ * 64-token tiles): with NB = ceil(L / block) blocks, keep
+ * max(1, ceil((1 - sparsity) * NB)) of them (116 of 576 at 0.8), a product
+ * within 1e-9 * NB of an integer taken as that integer. Host only.
+ * Returns that count, or -FA_ERR_SHAPE for block < 1, L < 1 or a sparsity
+ * outside [0, 1).
+ */
+int vsa_topk_for_sparsity(int L, int block, double sparsity);
+
+/*
  * VSA block selection ([P3] Purpose; [P5] key_quant.py and query_pool.py for
  * the tile means). With NB = ceil(L / block) (the last block may hold fewer
  * than block rows when L is not a multiple of block):

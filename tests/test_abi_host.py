@@ -241,3 +241,15 @@ def test_kernels_take_no_values_from_inline_asm():
             code = line.split("//")[0]
             if re.search(r"\basm\b", code):
                 assert any(a in code for a in allowed), f"{name}:{n}: {line.strip()}"
+
+
+def test_vsa_keep_ratio():
+    assert fa.vsa_topk_for_sparsity(36864, 0.8) == 116    # 576 blocks, 115.2 kept
+    assert fa.vsa_topk_for_sparsity(36864, 0.0) == 576
+    assert fa.vsa_topk_for_sparsity(64 * 3 + 1, 0.5) == 2  # 4 blocks, the last partial
+    assert fa.vsa_topk_for_sparsity(64, 0.99) == 1         # never below one block
+    assert fa.vsa_topk_for_sparsity(640, 0.7) == 3         # (1 - 0.7) * 10 is 3.0000000000000004
+    assert fa.vsa_topk_for_sparsity(1280, 0.9) == 2        # (1 - 0.9) * 20 is 1.9999999999999996
+    assert fa.vsa_topk_for_sparsity(36864, 1 - 64 / 576) == 64
+    with pytest.raises(fa.FaError):
+        fa.vsa_topk_for_sparsity(36864, 1.0)
