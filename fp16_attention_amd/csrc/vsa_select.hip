@@ -103,51 +103,60 @@ __global__ __launch_bounds__(256) void vsa_pool_kernel(const uint16_t* __restric
 }
 
 // grid: (ceil(NB/64)^2, B*H); 256 threads. Thread t owns query blocks
-// i0 + 4*(t/16) .. +3 and key blocks j0 + 4*(t%16) .. +3 of the tile.
+// i0 + 4*(t/16) .. +3 and key blocks j0 + 4*(t%16) .. +3 of the tile. The
+// means are staged 32 dimensions at a time, already widened to FP64 and
+// d-major, so the inner step is two LDS vector reads per 16 FMAs and a
+// workgroup needs 33 KB of LDS (four fit on a CU).
 constexpr int kST = 64;  // score tile edge
+constexpr int kDC = 32;  // dimensions per staged chunk
 __global__ __launch_bounds__(256) void vsa_scores_kernel(const float* __restrict__ qbar,
                                                          const float* __restrict__ kbar, int NB,
                                                          double* __restrict__ scores)
 {
-    __shared__ __attribute__((aligned(16))) float qs[kD][kST + 4];  // d-major: qs[d][i]
-    __shared__ __attribute__((aligned(16))) float ks[kD][kST + 4];
+    __shared__ __attribute__((aligned(16))) double qs[kDC][kST + 2];  // qs[d][i]
+    __shared__ __attribute__((aligned(16))) double ks[kDC][kST + 2];
     const int tid = threadIdx.x;
     const int tiles = (NB + kST - 1) / kST;
     const int i0 = (blockIdx.x / tiles) * kST, j0 = (blockIdx.x % tiles) * kST;
     const int64_t bh = blockIdx.y;
     const float* qb = qbar + bh * (int64_t)NB * kD;
     const float* kb = kbar + bh * (int64_t)NB * kD;
-    // stage: thread reads float4 (4 consecutive d) of row tid/32 + 8m, writes transposed
-    for (int m = 0; m < kST / 8; ++m) {
-        const int r = (tid >> 5) + 8 * m, d4 = (tid & 31) * 4;
-        float4 qv = {0.f, 0.f, 0.f, 0.f}, kv = {0.f, 0.f, 0.f, 0.f};
-        if (i0 + r < NB) qv = *(const float4*)(qb + (int64_t)(i0 + r) * kD + d4);
-        if (j0 + r < NB) kv = *(const float4*)(kb + (int64_t)(j0 + r) * kD + d4);
-        qs[d4][r] = qv.x;
-        qs[d4 + 1][r] = qv.y;
-        qs[d4 + 2][r] = qv.z;
-        qs[d4 + 3][r] = qv.w;
-        ks[d4][r] = kv.x;
-        ks[d4 + 1][r] = kv.y;
-        ks[d4 + 2][r] = kv.z;
-        ks[d4 + 3][r] = kv.w;
-    }
-    __syncthreads();
     const int ti = 4 * (tid >> 4), tj = 4 * (tid & 15);
     double acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[a][c] = 0.0;
-    for (int d = 0; d < kD; ++d) {
-        const float4 qv = *(const float4*)&qs[d][ti];
-        const float4 kv = *(const float4*)&ks[d][tj];
-        const double qd[4] = {qv.x, qv.y, qv.z, qv.w};
-        const double kd[4] = {kv.x, kv.y, kv.z, kv.w};
+    for (int d0 = 0; d0 < kD; d0 += kDC) {
+        if (d0 > 0) __syncthreads();  // every thread is done with the previous chunk
+        // stage: thread reads float4 (4 consecutive d) of rows tid/8 + 32m, writes them widened and transposed
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int m = 0; m < kST / 32; ++m) {
+            const int r = (tid >> 3) + 32 * m, d4 = (tid & 7) * 4;
+            float4 qv = {0.f, 0.f, 0.f, 0.f}, kv = {0.f, 0.f, 0.f, 0.f};
+            if (i0 + r < NB) qv = *(const float4*)(qb + (int64_t)(i0 + r) * kD + d0 + d4);
+            if (j0 + r < NB) kv = *(const float4*)(kb + (int64_t)(j0 + r) * kD + d0 + d4);
+            qs[d4][r] = qv.x;
+            qs[d4 + 1][r] = qv.y;
+            qs[d4 + 2][r] = qv.z;
+            qs[d4 + 3][r] = qv.w;
+            ks[d4][r] = kv.x;
+            ks[d4 + 1][r] = kv.y;
+            ks[d4 + 2][r] = kv.z;
+            ks[d4 + 3][r] = kv.w;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int d = 0; d < kDC; ++d) {
+            const double2 q01 = *(const double2*)&qs[d][ti], q23 = *(const double2*)&qs[d][ti + 2];
+            const double2 k01 = *(const double2*)&ks[d][tj], k23 = *(const double2*)&ks[d][tj + 2];
+            const double qd[4] = {q01.x, q01.y, q23.x, q23.y};
+            const double kd[4] = {k01.x, k01.y, k23.x, k23.y};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[a][c] = fma(qd[a], kd[c], acc[a][c]);
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[a][c] = fma(qd[a], kd[c], acc[a][c]);
+        }
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -190,10 +199,28 @@ __global__ __launch_bounds__(256) void vsa_topk_kernel(const double* __restrict_
     // at least topk keys >= T. After bits 63..b of T are fixed (in prefix),
     // `need` more keys must come from the `match` keys whose bits 63..b equal
     // prefix's; once match == need those are all taken and the lower bits of
-    // T no longer matter, so the walk stops there.
-    uint64_t prefix = 0;
-    int need = topk, match = NB, low = 0;  // low: bits below `low` are undecided
-    for (int bit = 63; bit >= 0; --bit) {
+    // T no longer matter, so the walk stops there. The bits every key shares
+    // (sign and most of the exponent, for scores of one magnitude) are fixed
+    // up front from the AND and OR of all keys.
+    uint64_t k_and = ~0ull, k_or = 0ull;
+#pragma unroll
+    for (int m = 0; m < kPerLane; ++m) {
+        if (m < per && lane + 64 * m < NB) {
+            k_and &= key[m];
+            k_or |= key[m];
+        }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        k_and &= __shfl_xor(k_and, o);
+        k_or |= __shfl_xor(k_or, o);
+    }
+    const uint64_t differ = k_and ^ k_or;  // bits where some keys differ
+    const int top = differ ? 63 - __clzll(differ) : -1;  // highest such bit
+    const uint64_t common = top < 0 ? ~0ull : top >= 63 ? 0ull : ~((2ull << top) - 1ull);  // bits above top
+    uint64_t prefix = k_and & common;
+    int need = topk, match = NB, low = top + 1;  // low: bits below `low` are undecided
+    for (int bit = (match == need ? -1 : top); bit >= 0; --bit) {
         const uint64_t cand = prefix | (1ull << bit);
         const uint64_t hi_mask = ~((1ull << bit) - 1ull);  // bits bit..63
         int cnt = 0;
@@ -214,12 +241,12 @@ __global__ __launch_bounds__(256) void vsa_topk_kernel(const double* __restrict_
     // keep keys whose bits 63..low exceed prefix's, and the `need` lowest-index
     // keys whose bits 63..low equal them (all of them after an early stop)
     int32_t* out = idx_out + row * topk;
-    const uint64_t tp = prefix >> low;
+    const uint64_t tp = low >= 64 ? 0ull : prefix >> low;
     int base = 0, eq_taken = 0;
     for (int m = 0; m < per; ++m) {
         const int j = lane + 64 * m;
         const bool valid = j < NB;
-        const uint64_t kt = key[m] >> low;
+        const uint64_t kt = low >= 64 ? 0ull : key[m] >> low;
         const bool gt = valid && kt > tp;
         const bool eq = valid && kt == tp;
         const uint64_t eq_mask = __ballot(eq);
