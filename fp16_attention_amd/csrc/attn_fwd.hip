@@ -7,8 +7,8 @@
 //     the key range into FP32 partial states that a second kernel merges
 //     ("[Kernel][SM70] Integrate FP32 v37 prefill and exact E4M3 bridge",
 //     Implementation),
-//   - the same prefill reading K/V from a paged E4M3 cache, decoded to FP16
-//     in registers on the way into LDS (same page, Purpose),
+//   - the same prefill reading K/V from a paged E4M3 cache, decoded exactly
+//     to FP16 inside the workgroup (same page, Purpose),
 //   - block-sparse attention over per-query-block KV block lists with dense
 //     prefix query blocks ("[Video] Integrate H3 SM70 execution, metrics and
 //     VSA diagnostics", Purpose).
@@ -20,8 +20,10 @@
 //   - LDS holds a ring of R K slots and R V slots. FP16 tiles move from
 //     HBM/L2 into LDS with buffer_load ... lds (no register staging; rows past
 //     the end of the key range read as zero through the buffer range check),
-//     R - 1 iterations ahead of their use. E4M3 tiles are loaded into
-//     registers, decoded exactly to FP16 and written to LDS.
+//     R - 1 iterations ahead of their use (at D = 256 a group's loads are
+//     spread over the MFMA steps of the iteration that issues them). E4M3
+//     code tiles move into a separate LDS byte ring the same way; the
+//     workgroup decodes each exactly to FP16 into the FP16 slots.
 //     K and V are stored row-major with 16-byte chunks XOR-swizzled by the
 //     row, which keeps the K operand reads and the transposing V reads free of
 //     bank conflicts.
