@@ -246,6 +246,23 @@ def test_vsa_select_bit_exact(lib, B, H, L, topk):
     assert np.array_equal(idx.cpu().numpy(), ref_idx)
 
 
+@pytest.mark.parametrize("k_sign", [1.0, -1.0])
+def test_vsa_select_scores_of_one_sign(lib, k_sign):
+    # every score near +-128: all keys share their sign and leading exponent bits
+    say(f"vsa select one-sign scores {k_sign:+.0f}")
+    B, H, L, topk = 1, 2, 64 * 24 + 5, 7
+    nq = synth.normal_f16(11, synth.TID_Q, (B, H, L, 128)).astype(np.float32)
+    nk = synth.normal_f16(11, synth.TID_K, (B, H, L, 128)).astype(np.float32)
+    q = (1.0 + 0.05 * nq).astype(np.float16)
+    k = (k_sign + 0.05 * nk).astype(np.float16)
+    idx, s = lib.vsa_block_select(dev(q), dev(k), topk, scores=True)
+    torch.cuda.synchronize()
+    ref_idx, ref_s = oracle.vsa_select(q, k, 64, topk)
+    assert np.all(np.sign(ref_s) == k_sign)
+    assert np.array_equal(s.cpu().numpy(), ref_s)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+
+
 def test_vsa_select_ties_take_lower_index(lib):
     say("vsa select ties")
     L = 64 * 40
