@@ -178,23 +178,26 @@ __device__ __forceinline__ uint64_t order_key(double s)
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-constexpr int kPerLane = kMaxNB / 64;
-
-// grid: ceil(B*H*NB / 4); 4 waves, one query block (row) each.
+// grid: ceil(B*H*NB / 4); 4 waves, one query block (row) each. PER keys per
+// lane (key j = lane + 64 * m, m < PER), PER * 64 >= NB.
+template <int PER>
 __global__ __launch_bounds__(256) void vsa_topk_kernel(const double* __restrict__ scores, int NB, int topk,
                                                        int64_t rows, int32_t* __restrict__ idx_out)
 {
+    constexpr int kPerLane = PER;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     const double* sr = scores + row * NB;
-    const int per = (NB + 63) / 64;  // keys per lane, key j = lane + 64 * m
+    // all loads first (indices clamped into the row), so they are in flight
+    // together; then the keys
+    double sv[kPerLane];
+#pragma unroll
+    for (int m = 0; m < kPerLane; ++m) sv[m] = sr[min(lane + 64 * m, NB - 1)];
     uint64_t key[kPerLane];
 #pragma unroll
-    for (int m = 0; m < kPerLane; ++m) {
-        const int j = lane + 64 * m;
-        key[m] = (m < per && j < NB) ? order_key(sr[j]) : 0ull;  // key 0 is below every real key
-    }
+    for (int m = 0; m < kPerLane; ++m)
+        key[m] = lane + 64 * m < NB ? order_key(sv[m]) : 0ull;  // key 0 is below every real key
     // Radix select, most significant bit first: T is the largest value with
     // at least topk keys >= T. After bits 63..b of T are fixed (in prefix),
     // `need` more keys must come from the `match` keys whose bits 63..b equal
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(256) void vsa_topk_kernel(const double* __restrict_
     uint64_t k_and = ~0ull, k_or = 0ull;
 #pragma unroll
     for (int m = 0; m < kPerLane; ++m) {
-        if (m < per && lane + 64 * m < NB) {
+        if (lane + 64 * m < NB) {
             k_and &= key[m];
             k_or |= key[m];
         }
@@ -223,11 +226,10 @@ __global__ __launch_bounds__(256) void vsa_topk_kernel(const double* __restrict_
     for (int bit = (match == need ? -1 : top); bit >= 0; --bit) {
         const uint64_t cand = prefix | (1ull << bit);
         const uint64_t hi_mask = ~((1ull << bit) - 1ull);  // bits bit..63
+        // a key past the row is 0 and never equals cand (cand has a bit set)
         int cnt = 0;
 #pragma unroll
-        for (int m = 0; m < kPerLane; ++m) {
-            if (m < per) cnt += __popcll(__ballot((key[m] & hi_mask) == cand && lane + 64 * m < NB));
-        }
+        for (int m = 0; m < kPerLane; ++m) cnt += __popcll(__builtin_amdgcn_ballot_w64((key[m] & hi_mask) == cand));
         if (cnt >= need) {
             prefix = cand;
             match = cnt;
@@ -243,7 +245,8 @@ __global__ __launch_bounds__(256) void vsa_topk_kernel(const double* __restrict_
     int32_t* out = idx_out + row * topk;
     const uint64_t tp = low >= 64 ? 0ull : prefix >> low;
     int base = 0, eq_taken = 0;
-    for (int m = 0; m < per; ++m) {
+#pragma unroll
+    for (int m = 0; m < kPerLane; ++m) {
         const int j = lane + 64 * m;
         const bool valid = j < NB;
         const uint64_t kt = low >= 64 ? 0ull : key[m] >> low;
@@ -279,8 +282,12 @@ hipError_t launch_vsa_select(const uint16_t* q, const uint16_t* k, int B, int H,
                        stream, qbar, kbar, NB, scores);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(vsa_topk_kernel, dim3((unsigned)((n_bhb + 3) / 4)), dim3(256), 0, stream, scores, NB,
-                       topk, n_bhb, idx_out);
+    if (NB <= 9 * 64)
+        hipLaunchKernelGGL(vsa_topk_kernel<9>, dim3((unsigned)((n_bhb + 3) / 4)), dim3(256), 0, stream, scores,
+                           NB, topk, n_bhb, idx_out);
+    else
+        hipLaunchKernelGGL(vsa_topk_kernel<kMaxNB / 64>, dim3((unsigned)((n_bhb + 3) / 4)), dim3(256), 0,
+                           stream, scores, NB, topk, n_bhb, idx_out);
     return hipGetLastError();
 }
 
