@@ -68,7 +68,8 @@ void fill_view(const fa_tensor& t, const _Float16*& p, int64_t& sb, int64_t& sh,
 // query tile's key range is cut into nseg near-equal segments; nseg is the
 // smallest count whose work items fill the resident workgroup slots of the
 // chip (one per CU at D = 256, two at D = 128) in whole rounds best, since a
-// last, partly filled round costs as much as a full one.
+// last, partly filled round costs far more than its share of the work (about
+// half a round's time at a quarter filled, with two slots per CU).
 struct SplitPlan {
     int n_qt, nseg;
     size_t workspace;
