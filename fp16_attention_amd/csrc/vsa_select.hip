@@ -103,25 +103,27 @@ __global__ __launch_bounds__(256) void vsa_pool_kernel(const uint16_t* __restric
 }
 
 // grid: (ceil(NB/64)^2, B*H); 256 threads. Thread t owns query blocks
-// i0 + 4*(t/16) .. +3 and key blocks j0 + 4*(t%16) .. +3 of the tile. The
-// means are staged 32 dimensions at a time, already widened to FP64 and
-// d-major, so the inner step is two LDS vector reads per 16 FMAs and a
-// workgroup needs 33 KB of LDS (four fit on a CU).
+// i0 + 4*(t/16) .. +3 and key blocks j0 + t%16 + 16c, c < 4, of the tile.
+// The means are staged 32 dimensions at a time, widened to FP64 and d-major
+// (32 KB, four workgroups per CU). Both the staging writes (consecutive lanes,
+// consecutive blocks) and the key reads (consecutive lanes, consecutive
+// doubles) are free of LDS bank conflicts; the query reads are broadcasts.
 constexpr int kST = 64;  // score tile edge
 constexpr int kDC = 32;  // dimensions per staged chunk
 __global__ __launch_bounds__(256) void vsa_scores_kernel(const float* __restrict__ qbar,
                                                          const float* __restrict__ kbar, int NB,
                                                          double* __restrict__ scores)
 {
-    __shared__ __attribute__((aligned(16))) double qs[kDC][kST + 2];  // qs[d][i]
-    __shared__ __attribute__((aligned(16))) double ks[kDC][kST + 2];
+    __shared__ __attribute__((aligned(16))) double qs[kDC][kST];  // qs[d][i]
+    __shared__ __attribute__((aligned(16))) double ks[kDC][kST];
     const int tid = threadIdx.x;
     const int tiles = (NB + kST - 1) / kST;
     const int i0 = (blockIdx.x / tiles) * kST, j0 = (blockIdx.x % tiles) * kST;
     const int64_t bh = blockIdx.y;
     const float* qb = qbar + bh * (int64_t)NB * kD;
     const float* kb = kbar + bh * (int64_t)NB * kD;
-    const int ti = 4 * (tid >> 4), tj = 4 * (tid & 15);
+    const int ti = 4 * (tid >> 4), tj = tid & 15;
+    const int sr = tid & 63, sd = (tid >> 6) * 8;  // staging: tile row sr, dimensions sd .. sd+7
     double acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -129,29 +131,32 @@ __global__ __launch_bounds__(256) void vsa_scores_kernel(const float* __restrict
         for (int c = 0; c < 4; ++c) acc[a][c] = 0.0;
     for (int d0 = 0; d0 < kD; d0 += kDC) {
         if (d0 > 0) __syncthreads();  // every thread is done with the previous chunk
-        // stage: thread reads float4 (4 consecutive d) of rows tid/8 + 32m, writes them widened and transposed
+        float4 qv0 = {0.f, 0.f, 0.f, 0.f}, qv1 = qv0, kv0 = qv0, kv1 = qv0;
+        if (i0 + sr < NB) {
+            const float* src = qb + (int64_t)(i0 + sr) * kD + d0 + sd;
+            qv0 = *(const float4*)src;
+            qv1 = *(const float4*)(src + 4);
+        }
+        if (j0 + sr < NB) {
+            const float* src = kb + (int64_t)(j0 + sr) * kD + d0 + sd;
+            kv0 = *(const float4*)src;
+            kv1 = *(const float4*)(src + 4);
+        }
+        const float qf[8] = {qv0.x, qv0.y, qv0.z, qv0.w, qv1.x, qv1.y, qv1.z, qv1.w};
+        const float kf[8] = {kv0.x, kv0.y, kv0.z, kv0.w, kv1.x, kv1.y, kv1.z, kv1.w};
 #pragma unroll
-        for (int m = 0; m < kST / 32; ++m) {
-            const int r = (tid >> 3) + 32 * m, d4 = (tid & 7) * 4;
-            float4 qv = {0.f, 0.f, 0.f, 0.f}, kv = {0.f, 0.f, 0.f, 0.f};
-            if (i0 + r < NB) qv = *(const float4*)(qb + (int64_t)(i0 + r) * kD + d0 + d4);
-            if (j0 + r < NB) kv = *(const float4*)(kb + (int64_t)(j0 + r) * kD + d0 + d4);
-            qs[d4][r] = qv.x;
-            qs[d4 + 1][r] = qv.y;
-            qs[d4 + 2][r] = qv.z;
-            qs[d4 + 3][r] = qv.w;
-            ks[d4][r] = kv.x;
-            ks[d4 + 1][r] = kv.y;
-            ks[d4 + 2][r] = kv.z;
-            ks[d4 + 3][r] = kv.w;
+        for (int e = 0; e < 8; ++e) {
+            qs[sd + e][sr] = qf[e];
+            ks[sd + e][sr] = kf[e];
         }
         __syncthreads();
 #pragma unroll 4
         for (int d = 0; d < kDC; ++d) {
             const double2 q01 = *(const double2*)&qs[d][ti], q23 = *(const double2*)&qs[d][ti + 2];
-            const double2 k01 = *(const double2*)&ks[d][tj], k23 = *(const double2*)&ks[d][tj + 2];
             const double qd[4] = {q01.x, q01.y, q23.x, q23.y};
-            const double kd[4] = {k01.x, k01.y, k23.x, k23.y};
+            double kd[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) kd[c] = ks[d][tj + 16 * c];
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(256) void vsa_scores_kernel(const float* __restrict
         double* row = scores + (bh * NB + i) * (int64_t)NB;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            if (j0 + tj + c < NB) row[j0 + tj + c] = acc[a][c];
+            if (j0 + tj + 16 * c < NB) row[j0 + tj + 16 * c] = acc[a][c];
     }
 }
 
