@@ -16,7 +16,7 @@
 // Work decomposition (MI355X-first, not the pages' SM70/SM121 designs):
 //   - A workgroup owns WAVES x 32 query rows of one (batch, head); every wave
 //     keeps its 32 query rows in registers as the MFMA B operand and streams
-//     32-key tiles of K and V through LDS.
+//     tiles of K and V through LDS (64 keys for dense D = 128, else 32).
 //   - LDS holds a ring of R K slots and R V slots. FP16 tiles move from
 //     HBM/L2 into LDS with buffer_load ... lds (no register staging; rows past
 //     the end of the key range read as zero through the buffer range check),
@@ -282,8 +282,11 @@ struct ByteDecoder {
 // ---------------------------------------------------------------------------
 template <int D, int SRC, int MODE>
 struct Tiling {
-    static constexpr int KT = 32;
-    static constexpr int R = (SRC != KV_E4M3_PAGED && MODE != KEYS_BLOCKS) ? 4 : 2;
+    // dense D = 128: 64-key tiles in a two-slot ring (half the barriers and
+    // per-tile overhead of 32-key tiles, same LDS, two workgroups per CU)
+    static constexpr bool WIDE = D == 128 && MODE == KEYS_DENSE;
+    static constexpr int KT = WIDE ? 64 : 32;
+    static constexpr int R = WIDE ? 2 : (SRC != KV_E4M3_PAGED && MODE != KEYS_BLOCKS) ? 4 : 2;
     static constexpr int RB = SRC == KV_E4M3_PAGED ? 4 : 1;  // E4M3 byte slots per K and V ring
     static constexpr int PH = SRC == KV_E4M3_PAGED ? RB : R;  // phases of the unrolled loop
 };
@@ -614,10 +617,12 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 
     // One exponential unit: scores r, r+1 of score block kb -> P (FP16) in the
     // PV operand order (register r of block kb is k-step 2kb + r/8, slot r%8).
+    // Units run block by block (u / 8 is the block), as the score MFMAs of the
+    // next tile do, so a block's scores die as its successor's accumulate.
     const h2 ones = {(_Float16)1.f, (_Float16)1.f};
     const bf2 ones_bf = {(__bf16)1.f, (__bf16)1.f};
     auto exp_unit = [&](const f16x (&s)[NSB], int u, float m_use, h8* pk) {
-        const int kb = u % NSB, r = 2 * (u / NSB);
+        const int kb = u / 8, r = 2 * (u % 8);
         const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], a.c, -m_use));
         const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], a.c, -m_use));
         h2 p;
@@ -806,7 +811,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         // ---- block B ----
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         h8 kop[NB];
-        auto kread = [&](int i) { return *(const h8*)(kt + koff_s[i / NSB] + (i % NSB) * 32 * ROW); };
+        auto kread = [&](int i) { return *(const h8*)(kt + koff_s[i % KK] + (i / KK) * 32 * ROW); };
         constexpr int PB = D == 256 ? 4 : 3;  // K operand reads in flight
 #pragma unroll
         for (int i = 0; i < PB; ++i) kop[i] = kread(i);
@@ -814,7 +819,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             if (i + PB < NB) kop[i + PB] = kread(i + PB);
-            const int kb = i % NSB, kk = i / NSB;
+            const int kb = i / KK, kk = i % KK;
             sn[kb] = mma<BF>(kop[i], qf[kk], kk == 0 ? f16x{} : sn[kb]);
             if constexpr (SPREAD) {
                 if (i % (NB / NL) == 1) DL::issue_one(sg.k, dl.koff, kslot(p), wave, i / (NB / NL));
