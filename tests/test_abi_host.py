@@ -20,7 +20,8 @@ A, B_, C, O, L, W = (0x10000000 * (i + 1) for i in range(6))
 
 
 def _declared():
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return set(re.findall(r"\b([a-z_0-9]+)\s*\([^;{]*\)\s*;", text)) - {"if", "while"}
 
@@ -237,7 +238,9 @@ def test_kernels_take_no_values_from_inline_asm():
     for name in sorted(os.listdir(csrc)):
         if not name.endswith((".hip", ".h", ".cpp")):
             continue
-        for n, line in enumerate(open(os.path.join(csrc, name)), 1):
+        with open(os.path.join(csrc, name)) as f:
+            lines = f.read().splitlines()
+        for n, line in enumerate(lines, 1):
             code = line.split("//")[0]
             if re.search(r"\basm\b", code):
                 assert any(a in code for a in allowed), f"{name}:{n}: {line.strip()}"
