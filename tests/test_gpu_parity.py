@@ -18,6 +18,8 @@ def dev(x):
 @pytest.mark.parametrize("B,H,Lq,Lkv,D", [(1, 2, 256, 256, 128),     # the tiny dense workload
                                           (2, 3, 300, 1000, 128),    # ragged query and key tails
                                           (1, 2, 129, 65, 256),
+                                          (1, 2, 200, 100, 128),     # one full 64-key tile, then a partial one
+                                          (1, 1, 130, 321, 128),     # an odd count of full tiles, then one key
                                           (1, 1, 1, 1, 128)])        # single row, single key
 def test_dense_parity(lib, B, H, Lq, Lkv, D):
     say(f"dense B{B} H{H} Lq{Lq} Lkv{Lkv} D{D}")
