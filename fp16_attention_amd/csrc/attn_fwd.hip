@@ -793,7 +793,8 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     // steps separated by scheduling fences: block B issues the score MFMAs of
     // tile it+1 with the exponentials of tile it between them, block C the PV
     // MFMAs of tile it with the row maximum of tile it+1 between them; every
-    // LDS operand read is issued two to four MFMAs ahead.
+    // LDS operand read is issued two to four MFMAs ahead, the first V reads
+    // already in the last steps of block B.
     auto iteration_main = [&](auto p, int it) {
         using PN = std::integral_constant<int, decltype(p)::value + 1>;
         const unsigned char* kt = kslot(PN{});
@@ -808,6 +809,10 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         SpreadGroup sg;
         if constexpr (SPREAD) sg = spread_group(it);
 
+        // V operands: the first PC are read in the last steps of block B
+        h8 vop[NC];
+        constexpr int PC = D == 256 ? 3 : 2;  // V operand reads in flight
+
         // ---- block B ----
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         h8 kop[NB];
@@ -821,6 +826,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
             if (i + PB < NB) kop[i + PB] = kread(i + PB);
             const int kb = i / KK, kk = i % KK;
             sn[kb] = mma<BF>(kop[i], qf[kk], kk == 0 ? f16x{} : sn[kb]);
+            if (i >= NB - PC) vop[i - (NB - PC)] = vread(vt, i - (NB - PC));
             if constexpr (SPREAD) {
                 if (i % (NB / NL) == 1) DL::issue_one(sg.k, dl.koff, kslot(p), wave, i / (NB / NL));
             }
@@ -843,10 +849,6 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
             else
                 Dec::store(vslot(Q1{}), braw[u], tid, u - Dec::kChunks);
         };
-        h8 vop[NC];
-        constexpr int PC = D == 256 ? 3 : 2;  // V operand reads in flight
-#pragma unroll
-        for (int i = 0; i < PC; ++i) vop[i] = vread(vt, i);
         if constexpr (NDC > 0) {
 #pragma unroll
             for (int i = 0; i < Dec::kChunks; ++i) {
