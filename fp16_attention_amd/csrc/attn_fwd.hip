@@ -270,20 +270,23 @@ struct ByteDecoder {
 // The attention kernel.
 //
 // Tiling<D, SRC, MODE>: KT keys per K/V tile and R slots per K and V ring.
-// FP16 K/V stream through rings of four 32-key slots (64 KB of LDS at
-// D = 128, so two workgroups share a CU; 128 KB at D = 256), giving each
-// load three iterations to arrive: all workgroups on an XCD read the same
-// tiles at about the same time, so every tile costs them the latency of an
-// L2 miss together. Block lists (two 32-key tiles per selected block) use two
-// slots: their two-wave workgroups then take 32 KB, four per CU, which keeps
-// two waves on every SIMD. The paged E4M3 source is staged through registers
-// with two slots, fed from a four-slot ring of E4M3 byte tiles (at D = 256:
-// 64 KB of FP16 slots and 64 KB of byte slots).
+// The causal FP16/BF16 K/V stream through rings of four 32-key slots (64 KB
+// of LDS at D = 128, so two workgroups share a CU; 128 KB at D = 256), giving
+// each load three iterations to arrive: all workgroups on an XCD read the
+// same tiles at about the same time, so every tile costs them the latency of
+// an L2 miss together. Dense D = 128 uses two 64-key slots instead (the same
+// 64 KB). Block lists (two 32-key tiles per selected block) use two slots:
+// their two-wave workgroups then take 32 KB, four per CU, which keeps two
+// waves on every SIMD. The paged E4M3 source is decoded into two FP16 slots
+// from a four-slot ring of E4M3 byte tiles (at D = 256: 64 KB of FP16 slots
+// and 64 KB of byte slots).
 // ---------------------------------------------------------------------------
 template <int D, int SRC, int MODE>
 struct Tiling {
     // dense D = 128: 64-key tiles in a two-slot ring (half the barriers and
-    // per-tile overhead of 32-key tiles, same LDS, two workgroups per CU)
+    // per-tile overhead of 32-key tiles, same LDS, two workgroups per CU).
+    // Dense D = 256 keeps 32-key tiles: two score blocks per tile would not
+    // fit the registers next to its FP32 output accumulators.
     static constexpr bool WIDE = D == 128 && MODE == KEYS_DENSE;
     static constexpr int KT = WIDE ? 64 : 32;
     static constexpr int R = WIDE ? 2 : (SRC != KV_E4M3_PAGED && MODE != KEYS_BLOCKS) ? 4 : 2;
