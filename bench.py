@@ -355,7 +355,7 @@ def main():
                          "device copy that calibrates the HBM byte counters")
     ap.add_argument("--no-extra", action="store_true", help="skip the non-headline workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=128, help="oracle rows per head for cpu_baseline")
+    ap.add_argument("--cpu-rows", type=int, default=384, help="oracle rows per head for cpu_baseline")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch of the dense kernel (from rocprofv3 PMC runs)")
     args = ap.parse_args()
