@@ -20,6 +20,7 @@ def dev(x):
                                           (1, 2, 129, 65, 256),
                                           (1, 2, 200, 100, 128),     # one full 64-key tile, then a partial one
                                           (1, 1, 130, 321, 128),     # an odd count of full tiles, then one key
+                                          (1, 2, 600, 4100, 128),    # three 256-row query tiles, many key tiles
                                           (1, 1, 1, 1, 128)])        # single row, single key
 def test_dense_parity(lib, B, H, Lq, Lkv, D):
     say(f"dense B{B} H{H} Lq{Lq} Lkv{Lkv} D{D}")
