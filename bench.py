@@ -30,6 +30,11 @@ last-level cache, outside the timed events.
 headline workload on this host's cores (a reported baseline, not a target),
 and "parity_sample" compares those rows with the GPU output.
 
+"roofline.measured_ceiling" is the rate of fa_mfma_ceiling, a kernel of
+nothing but FP16 MFMAs on operands varied per lane: the matrix throughput the
+chip sustains on data like these inputs, timed right after the headline and
+reported beside the published peak.
+
 Only one GPU is supported: --gpus N with N > 1 exits with an error.
 """
 from __future__ import annotations
@@ -313,6 +318,17 @@ def bench_vsa(fa, torch, iters, timer, flush):
 
 # -------------------------------------------------------------------------- CPU oracle
 
+def bench_mfma_ceiling(fa, torch, timer, iters=16384, launches=5):
+    """FP16 MFMA rate the chip sustains on varied operands (fa_mfma_ceiling):
+    the attainable matrix throughput beside the published peak."""
+    out = torch.empty(fa.MFMA_CEILING_OUT, dtype=torch.float32, device="cuda")
+    ms, _ = timer.run(lambda: fa.mfma_ceiling(out, iters), launches, 2)
+    tf = fa.mfma_ceiling_flop(iters) / (np.median(ms) * 1e-3) / 1e12
+    log(f"MFMA ceiling (varied FP16 operands): {np.median(ms):.3f} ms, {tf:.0f} TFLOP/s")
+    return {"value": tf, "unit": "TFLOP/s", "kind": "fa_mfma_ceiling: FP16 MFMAs only, operands varied per lane",
+            "flop_per_launch": fa.mfma_ceiling_flop(iters), **stats(ms)}
+
+
 def cpu_baseline(w, qkv, out_gpu, rows_per_head):
     """Time the FP64 oracle on a seeded sample of query rows of the headline
     workload and compare the GPU output on those rows."""
@@ -350,7 +366,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--iters", type=int, default=10, help="timed launches of each extra workload")
-    ap.add_argument("--only", choices=["dense", "causal", "ragged", "paged", "prefix", "vsa", "copy"], default=None,
+    ap.add_argument("--only", choices=["dense", "causal", "ragged", "paged", "prefix", "vsa", "copy", "ceiling"], default=None,
                     help="run one workload only (for profiling); 'copy' runs the plain 1 GiB "
                          "device copy that calibrates the HBM byte counters")
     ap.add_argument("--no-extra", action="store_true", help="skip the non-headline workloads")
@@ -388,6 +404,10 @@ def main():
 
     extra = {}
     result = None
+    if args.only == "ceiling":
+        print(json.dumps({"metric": "fp16 mfma ceiling", "partial": True, "only": "ceiling",
+                          **bench_mfma_ceiling(fa, torch, timer)}), flush=True)
+        return
     if args.only == "copy":
         # A plain copy of a known size: the kernel whose FETCH_SIZE / WRITE_SIZE
         # readings scale the attention kernel's counters to bytes.
@@ -423,6 +443,10 @@ def main():
                          "algorithmic_flop_per_launch": flop},
         }
         result["headline_stats"] = stats(ms)
+        ceiling = bench_mfma_ceiling(fa, torch, timer)
+        result["roofline"]["measured_ceiling"] = ceiling["value"]
+        result["roofline"]["frac_of_measured_ceiling"] = achieved / ceiling["value"]
+        result["mfma_ceiling"] = ceiling
         if not args.no_cpu:
             out_np = out.cpu().numpy()
             cpu, parity = cpu_baseline(w, qkv, out_np, args.cpu_rows)

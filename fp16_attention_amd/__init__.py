@@ -26,7 +26,7 @@ EXPORTS = ("fa_abi_version", "fa_error_string", "attn_fwd_dense", "attn_fwd_dens
            "attn_fwd_paged_e4m3_decode_workspace", "attn_fwd_paged_e4m3_decode",
            "kv_e4m3_paged_to_fp16", "kv_prefix_fp8_gather", "vsa_topk_for_sparsity", "vsa_block_select_workspace",
            "vsa_block_select",
-           "vsa_block_sparse_attn_workspace", "vsa_block_sparse_attn")
+           "vsa_block_sparse_attn_workspace", "vsa_block_sparse_attn", "fa_mfma_ceiling")
 
 
 class FaTensor(ctypes.Structure):
@@ -62,6 +62,7 @@ _SIGS = {
     "vsa_block_select": (_i, [_vp, _vp] + [_i] * 6 + [_vp, _vp, _vp, _sz, _vp]),
     "vsa_block_sparse_attn_workspace": (_sz, [_i] * 7),
     "vsa_block_sparse_attn": (_i, [FaTensor] * 4 + [_vp, _vp] + [_i] * 7 + [_f, _vp, _sz, _vp]),
+    "fa_mfma_ceiling": (_i, [_i, _vp, _vp]),
 }
 
 
@@ -303,4 +304,23 @@ def vsa_block_sparse_attn(q, k, v, idx, dense_prefix_qblocks=2, block=64, out=No
     _check(load().vsa_block_sparse_attn(_view(q), _view(k), _view(v), _view(out), idx.data_ptr(), _ptr(lse),
                                         B, H, L, D, block, topk, dense_prefix_qblocks, scale, _ptr(ws), nbytes,
                                         _stream(q)))
+    return out
+
+
+MFMA_CEILING_OUT = 512 * 256  # FP32 values fa_mfma_ceiling writes
+
+
+def mfma_ceiling_flop(iters: int) -> float:
+    """FLOP of one fa_mfma_ceiling launch."""
+    return 512.0 * 4 * iters * 4 * 32768
+
+
+def mfma_ceiling(out, iters: int):
+    """Launch the FP16 MFMA rate kernel (a measurement aid) on out's stream;
+    out: CUDA float32 tensor of at least MFMA_CEILING_OUT elements."""
+    _need_cuda(out)
+    import torch
+    if out.dtype != torch.float32 or out.numel() < MFMA_CEILING_OUT or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor of MFMA_CEILING_OUT elements")
+    _check(load().fa_mfma_ceiling(int(iters), out.data_ptr(), _stream(out)))
     return out

@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa16attn.so")
-SOURCES = ["abi.cpp", "attn_fwd.hip", "e4m3_bridge.hip", "prefix_fp8.hip", "vsa_select.hip"]
+SOURCES = ["abi.cpp", "attn_fwd.hip", "e4m3_bridge.hip", "mfma_ceiling.hip", "prefix_fp8.hip",
+           "vsa_select.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming packed FP32 VALU ops.

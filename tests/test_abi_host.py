@@ -256,3 +256,12 @@ def test_vsa_keep_ratio():
     assert fa.vsa_topk_for_sparsity(36864, 1 - 64 / 576) == 64
     with pytest.raises(fa.FaError):
         fa.vsa_topk_for_sparsity(36864, 1.0)
+
+
+def test_mfma_ceiling_rejections():
+    lib = fa.load()
+    assert lib.fa_mfma_ceiling(16, None, None) == fa.FA_ERR_NULL
+    # the pointer is never dereferenced on the host, and no launch happens
+    assert lib.fa_mfma_ceiling(0, 256, None) == fa.FA_ERR_SHAPE
+    assert lib.fa_mfma_ceiling((1 << 20) + 1, 256, None) == fa.FA_ERR_SHAPE
+    assert fa.mfma_ceiling_flop(1000) == 512.0 * 4 * 1000 * 4 * 32768
