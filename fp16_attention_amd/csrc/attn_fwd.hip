@@ -62,6 +62,8 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s4 lds_s4_t;
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i_t;
 
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
@@ -201,9 +203,10 @@ struct DirectLoader {
 // ---------------------------------------------------------------------------
 // Paged E4M3 tiles. A 32-key tile is one page: its codes move into an LDS byte
 // slot with buffer_load ... lds (row-major, D bytes per row; wave w's j-th
-// load covers the 1 KB block (w + WAVES * j) of the tile), and the workgroup
-// then decodes the slot exactly into an FP16 tile, each thread one or two
-// 16-code chunks.
+// load covers the 1 KB block (w + WAVES * j) of the tile, each lane one 16-code
+// chunk). Chunk c of row r sits at position c ^ bswz<D>(r), which keeps the
+// 8-byte K operand reads and the byte-transposing V reads free of bank
+// conflicts. The MFMA operands are decoded from these codes in registers.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 
@@ -211,6 +214,19 @@ typedef __attribute__((address_space(4))) const int32_t const_i32;
 __device__ __forceinline__ int scalar_load(const int32_t* p, int i)
 {
     return __builtin_bit_cast(const const_i32*, p)[i];
+}
+
+template <int D>
+__device__ __forceinline__ int bswz(int r)
+{
+    return D == 256 ? (r & 15) : ((r >> 1) & 7);  // 16 chunks per row, or 8 (then rows pair up in a bank line)
+}
+
+// byte offset of code d of row r in a byte tile
+template <int D>
+__device__ __forceinline__ int btile_off(int r, int d)
+{
+    return r * D + ((((d >> 4) ^ bswz<D>(r))) << 4) + (d & 15);
 }
 
 template <int D, int WAVES, int KT>
@@ -224,7 +240,9 @@ struct ByteLoader {
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
             const int pos = (wave + WAVES * j) * 1024 + lane * 16;
-            off[j] = (pos / D) * row_stride + pos % D;
+            const int row = pos / D;
+            const int chunk = ((pos % D) >> 4) ^ bswz<D>(row);
+            off[j] = row * row_stride + chunk * 16;
         }
     }
 
@@ -240,32 +258,6 @@ struct ByteLoader {
     }
 };
 
-template <int D, int NT, int KT>
-struct ByteDecoder {
-    static constexpr int kChunks = KT * D / 16 / NT;  // 16-code chunks per thread per tile
-
-    // chunk i of this thread: the 16 codes of row c / (D/16), columns 16 (c % (D/16)) ..
-    static __device__ __forceinline__ u4 read(const unsigned char* bytes, int tid, int i)
-    {
-        const int c = tid + NT * i;
-        return *(const u4*)(bytes + (c / (D / 16)) * D + (c % (D / 16)) * 16);
-    }
-    static __device__ __forceinline__ void store(unsigned char* tile, u4 w, int tid, int i)
-    {
-        const int c = tid + NT * i;
-        const int row = c / (D / 16), c16 = c % (D / 16);
-        const u2 a0 = e4m3x4_to_f16(w.x), a1 = e4m3x4_to_f16(w.y);
-        const u2 a2 = e4m3x4_to_f16(w.z), a3 = e4m3x4_to_f16(w.w);
-        *(u4*)(tile + tile_off<D>(row, 2 * c16)) = u4{a0.x, a0.y, a1.x, a1.y};
-        *(u4*)(tile + tile_off<D>(row, 2 * c16 + 1)) = u4{a2.x, a2.y, a3.x, a3.y};
-    }
-    static __device__ __forceinline__ void run(const unsigned char* bytes, unsigned char* tile, int tid)
-    {
-#pragma unroll
-        for (int i = 0; i < kChunks; ++i) store(tile, read(bytes, tid, i), tid, i);
-    }
-};
-
 // ---------------------------------------------------------------------------
 // The attention kernel.
 //
@@ -277,9 +269,8 @@ struct ByteDecoder {
 // an L2 miss together. Dense D = 128 uses two 64-key slots instead (the same
 // 64 KB). Block lists (two 32-key tiles per selected block) use two slots:
 // their two-wave workgroups then take 32 KB, four per CU, which keeps two
-// waves on every SIMD. The paged E4M3 source is decoded into two FP16 slots
-// from a four-slot ring of E4M3 byte tiles (at D = 256: 64 KB of FP16 slots
-// and 64 KB of byte slots).
+// waves on every SIMD. The paged E4M3 source streams through four byte slots
+// of 32-key pages (32 KB at D = 256), decoded in registers as operands.
 // ---------------------------------------------------------------------------
 template <int D, int SRC, int MODE>
 struct Tiling {
@@ -289,26 +280,23 @@ struct Tiling {
     // fit the registers next to its FP32 output accumulators.
     static constexpr bool WIDE = D == 128 && MODE == KEYS_DENSE;
     static constexpr int KT = WIDE ? 64 : 32;
-    static constexpr int R = WIDE ? 2 : (SRC != KV_E4M3_PAGED && MODE != KEYS_BLOCKS) ? 4 : 2;
-    static constexpr int RB = SRC == KV_E4M3_PAGED ? 4 : 1;  // E4M3 byte slots per K and V ring
-    static constexpr int PH = SRC == KV_E4M3_PAGED ? RB : R;  // phases of the unrolled loop
+    static constexpr int R = WIDE ? 2 : MODE != KEYS_BLOCKS ? 4 : 2;
+    static constexpr int PH = R;  // phases of the unrolled loop
 };
 
 template <int D, int WAVES, int SRC, int MODE, bool SPLIT>
 __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kernel(const AttnArgs a)
 {
-    constexpr int NT = WAVES * 64;
     constexpr int M = WAVES * kRowsPerWave;
     constexpr int KT = Tiling<D, SRC, MODE>::KT;
     constexpr int NSB = KT / 32;  // 32-key score blocks per tile
     constexpr int KS = KT / 16;   // 16-key PV k-steps per tile
     constexpr int KK = D / 16;    // MFMA k-steps over D for S
     constexpr int DB = D / 32;    // 32-wide d blocks of O^T
-    constexpr int TB = KT * D * 2;
-    constexpr int ROW = 2 * D;    // bytes per LDS row
+    constexpr bool DIRECT = SRC != KV_E4M3_PAGED;  // 16-bit K/V (else E4M3 codes, decoded in registers)
+    constexpr int ROW = (DIRECT ? 2 : 1) * D;      // bytes per LDS row
+    constexpr int TB = KT * ROW;
     constexpr int R = Tiling<D, SRC, MODE>::R;
-    constexpr int RB = Tiling<D, SRC, MODE>::RB;
-    constexpr bool DIRECT = SRC != KV_E4M3_PAGED;  // 16-bit K/V loaded straight into LDS
     // D = 256: the loads of a ring group are spread over the next iteration's
     // MFMA steps instead of being issued together after the barrier (the
     // tile's bytes then arrive in LDS spread out too; measured 3-4% faster on
@@ -316,8 +304,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     constexpr bool SPREAD = DIRECT && D == 256;
     constexpr bool BF = SRC == KV_BF16;
     constexpr int PH = Tiling<D, SRC, MODE>::PH;
-    constexpr int BB = SRC == KV_E4M3_PAGED ? KT * D : 16;  // bytes per byte slot
-    static_assert(R >= 2 && R <= 4 && (DIRECT || (R == 2 && RB == 4)), "ring depth");
+    static_assert(R >= 2 && R <= 4, "ring depth");
     static_assert(DIRECT || KT == 32, "an E4M3 tile is one 32-token page");
     __shared__ __attribute__((aligned(1024))) unsigned char kslot0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char kslot1[TB];
@@ -327,18 +314,10 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     __shared__ __attribute__((aligned(1024))) unsigned char vslot1[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char vslot2[R > 2 ? TB : 16];
     __shared__ __attribute__((aligned(1024))) unsigned char vslot3[R > 3 ? TB : 16];
-    __shared__ __attribute__((aligned(1024))) unsigned char kbyte0[BB];
-    __shared__ __attribute__((aligned(1024))) unsigned char kbyte1[BB];
-    __shared__ __attribute__((aligned(1024))) unsigned char kbyte2[BB];
-    __shared__ __attribute__((aligned(1024))) unsigned char kbyte3[BB];
-    __shared__ __attribute__((aligned(1024))) unsigned char vbyte0[BB];
-    __shared__ __attribute__((aligned(1024))) unsigned char vbyte1[BB];
-    __shared__ __attribute__((aligned(1024))) unsigned char vbyte2[BB];
-    __shared__ __attribute__((aligned(1024))) unsigned char vbyte3[BB];
     // s_waitcnt that leaves the (ring depth - 2) most recent load groups in flight
     constexpr int kGroupLoads =
         2 * (DIRECT ? DirectLoader<D, WAVES, KT>::kLoads : ByteLoader<D, WAVES, KT>::kLoads);
-    constexpr int kVmLeft = ((DIRECT ? R : RB) - 2) * kGroupLoads;
+    constexpr int kVmLeft = (R - 2) * kGroupLoads;
     static_assert(kVmLeft < 64, "vmcnt range");
     constexpr int kWaitGroups = (kVmLeft & 15) | ((kVmLeft >> 4) << 14) | 0x0070;  // and lgkmcnt(0)
 
@@ -458,18 +437,6 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     auto valid_rows = [&](bool ok, int key0) {
         return __builtin_amdgcn_readfirstlane(ok ? max(0, min(KT, key_end - key0)) : 0);
     };
-    auto issue_k = [&](int it, unsigned char* slot) {
-        const bool ok = it < n_tiles;
-        const int key0 = tile_key0(ok ? it : n_tiles - 1);
-        DirectLoader<D, WAVES, KT>::issue(kbase + (int64_t)key0 * a.k_ss, a.k_ss, dl.koff,
-                                          valid_rows(ok, key0), slot, wave);
-    };
-    auto issue_v = [&](int it, unsigned char* slot) {
-        const bool ok = it < n_tiles;
-        const int key0 = tile_key0(ok ? it : n_tiles - 1);
-        DirectLoader<D, WAVES, KT>::issue(vbase + (int64_t)key0 * a.v_ss, a.v_ss, dl.voff,
-                                          valid_rows(ok, key0), slot, wave);
-    };
     // E4M3: tile it is page table[tile_key0(it) / 32] (tiles are page aligned)
     auto issue_b = [&](const uint8_t* cache, int it, unsigned char* slot) {
         const bool ok = it < n_tiles;
@@ -477,6 +444,26 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         const int page = min(max(scalar_load(table, key0 >> 5), 0), a.num_pages - 1);
         const int rows = ok ? min(KT, key_end - key0) : 0;
         bl.issue(cache + ((int64_t)page * 32 * a.Hkv + g) * D, rows * a.Hkv * D, slot, wave);
+    };
+    auto issue_k = [&](int it, unsigned char* slot) {
+        if constexpr (!DIRECT) {
+            issue_b(a.kc, it, slot);
+        } else {
+            const bool ok = it < n_tiles;
+            const int key0 = tile_key0(ok ? it : n_tiles - 1);
+            DirectLoader<D, WAVES, KT>::issue(kbase + (int64_t)key0 * a.k_ss, a.k_ss, dl.koff,
+                                              valid_rows(ok, key0), slot, wave);
+        }
+    };
+    auto issue_v = [&](int it, unsigned char* slot) {
+        if constexpr (!DIRECT) {
+            issue_b(a.vc, it, slot);
+        } else {
+            const bool ok = it < n_tiles;
+            const int key0 = tile_key0(ok ? it : n_tiles - 1);
+            DirectLoader<D, WAVES, KT>::issue(vbase + (int64_t)key0 * a.v_ss, a.v_ss, dl.voff,
+                                              valid_rows(ok, key0), slot, wave);
+        }
     };
 
     // ---- this lane's query row: head qh, position my_row ------------------------
@@ -508,23 +495,40 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     }
 
     // ---- per-lane LDS offsets ------------------------------------------------
-    // K operand of S^T = K Q^T: row l32 (+32 per score block), chunk 2kk + hlf.
-    // V^T operand of O^T += V^T P^T through ds_read_b64_tr_b16: within each
-    // 16-lane group G, source lane s points at 4 FP16 of key row
+    // K operand of S^T = K Q^T: row l32 (+32 per score block), d = 16kk + 8hlf .. +7.
+    // FP16 V^T operand of O^T += V^T P^T through ds_read_b64_tr_b16: within
+    // each 16-lane group G, source lane s points at 4 FP16 of key row
     // 4*(G/2) + s/4 (+8 for the second read), d = 32db + 16(G%2) + 4(s%4); the
     // transposing read then hands lane (G, t) the 4 keys of d = 32db+16(G%2)+t.
+    // Both hand lane (G, t) the keys 4(G/2) + 0..3 and 8 + 4(G/2) + 0..3 of
+    // its k-step, the order in which the score registers (and so P) hold them.
+    // E4M3 V^T operand through ds_read_b64_tr_b8: the read gives lane (G, t)
+    // element j from source lanes 2j and 2j+1 of its group, column
+    // d = 32db + 16(G%2) + t; so source lane s of group G points at 8 codes of
+    // key row 4*(G/2) + (s/2)%4 + 8*(s/8), d = 32db + 16(G%2) + 8(s%2).
     const int grp = lane >> 4, sl = lane & 15;
-    const int vrow = 4 * (grp >> 1) + (sl >> 2);
-    const int vbyte = (sl & 1) * 8;
-    const int vchunk = 2 * (grp & 1) + ((sl & 3) >> 1);
     int koff_s[KK];
     int voff_a[DB], voff_b[DB];
+    if constexpr (DIRECT) {
+        const int vrow = 4 * (grp >> 1) + (sl >> 2);
+        const int vbyte = (sl & 1) * 8;
+        const int vchunk = 2 * (grp & 1) + ((sl & 3) >> 1);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) koff_s[kk] = tile_off<D>(l32, 2 * kk + hlf);
+        for (int kk = 0; kk < KK; ++kk) koff_s[kk] = tile_off<D>(l32, 2 * kk + hlf);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        voff_a[db] = tile_off<D>(vrow, 4 * db + vchunk) + vbyte;
-        voff_b[db] = tile_off<D>(vrow + 8, 4 * db + vchunk) + vbyte;
+        for (int db = 0; db < DB; ++db) {
+            voff_a[db] = tile_off<D>(vrow, 4 * db + vchunk) + vbyte;
+            voff_b[db] = tile_off<D>(vrow + 8, 4 * db + vchunk) + vbyte;
+        }
+    } else {
+        const int vrow = 4 * (grp >> 1) + ((sl >> 1) & 3) + 8 * (sl >> 3);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) koff_s[kk] = btile_off<D>(l32, 16 * kk + 8 * hlf);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            voff_a[db] = btile_off<D>(vrow, 32 * db + 16 * (grp & 1) + 8 * (sl & 1));
+            voff_b[db] = 0;
+        }
     }
 
     f16x oacc[DB];
@@ -534,6 +538,26 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
     float m_run = -INFINITY;  // reference maximum of scores * c (log2 units)
     float l_run = 0.f;        // this lane half's share of the sum of P
+
+    // Operand fetch and use. FP16: the LDS read is the operand. E4M3: the
+    // read brings 8 codes, decoded exactly to FP16 only where the MFMA
+    // consumes them, so the read stays in flight meanwhile. Row offsets of
+    // score block kb and k-step kstep are multiples of 16 rows, where both
+    // swizzles repeat.
+    using KRaw = std::conditional_t<DIRECT, h8, u2>;
+    auto kfetch = [&](const unsigned char* kt, int kb, int kk) -> KRaw {
+        return *(const KRaw*)(kt + koff_s[kk] + kb * 32 * ROW);
+    };
+    auto decode8 = [](u2 w) -> h8 {
+        const u2 lo = e4m3x4_to_f16(w.x), hi = e4m3x4_to_f16(w.y);
+        return __builtin_bit_cast(h8, u4{lo.x, lo.y, hi.x, hi.y});
+    };
+    auto opuse = [&](const KRaw& r) -> h8 {
+        if constexpr (DIRECT)
+            return r;
+        else
+            return decode8(r);
+    };
 
     // S^T = K Q^T for KT keys x 32 queries (NSB blocks of 32 x 32)
     auto compute_s = [&](const unsigned char* kt, f16x (&s)[NSB]) {
@@ -545,23 +569,27 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
             for (int kb = 0; kb < NSB; ++kb) {
-                h8 k = *(const h8*)(kt + koff_s[kk] + kb * 32 * ROW);
-                s[kb] = mma<BF>(k, qf[kk], s[kb]);
+                s[kb] = mma<BF>(opuse(kfetch(kt, kb, kk)), qf[kk], s[kb]);
             }
     };
 
     // O^T += V^T P^T
-    auto vread = [&](const unsigned char* vt, int i) {
+    auto vread = [&](const unsigned char* vt, int i) -> KRaw {
         const int kstep = i / DB, db = i % DB;
-        s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + voff_a[db]));
-        s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + voff_b[db]));
-        return __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        if constexpr (DIRECT) {
+            s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + voff_a[db]));
+            s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + voff_b[db]));
+            return __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+            return __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                              (lds_v2i_t*)(vt + kstep * 16 * ROW + voff_a[db])));
+        }
     };
     auto compute_pv = [&](const unsigned char* vt, const h8* pk) {
 #pragma unroll
         for (int i = 0; i < KS * DB; ++i) {
             const int kstep = i / DB, db = i % DB;
-            oacc[db] = mma<BF>(vread(vt, i), pk[kstep], oacc[db]);
+            oacc[db] = mma<BF>(opuse(vread(vt, i)), pk[kstep], oacc[db]);
         }
     };
 
@@ -648,18 +676,12 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     };
 
     // ---- pipeline --------------------------------------------------------------
-    // K(j) and V(j) live in slot j % R. Load group g is {K(g+1), V(g)}; at the
-    // end of iteration it the slots of K(it+1) and V(it) are free and group
-    // it+R is issued into them, so every FP16 group has R-1 iterations to
-    // arrive. Invariant entering iteration it: S(it) is in scur with its
-    // maximum folded into m_run; K(it+1) and V(it) are in LDS; groups
-    // it+1 .. it+R-1 are in flight (FP16).
-    // E4M3: the codes of K(j) and V(j) live in byte slot j % RB and byte group
-    // g = {K(g+1), V(g)} is decoded during iteration g-1 into the FP16 slots
-    // (R = 2) that iteration does not read. Entering iteration it, byte group
-    // it+1 is in LDS and groups it+2 .. it+RB are in flight; at its end the
-    // slots of group it+1 are free and group it+RB+1 is issued into them, so
-    // every byte group has RB-1 iterations to arrive.
+    // K(j) and V(j) live in slot j % R (FP16 tiles, or E4M3 code tiles). Load
+    // group g is {K(g+1), V(g)}; at the end of iteration it the slots of
+    // K(it+1) and V(it) are free and group it+R is issued into them, so every
+    // group has R-1 iterations to arrive. Invariant entering iteration it:
+    // S(it) is in scur with its maximum folded into m_run; K(it+1) and V(it)
+    // are in LDS; groups it+1 .. it+R-1 are in flight.
     auto kslot = [&](auto p) -> unsigned char* {
         constexpr int S = decltype(p)::value % R;
         if constexpr (S == 0) return kslot0;
@@ -674,56 +696,22 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         else if constexpr (S == 2) return vslot2;
         else return vslot3;
     };
-    auto kbslot = [&](auto p) -> unsigned char* {
-        constexpr int S = decltype(p)::value % RB;
-        if constexpr (S == 0) return kbyte0;
-        else if constexpr (S == 1) return kbyte1;
-        else if constexpr (S == 2) return kbyte2;
-        else return kbyte3;
-    };
-    auto vbslot = [&](auto p) -> unsigned char* {
-        constexpr int S = decltype(p)::value % RB;
-        if constexpr (S == 0) return vbyte0;
-        else if constexpr (S == 1) return vbyte1;
-        else if constexpr (S == 2) return vbyte2;
-        else return vbyte3;
-    };
-    using Dec = ByteDecoder<D, NT, KT>;
-    // byte group g -> its slots; phase p stands for g modulo RB
-    auto issue_group_b = [&](auto p, int g8) {
-        using PN = std::integral_constant<int, decltype(p)::value + 1>;
-        issue_b(a.kc, g8 + 1, kbslot(PN{}));
-        issue_b(a.vc, g8, vbslot(p));
-    };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     using P2 = std::integral_constant<int, 2>;
     using P3 = std::integral_constant<int, 3>;
     using P4 = std::integral_constant<int, 4>;
 
-    if constexpr (DIRECT) {
-        issue_k(0, kslot0);
-        issue_v(0, vslot0);
-        issue_k(1, kslot1);
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    } else {
-        // byte groups -1 .. RB-2: K(0 .. RB-1), V(0 .. RB-2)
-        issue_b(a.kc, 0, kbyte0);
-        issue_group_b(P0{}, 0);
-        issue_group_b(P1{}, 1);
-        issue_group_b(P2{}, 2);
-        static_assert(RB == 4, "prologue written for four byte slots");
-        ring_barrier<(2 * kGroupLoads & 15) | (((2 * kGroupLoads) >> 4) << 14) | 0x0070>();
-        Dec::run(kbyte0, kslot0, tid);
-        Dec::run(kbyte1, kslot1, tid);
-        Dec::run(vbyte0, vslot0, tid);
-    }
+    issue_k(0, kslot0);
+    issue_v(0, vslot0);
+    issue_k(1, kslot1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     f16x scur[NSB];
     compute_s(kslot0, scur);
     raise_max(row_max(scur, tile_key0(0), true));
     __syncthreads();
-    if constexpr (DIRECT) {
+    {
         // groups 1 .. R-1 (SPREAD: 1 .. R-2; iteration 0 issues group R-1)
         constexpr int last = SPREAD ? R - 2 : R - 1;
         if constexpr (last >= 1) {
@@ -738,12 +726,6 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
             issue_k(4, kslot(P4{}));
             issue_v(3, vslot(P3{}));
         }
-    } else {
-        // groups -1 and 0 are decoded: issue groups 3 and 4 into their slots,
-        // then wait for group 1, which iteration 0 decodes
-        issue_group_b(P3{}, 3);
-        issue_group_b(P4{}, 4);
-        ring_barrier<((3 * kGroupLoads) & 15) | (((3 * kGroupLoads) >> 4) << 14) | 0x0070>();
     }
 
     // end of iteration it (phase p = it % R): wait for group it+1, then refill
@@ -754,26 +736,10 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         if constexpr (SPREAD) {
             (void)it;
             ring_barrier<kWaitGroups>();
-        } else if constexpr (DIRECT) {
+        } else {
             ring_barrier<kWaitGroups>();
             issue_k(it + R + 1, kslot(PN{}));
             issue_v(it + R, vslot(p));
-        } else {
-            // byte group it+2 must be in LDS for the next iteration
-            using PG = std::integral_constant<int, decltype(p)::value + 1 + RB>;
-            ring_barrier<kWaitGroups>();
-            issue_group_b(PG{}, it + RB + 1);
-        }
-    };
-
-    // E4M3: decode byte group it+1 (K(it+2), V(it+1)) into the FP16 slots
-    // that iteration it does not read
-    auto decode_next = [&](auto p) {
-        if constexpr (SRC == KV_E4M3_PAGED) {
-            using Q1 = std::integral_constant<int, decltype(p)::value + 1>;
-            using Q2 = std::integral_constant<int, decltype(p)::value + 2>;
-            Dec::run(kbslot(Q2{}), kslot(Q2{}), tid);
-            Dec::run(vbslot(Q1{}), vslot(Q1{}), tid);
         }
     };
 
@@ -813,13 +779,13 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         if constexpr (SPREAD) sg = spread_group(it);
 
         // V operands: the first PC are read in the last steps of block B
-        h8 vop[NC];
+        KRaw vop[NC];
         constexpr int PC = D == 256 ? 3 : 2;  // V operand reads in flight
 
         // ---- block B ----
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        h8 kop[NB];
-        auto kread = [&](int i) { return *(const h8*)(kt + koff_s[i % KK] + (i / KK) * 32 * ROW); };
+        KRaw kop[NB];
+        auto kread = [&](int i) { return kfetch(kt, i / KK, i % KK); };
         constexpr int PB = D == 256 ? 4 : 3;  // K operand reads in flight
 #pragma unroll
         for (int i = 0; i < PB; ++i) kop[i] = kread(i);
@@ -828,7 +794,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         for (int i = 0; i < NB; ++i) {
             if (i + PB < NB) kop[i + PB] = kread(i + PB);
             const int kb = i / KK, kk = i % KK;
-            sn[kb] = mma<BF>(kop[i], qf[kk], kk == 0 ? f16x{} : sn[kb]);
+            sn[kb] = mma<BF>(opuse(kop[i]), qf[kk], kk == 0 ? f16x{} : sn[kb]);
             if (i >= NB - PC) vop[i - (NB - PC)] = vread(vt, i - (NB - PC));
             if constexpr (SPREAD) {
                 if (i % (NB / NL) == 1) DL::issue_one(sg.k, dl.koff, kslot(p), wave, i / (NB / NL));
@@ -840,25 +806,6 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         }
 
         // ---- block C ----
-        // E4M3: the code chunks of byte group it+1 are read with the first V
-        // operands and decoded into the free FP16 slots between later MFMAs
-        using Q1 = std::integral_constant<int, decltype(p)::value + 1>;
-        using Q2 = std::integral_constant<int, decltype(p)::value + 2>;
-        constexpr int NDC = SRC == KV_E4M3_PAGED ? 2 * Dec::kChunks : 0;  // decode units
-        u4 braw[NDC > 0 ? NDC : 1];
-        auto dec_unit = [&](int u) {
-            if (u < Dec::kChunks)
-                Dec::store(kslot(Q2{}), braw[u], tid, u);
-            else
-                Dec::store(vslot(Q1{}), braw[u], tid, u - Dec::kChunks);
-        };
-        if constexpr (NDC > 0) {
-#pragma unroll
-            for (int i = 0; i < Dec::kChunks; ++i) {
-                braw[i] = Dec::read(kbslot(Q2{}), tid, i);
-                braw[Dec::kChunks + i] = Dec::read(vbslot(Q1{}), tid, i);
-            }
-        }
         __builtin_amdgcn_sched_barrier(0);
         float macc = -INFINITY, mpart = -INFINITY;
         constexpr int NMX = 8 * NSB;  // max3 units: two scores each
@@ -874,7 +821,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         for (int i = 0; i < NC; ++i) {
             if (i + PC < NC) vop[i + PC] = vread(vt, i + PC);
             const int kstep = i / DB, db = i % DB;
-            oacc[db] = mma<BF>(vop[i], pk[kstep], oacc[db]);
+            oacc[db] = mma<BF>(opuse(vop[i]), pk[kstep], oacc[db]);
             if constexpr (SPREAD) {
                 if (i % (NC / NL) == 1) DL::issue_one(sg.v, dl.voff, vslot(PV{}), wave, i / (NC / NL));
             }
@@ -887,13 +834,6 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
                 }
             }
             if (XCHG_EARLY && i == MX0 + MXS - 1) mpart = __shfl_xor(macc, 32);
-            // decode units, starting four MFMAs in
-            if constexpr (NDC > 0) {
-                if (i >= 4) {
-#pragma unroll
-                    for (int u = ((i - 4) * NDC) / (NC - 4); u < ((i - 3) * NDC) / (NC - 4); ++u) dec_unit(u);
-                }
-            }
             __builtin_amdgcn_sched_barrier(0);
         }
         raise_max((XCHG_EARLY ? fmaxf(macc, mpart) : wave_half_max(macc)) * a.c);
@@ -914,7 +854,6 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
                 DL::issue_one(sg.v, dl.voff, vslot(PV{}), wave, j);
             }
         }
-        decode_next(p);
         f16x sn[NSB];
 #pragma unroll
         for (int kb = 0; kb < NSB; ++kb) sn[kb] = f16x{};
