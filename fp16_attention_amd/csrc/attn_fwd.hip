@@ -8,7 +8,7 @@
 //     ("[Kernel][SM70] Integrate FP32 v37 prefill and exact E4M3 bridge",
 //     Implementation),
 //   - the same prefill reading K/V from a paged E4M3 cache, decoded exactly
-//     to FP16 inside the workgroup (same page, Purpose),
+//     to FP16 in registers as the MFMA operands (same page, Purpose),
 //   - block-sparse attention over per-query-block KV block lists with dense
 //     prefix query blocks ("[Video] Integrate H3 SM70 execution, metrics and
 //     VSA diagnostics", Purpose).
@@ -21,12 +21,13 @@
 //     HBM/L2 into LDS with buffer_load ... lds (no register staging; rows past
 //     the end of the key range read as zero through the buffer range check),
 //     R - 1 iterations ahead of their use (at D = 256 a group's loads are
-//     spread over the MFMA steps of the iteration that issues them). E4M3
-//     code tiles move into a separate LDS byte ring the same way; the
-//     workgroup decodes each exactly to FP16 into the FP16 slots.
-//     K and V are stored row-major with 16-byte chunks XOR-swizzled by the
-//     row, which keeps the K operand reads and the transposing V reads free of
-//     bank conflicts.
+//     spread over the MFMA steps of the iteration that issues them). Paged
+//     E4M3 code tiles (one 32-token page each) move into the ring the same
+//     way, half the bytes of FP16 tiles; each wave decodes the codes of every
+//     operand it reads exactly to FP16 in registers, right before the MFMA
+//     that consumes it. K and V are stored row-major with 16-byte chunks
+//     XOR-swizzled by the row, which keeps the K operand reads and the
+//     transposing V reads (16-bit or 8-bit) free of bank conflicts.
 //   - Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_f16: each lane owns one query (lane % 32) and 16
 //     keys per 32-key block, so the row max and row sum are in-lane work plus
