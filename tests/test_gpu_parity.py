@@ -108,10 +108,14 @@ def _paged_inputs(seed, Hkv, D, kv_len, pages, ks, vs):
     return k_codes, v_codes, table
 
 
-@pytest.mark.parametrize("ks,vs", [(1.0, 1.0), (0.0625, 0.03125), (0.0371, 0.0815)])
-def test_paged_e4m3_parity(lib, ks, vs):
-    Hq, Hkv, D, q_rows, q_real, kv_len, pages = 6, 1, 256, 128, 100, 2048, 80
-    say(f"paged e4m3 scales {ks} {vs}")
+@pytest.mark.parametrize("Hq,Hkv,D,q_rows,q_real,kv_len,pages,ks,vs", [
+    (6, 1, 256, 128, 100, 2048, 80, 1.0, 1.0),
+    (6, 1, 256, 128, 100, 2048, 80, 0.0625, 0.03125),
+    (6, 1, 256, 128, 100, 2048, 80, 0.0371, 0.0815),
+    (4, 2, 128, 192, 150, 1056, 40, 0.0371, 0.0815),   # D128 byte swizzle, two kv heads, a 32-key tail
+])
+def test_paged_e4m3_parity(lib, Hq, Hkv, D, q_rows, q_real, kv_len, pages, ks, vs):
+    say(f"paged e4m3 Hq{Hq} Hkv{Hkv} D{D} q{q_rows} real{q_real} kv{kv_len} scales {ks} {vs}")
     ks, vs = float(np.float32(ks)), float(np.float32(vs))
     q = synth.normal_f16(5, synth.TID_Q, (1, Hq, q_rows, D))
     kc, vc, table = _paged_inputs(5, Hkv, D, kv_len, pages, ks, vs)
