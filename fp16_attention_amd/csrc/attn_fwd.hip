@@ -271,7 +271,8 @@ struct ByteLoader {
 // 64 KB). Block lists (two 32-key tiles per selected block) use two slots:
 // their two-wave workgroups then take 32 KB, four per CU, which keeps two
 // waves on every SIMD. The paged E4M3 source streams through four byte slots
-// of 32-key pages (32 KB at D = 256), decoded in registers as operands.
+// of 32-key pages (32 KB at D = 256; two for decode), decoded in registers as
+// operands.
 // ---------------------------------------------------------------------------
 template <int D, int SRC, int MODE>
 struct Tiling {
@@ -281,7 +282,9 @@ struct Tiling {
     // fit the registers next to its FP32 output accumulators.
     static constexpr bool WIDE = D == 128 && MODE == KEYS_DENSE;
     static constexpr int KT = WIDE ? 64 : 32;
-    static constexpr int R = WIDE ? 2 : MODE != KEYS_BLOCKS ? 4 : 2;
+    // decode items stream only a few dozen tiles each: there the two-slot
+    // ring's shorter unrolled loop measured faster than four slots
+    static constexpr int R = WIDE ? 2 : (MODE != KEYS_BLOCKS && MODE != KEYS_DECODE) ? 4 : 2;
     static constexpr int PH = R;  // phases of the unrolled loop
 };
 
