@@ -138,8 +138,9 @@ int attn_fwd_prefix_causal(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, f
  * physical page of logical token t (t < kv_len). Entries must lie in
  * [0, num_phys_pages); an entry outside is clamped into range (no fault, the
  * result for that sequence is then unspecified).
- * The loader decodes each byte to FP16 exactly (every E4M3 value is an FP16
- * value); k_scale multiplies the scores and v_scale the output in FP32.
+ * Each code is decoded to FP16 exactly (every E4M3 value is an FP16 value)
+ * in registers, as the MFMA operand; k_scale multiplies the scores and
+ * v_scale the output in FP32.
  * Domain as attn_fwd_prefix_causal, plus page_size == 32,
  * table_stride >= kv_len / 32, num_phys_pages >= 1, finite scales > 0.
  */
