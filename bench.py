@@ -478,6 +478,10 @@ def main():
     if result is None:
         print(json.dumps({"metric": METRIC, "partial": True, "only": args.only, "extra": extra}), flush=True)
         return
+    # FP16 MFMA-bound workloads against the same measured (FP16) ceiling as the headline
+    for rec in extra.values():
+        if "tflops" in rec and "BF16" not in rec["workload"]:
+            rec["frac_of_measured_ceiling"] = rec["tflops"] / result["mfma_ceiling"]["value"]
     result["extra"] = extra
     result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                         "compute_units": props.multi_processor_count}
