@@ -354,8 +354,20 @@ def cpu_baseline(w, qkv, out_gpu, rows_per_head):
     cpu = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
            "sample": f"{len(rows)} query rows ({rows_per_head} per head, seeded) of the headline workload, "
                      f"each against all {w['Lkv']} keys, FP64; {dt:.2f} s wall",
-           "seconds": dt}
+           "seconds": dt, "host_cpus_online": os.cpu_count(), "cpu_model": _cpu_model()}
     return cpu, parity
+
+
+def _cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (empty if unavailable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
 
 
 # --------------------------------------------------------------------------------- main
