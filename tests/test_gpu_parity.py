@@ -20,7 +20,7 @@ def dev(x):
                                           (1, 2, 129, 65, 256),
                                           (1, 2, 200, 100, 128),     # one full 64-key tile, then a partial one
                                           (1, 1, 130, 321, 128),     # an odd count of full tiles, then one key
-                                          (1, 2, 600, 4100, 128),    # three 256-row query tiles, many key tiles
+                                          (1, 2, 600, 4100, 128),    # five query tiles, the last ragged; many key tiles
                                           (1, 1, 1, 1, 128)])        # single row, single key
 def test_dense_parity(lib, B, H, Lq, Lkv, D):
     say(f"dense B{B} H{H} Lq{Lq} Lkv{Lkv} D{D}")
@@ -241,7 +241,8 @@ def test_bridge_paged_layout_bit_exact(lib):
 
 
 @pytest.mark.parametrize("B,H,L,topk", [(1, 2, 4096, 8), (2, 1, 64 * 300, 64), (1, 1, 128, 2),
-                                         (1, 2, 64 * 20 + 37, 6), (1, 1, 50, 1)])  # partial last blocks
+                                         (1, 2, 64 * 20 + 37, 6), (1, 1, 50, 1),  # partial last blocks
+                                         (1, 1, 64 * 1000 + 17, 64)])  # 1001 blocks: 16 keys per lane in the top-k
 def test_vsa_select_bit_exact(lib, B, H, L, topk):
     say(f"vsa select B{B} H{H} L{L} k{topk}")
     q = synth.normal_f16(8, synth.TID_Q, (B, H, L, 128))
