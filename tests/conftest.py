@@ -23,7 +23,7 @@ def gpu_available() -> bool:
 
 @pytest.fixture(scope="session")
 def lib():
-    """The HIP library's Python binding; on a GPU machine it must load."""
+    """The HIP library's Python binding; wherever a GPU is present it must load."""
     import fp16_attention_amd as fa
     fa.load()
     return fa
