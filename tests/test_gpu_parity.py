@@ -310,3 +310,27 @@ def test_bitwise_repeatability_without_sync(lib):
         assert torch.equal(o, outs[0])
     for o in dens[1:]:
         assert torch.equal(o, dens[0])
+
+
+@pytest.mark.parametrize("decode,Hq,Hkv,D,q_rows,q_real,kv_len", [
+    (False, 4, 2, 128, 128, 100, 640),   # prefill, two sequences with their own page lists
+    (True, 6, 1, 256, 16, 16, 1056),     # decode, two sequences, a 32-key tail
+])
+def test_paged_two_sequences_parity(lib, decode, Hq, Hkv, D, q_rows, q_real, kv_len):
+    say(f"paged {'decode' if decode else 'prefill'} B2 Hq{Hq} Hkv{Hkv} D{D} q{q_rows} real{q_real} kv{kv_len}")
+    B, ks, vs = 2, float(np.float32(0.0371)), float(np.float32(0.0815))
+    per = kv_len // 32
+    pages = 2 * per + 7
+    q = synth.normal_f16(13, synth.TID_Q, (B, Hq, q_rows, D))
+    kc = synth.e4m3_codes(13, synth.TID_K, (pages, 32, Hkv, D), ks)
+    vc = synth.e4m3_codes(13, synth.TID_V, (pages, 32, Hkv, D), vs)
+    perm = synth.permutation(13, synth.TID_TABLE, pages)
+    table = np.stack([perm[:per], perm[per:2 * per]]).astype(np.int32)
+    fn = lib.attn_fwd_paged_e4m3_decode if decode else lib.attn_fwd_paged_e4m3
+    scale = lib.default_scale(D)
+    out = fn(dev(q), dev(kc), dev(vc), dev(table), kv_len, q_real, ks, vs, scale=scale)
+    torch.cuda.synchronize()
+    kf = oracle.e4m3_to_f16(oracle.paged_gather(kc, table, kv_len), ks).view(np.float16)
+    vf = oracle.e4m3_to_f16(oracle.paged_gather(vc, table, kv_len), vs).view(np.float16)
+    ref, _ = oracle.attention(q, kf, vf, scale, mode=oracle.MODE_CAUSAL, offset=kv_len - q_real)
+    assert_close(out.cpu().numpy().reshape(-1, D), ref, "O")
