@@ -281,11 +281,12 @@ def test_vsa_select_ties_take_lower_index(lib):
     assert np.array_equal(idx.cpu().numpy()[0, 0], np.broadcast_to(np.arange(5), (40, 5)))
 
 
-@pytest.mark.parametrize("L,topk,dp", [(2048, 8, 2), (64 * 20, 20, 0), (1024, 3, 16),
-                                       (64 * 30 + 37, 7, 2), (64 * 6 + 1, 7, 7)])  # partial last blocks
-def test_vsa_sparse_attn_parity(lib, L, topk, dp):
-    say(f"vsa sparse L{L} k{topk} dp{dp}")
-    B, H, D = 1, 2, 128
+@pytest.mark.parametrize("B,H,L,topk,dp", [(1, 2, 2048, 8, 2), (1, 2, 64 * 20, 20, 0), (1, 2, 1024, 3, 16),
+                                           (1, 2, 64 * 30 + 37, 7, 2), (1, 2, 64 * 6 + 1, 7, 7),  # partial last blocks
+                                           (2, 3, 64 * 12 + 5, 5, 1)])  # two batches, three heads
+def test_vsa_sparse_attn_parity(lib, B, H, L, topk, dp):
+    say(f"vsa sparse B{B} H{H} L{L} k{topk} dp{dp}")
+    D = 128
     q, k, v = qkv(10, B, H, H, L, L, D)
     ref_idx, _ = oracle.vsa_select(q, k, 64, topk)
     scale = lib.default_scale(D)
