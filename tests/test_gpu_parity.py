@@ -64,19 +64,20 @@ def test_dense_strided_views(lib):
     assert_close(out_store.transpose(1, 2).cpu().numpy().reshape(-1, D), ref, "O strided")
 
 
-@pytest.mark.parametrize("Hq,Hkv,D,q_rows,q_real,kv_len", [
-    (6, 1, 256, 256, 200, 4096),   # split over the key range, padded rows
-    (6, 1, 256, 128, 128, 160),    # one segment, KV tail not a multiple of 64
-    (4, 2, 128, 192, 150, 2400),   # GQA groups of 2, D128
-    (2, 1, 256, 64, 64, 16480),    # 16 segments of 17 units, the last 3 units with a 32-key tail
-    (3, 1, 128, 64, 40, 9024),     # 9 segments at D128, padded rows
+@pytest.mark.parametrize("B,Hq,Hkv,D,q_rows,q_real,kv_len", [
+    (1, 6, 1, 256, 256, 200, 4096),   # split over the key range, padded rows
+    (1, 6, 1, 256, 128, 128, 160),    # one segment, KV tail not a multiple of 64
+    (1, 4, 2, 128, 192, 150, 2400),   # GQA groups of 2, D128
+    (1, 2, 1, 256, 64, 64, 16480),    # 16 segments of 17 units, the last 3 units with a 32-key tail
+    (1, 3, 1, 128, 64, 40, 9024),     # 9 segments at D128, padded rows
+    (2, 4, 2, 256, 128, 90, 3072),    # two batches: their items and merges side by side
 ])
-def test_prefix_causal_parity(lib, Hq, Hkv, D, q_rows, q_real, kv_len):
-    say(f"causal Hq{Hq} Hkv{Hkv} D{D} rows{q_rows} real{q_real} kv{kv_len} "
-        f"ws={lib.prefix_causal_workspace(1, Hq, Hkv, D, q_rows, kv_len)}")
-    q, k, v = qkv(3, 1, Hq, Hkv, q_rows, kv_len, D)
+def test_prefix_causal_parity(lib, B, Hq, Hkv, D, q_rows, q_real, kv_len):
+    say(f"causal B{B} Hq{Hq} Hkv{Hkv} D{D} rows{q_rows} real{q_real} kv{kv_len} "
+        f"ws={lib.prefix_causal_workspace(B, Hq, Hkv, D, q_rows, kv_len)}")
+    q, k, v = qkv(3, B, Hq, Hkv, q_rows, kv_len, D)
     scale = lib.default_scale(D)
-    lse = torch.empty((1, Hq, q_rows), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, q_rows), dtype=torch.float32, device="cuda")
     out = lib.attn_fwd_prefix_causal(dev(q), dev(k), dev(v), q_real, lse=lse, scale=scale)
     torch.cuda.synchronize()
     ref, ref_lse = oracle.attention(q, k, v, scale, mode=oracle.MODE_CAUSAL, offset=kv_len - q_real)
