@@ -319,14 +319,16 @@ def bench_vsa(fa, torch, iters, timer, flush):
 # -------------------------------------------------------------------------- CPU oracle
 
 def bench_mfma_ceiling(fa, torch, timer, iters=16384, launches=5):
-    """FP16 MFMA rate the chip sustains on varied operands (fa_mfma_ceiling):
-    the attainable matrix throughput beside the published peak."""
-    out = torch.empty(fa.MFMA_CEILING_OUT, dtype=torch.float32, device="cuda")
-    ms, _ = timer.run(lambda: fa.mfma_ceiling(out, iters), launches, 2)
-    tf = fa.mfma_ceiling_flop(iters) / (np.median(ms) * 1e-3) / 1e12
+    """FP16 MFMA rate the chip sustains on varied operands (fa_mfma_ceiling, a
+    measurement aid in its own library): the attainable matrix throughput
+    beside the published peak."""
+    from fp16_attention_amd import measure
+    out = torch.empty(measure.MFMA_CEILING_OUT, dtype=torch.float32, device="cuda")
+    ms, _ = timer.run(lambda: measure.mfma_ceiling(out, iters), launches, 2)
+    tf = measure.mfma_ceiling_flop(iters) / (np.median(ms) * 1e-3) / 1e12
     log(f"MFMA ceiling (varied FP16 operands): {np.median(ms):.3f} ms, {tf:.0f} TFLOP/s")
     return {"value": tf, "unit": "TFLOP/s", "kind": "fa_mfma_ceiling: FP16 MFMAs only, operands varied per lane",
-            "flop_per_launch": fa.mfma_ceiling_flop(iters), **stats(ms)}
+            "flop_per_launch": measure.mfma_ceiling_flop(iters), **stats(ms)}
 
 
 def cpu_baseline(w, qkv, out_gpu, rows_per_head):

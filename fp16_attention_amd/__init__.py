@@ -26,7 +26,7 @@ EXPORTS = ("fa_abi_version", "fa_error_string", "attn_fwd_dense", "attn_fwd_dens
            "attn_fwd_paged_e4m3_decode_workspace", "attn_fwd_paged_e4m3_decode",
            "kv_e4m3_paged_to_fp16", "kv_prefix_fp8_gather", "vsa_topk_for_sparsity", "vsa_block_select_workspace",
            "vsa_block_select",
-           "vsa_block_sparse_attn_workspace", "vsa_block_sparse_attn", "fa_mfma_ceiling")
+           "vsa_block_sparse_attn_workspace", "vsa_block_sparse_attn")
 
 
 class FaTensor(ctypes.Structure):
@@ -62,7 +62,6 @@ _SIGS = {
     "vsa_block_select": (_i, [_vp, _vp] + [_i] * 6 + [_vp, _vp, _vp, _sz, _vp]),
     "vsa_block_sparse_attn_workspace": (_sz, [_i] * 7),
     "vsa_block_sparse_attn": (_i, [FaTensor] * 4 + [_vp, _vp] + [_i] * 7 + [_f, _vp, _sz, _vp]),
-    "fa_mfma_ceiling": (_i, [_i, _vp, _vp]),
 }
 
 
@@ -110,9 +109,44 @@ def _stream(t):
 
 
 def _need_cuda(*ts):
+    """Every given tensor is a CUDA (HIP) tensor on the device of the first."""
+    dev = None
     for t in ts:
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ValueError("fp16_attention_amd operates on CUDA (HIP) tensors only")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors of a call must be on the same device")
+
+
+def _dtype_name(t):
+    return str(t.dtype).replace("torch.", "")
+
+
+def _want(t, name, dtypes, ndim=None, shape=None, contiguous=False, unit_d=False):
+    """Check a tensor's dtype, rank, exact shape, contiguity and (for BHSD views)
+    the unit stride along D, before anything is handed to the library."""
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d).replace('torch.', '') for d in dtypes)}, "
+                         f"not {_dtype_name(t)}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, not {t.dim()}-D")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if unit_d and t.stride(-1) != 1 and t.size(-1) > 1:
+        raise ValueError(f"{name}: the D dimension must have stride 1")
+
+
+def _lse_shape_ok(lse, shape):
+    import torch
+    _want(lse, "lse", (torch.float32,), shape=shape, contiguous=True)
 
 
 def default_scale(D: int) -> float:
@@ -122,21 +156,34 @@ def default_scale(D: int) -> float:
 
 
 # --------------------------------------------------------------------------- attention
+#
+# Every wrapper checks dtypes, shapes, contiguity and devices of all its
+# tensors (outputs, LSE and workspaces included) before the library sees a
+# pointer: the C side gets bare device pointers and cannot check them itself.
+
+def _f16():
+    import torch
+    return (torch.float16,)
+
 
 def attn_fwd_dense(q, k, v, out=None, lse=None, scale=None):
     """Dense non-causal attention. q [B,H,Lq,D], k/v [B,H,Lkv,D] FP16 or BF16 -> out of the same type.
-    BF16 operands go to attn_fwd_dense_bf16."""
+    BF16 operands go to attn_fwd_dense_bf16. lse: optional float32 [B,H,Lq] contiguous."""
     import torch
-    _need_cuda(q, k, v, out, lse)
     dt = q.dtype
-    if dt not in (torch.float16, torch.bfloat16) or k.dtype != dt or v.dtype != dt:
-        raise ValueError("q, k, v must all be float16 or all bfloat16")
+    if dt not in (torch.float16, torch.bfloat16):
+        raise ValueError("q must be float16 or bfloat16")
+    _want(q, "q", (dt,), ndim=4, unit_d=True)
     B, H, Lq, D = q.shape
+    _want(k, "k", (dt,), ndim=4, unit_d=True)
     Lkv = k.shape[2]
+    _want(k, "k", (dt,), shape=(B, H, Lkv, D))
+    _want(v, "v", (dt,), shape=(B, H, Lkv, D), unit_d=True)
+    _want(out, "out", (dt,), shape=(B, H, Lq, D), unit_d=True)
+    _lse_shape_ok(lse, (B, H, Lq))
+    _need_cuda(q, k, v, out, lse)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
-    elif out.dtype != dt:
-        raise ValueError("out must have the dtype of q")
     scale = default_scale(D) if scale is None else scale
     fn = load().attn_fwd_dense_bf16 if dt == torch.bfloat16 else load().attn_fwd_dense
     _check(fn(_view(q), _view(k), _view(v), _view(out), _ptr(lse), B, H, Lq, Lkv, D, scale, _stream(q)))
@@ -148,33 +195,51 @@ def prefix_causal_workspace(B, Hq, Hkv, D, q_rows, kv_len) -> int:
 
 
 def _workspace(nbytes, device, workspace):
+    """The caller's workspace (a CUDA uint8 tensor of at least nbytes on the
+    call's device), or a fresh one; None when nothing is needed."""
     import torch
     if nbytes == 0:
         return workspace
-    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _want(workspace, "workspace", (torch.uint8,), contiguous=True)
+    if not workspace.is_cuda or workspace.device != device:
+        raise ValueError("workspace must be a CUDA tensor on the device of the operands")
+    if workspace.numel() < nbytes:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, {nbytes} needed")
     return workspace
 
 
+def _nbytes(ws):
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
 def attn_fwd_prefix_causal(q, k, v, q_real, out=None, lse=None, scale=None, workspace=None):
-    """Causal prefill against a prefix KV (GQA). q [B,Hq,q_rows,D], k/v [B,Hkv,kv_len,D]."""
+    """Causal prefill against a prefix KV (GQA). q [B,Hq,q_rows,D], k/v [B,Hkv,kv_len,D] FP16;
+    lse: optional float32 [B,Hq,q_rows] contiguous."""
     import torch
-    _need_cuda(q, k, v, out, lse)
+    _want(q, "q", _f16(), ndim=4, unit_d=True)
     B, Hq, q_rows, D = q.shape
+    _want(k, "k", _f16(), ndim=4, unit_d=True)
     Hkv, kv_len = k.shape[1], k.shape[2]
+    _want(k, "k", _f16(), shape=(B, Hkv, kv_len, D))
+    _want(v, "v", _f16(), shape=(B, Hkv, kv_len, D), unit_d=True)
+    _want(out, "out", _f16(), shape=(B, Hq, q_rows, D), unit_d=True)
+    _lse_shape_ok(lse, (B, Hq, q_rows))
+    _need_cuda(q, k, v, out, lse)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     scale = default_scale(D) if scale is None else scale
     ws = _workspace(prefix_causal_workspace(B, Hq, Hkv, D, q_rows, kv_len), q.device, workspace)
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().attn_fwd_prefix_causal(_view(q), _view(k), _view(v), _view(out), _ptr(lse), B, Hq, Hkv,
-                                         D, q_rows, q_real, kv_len, scale, _ptr(ws), nbytes, _stream(q)))
+                                         D, q_rows, q_real, kv_len, scale, _ptr(ws), _nbytes(ws), _stream(q)))
     return out
 
 
 def attn_fwd_paged_e4m3(q, k_cache, v_cache, page_table, kv_len, q_real, k_scale=1.0, v_scale=1.0,
                         out=None, lse=None, scale=None, workspace=None):
-    """Causal prefill reading an E4M3 paged cache [pages, 32, Hkv, D] (uint8) via an int32 page table."""
+    """Causal prefill reading an E4M3 paged cache [pages, 32, Hkv, D] (uint8) via an int32 page table
+    [B, pages_per_seq]."""
     return _paged(False, q, k_cache, v_cache, page_table, kv_len, q_real, k_scale, v_scale, out, lse, scale,
                   workspace)
 
@@ -189,14 +254,19 @@ def attn_fwd_paged_e4m3_decode(q, k_cache, v_cache, page_table, kv_len, q_real=N
 
 def _paged(decode, q, k_cache, v_cache, page_table, kv_len, q_real, k_scale, v_scale, out, lse, scale, workspace):
     import torch
-    _need_cuda(q, k_cache, v_cache, page_table, out, lse)
+    _want(q, "q", _f16(), ndim=4, unit_d=True)
     B, Hq, q_rows, D = q.shape
+    _want(k_cache, "k_cache", (torch.uint8,), ndim=4, contiguous=True)
     pages, page_size, Hkv, Dc = k_cache.shape
-    if Dc != D or tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise ValueError("cache shape mismatch")
-    for t in (k_cache, v_cache, page_table):
-        if not t.is_contiguous():
-            raise ValueError("caches and the page table must be contiguous")
+    if Dc != D:
+        raise ValueError("the caches' D differs from q's")
+    _want(v_cache, "v_cache", (torch.uint8,), shape=k_cache.shape, contiguous=True)
+    _want(page_table, "page_table", (torch.int32,), ndim=2, contiguous=True)
+    if page_table.shape[0] != B:
+        raise ValueError("page_table must have one row per sequence")
+    _want(out, "out", _f16(), shape=(B, Hq, q_rows, D), unit_d=True)
+    _lse_shape_ok(lse, (B, Hq, q_rows))
+    _need_cuda(q, k_cache, v_cache, page_table, out, lse)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     scale = default_scale(D) if scale is None else scale
@@ -204,10 +274,9 @@ def _paged(decode, q, k_cache, v_cache, page_table, kv_len, q_real, k_scale, v_s
     wsq = lib.attn_fwd_paged_e4m3_decode_workspace if decode else lib.attn_fwd_paged_e4m3_workspace
     fn = lib.attn_fwd_paged_e4m3_decode if decode else lib.attn_fwd_paged_e4m3
     ws = _workspace(int(wsq(B, Hq, Hkv, D, q_rows, kv_len)), q.device, workspace)
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(fn(_view(q), k_cache.data_ptr(), v_cache.data_ptr(), page_table.data_ptr(), page_table.stride(0),
               pages, page_size, k_scale, v_scale, _view(out), _ptr(lse), B, Hq, Hkv, D, q_rows, q_real, kv_len,
-              scale, _ptr(ws), nbytes, _stream(q)))
+              scale, _ptr(ws), _nbytes(ws), _stream(q)))
     return out
 
 
@@ -215,16 +284,20 @@ def kv_e4m3_paged_to_fp16(k_cache, v_cache, page_table, B, kv_len, k_scale=1.0, 
                           k_out=None, v_out=None):
     """Exact paged E4M3 -> FP16 bridge. Returns contiguous FP16 (k, v) [B, Hkv, kv_len, D]."""
     import torch
-    _need_cuda(k_cache, v_cache, page_table, k_out, v_out)
+    _want(k_cache, "k_cache", (torch.uint8,), ndim=4, contiguous=True)
     pages, page_size, Hkv, D = k_cache.shape
+    _want(v_cache, "v_cache", (torch.uint8,), shape=k_cache.shape, contiguous=True)
+    _want(page_table, "page_table", (torch.int32,), ndim=2, contiguous=True)
+    if page_table.shape[0] != B:
+        raise ValueError("page_table must have one row per sequence")
     shape = (B, Hkv, kv_len, D)
+    _want(k_out, "k_out", _f16(), shape=shape, contiguous=True)
+    _want(v_out, "v_out", _f16(), shape=shape, contiguous=True)
+    _need_cuda(k_cache, v_cache, page_table, k_out, v_out)
     if k_out is None:
         k_out = torch.empty(shape, dtype=torch.float16, device=k_cache.device)
     if v_out is None:
         v_out = torch.empty(shape, dtype=torch.float16, device=k_cache.device)
-    for t in (k_cache, v_cache, page_table, k_out, v_out):
-        if not t.is_contiguous():
-            raise ValueError("bridge operands must be contiguous")
     _check(load().kv_e4m3_paged_to_fp16(k_cache.data_ptr(), v_cache.data_ptr(), page_table.data_ptr(),
                                         page_table.stride(0), pages, page_size, B, Hkv, D, kv_len, k_scale,
                                         v_scale, k_out.data_ptr(), v_out.data_ptr(), _stream(k_cache)))
@@ -237,13 +310,14 @@ def kv_prefix_fp8_gather(k, v, index, k_out=None, v_out=None):
     """FP8 round trip of K per (row, head) with the row gather. k, v: bfloat16 [B, N, H, 128]
     contiguous; index: int32 [rows]. Returns (k_out, v_out) bfloat16 [B, rows, H, 128]."""
     import torch
-    _need_cuda(k, v, index, k_out, v_out)
-    if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16 or not k.is_contiguous() or not v.is_contiguous():
-        raise ValueError("k and v must be contiguous bfloat16 [B, N, H, D]")
-    if index.dtype != torch.int32 or not index.is_contiguous():
-        raise ValueError("index must be contiguous int32")
+    _want(k, "k", (torch.bfloat16,), ndim=4, contiguous=True)
     B, N, H, D = k.shape
+    _want(v, "v", (torch.bfloat16,), shape=k.shape, contiguous=True)
+    _want(index, "index", (torch.int32,), ndim=1, contiguous=True)
     rows = index.numel()
+    _want(k_out, "k_out", (torch.bfloat16,), shape=(B, rows, H, D), contiguous=True)
+    _want(v_out, "v_out", (torch.bfloat16,), shape=(B, rows, H, D), contiguous=True)
+    _need_cuda(k, v, index, k_out, v_out)
     if k_out is None:
         k_out = torch.empty((B, rows, H, D), dtype=torch.bfloat16, device=k.device)
     if v_out is None:
@@ -262,23 +336,22 @@ def vsa_topk_for_sparsity(L: int, sparsity: float, block: int = 64) -> int:
 
 
 def vsa_block_select(q, k, topk, block=64, scores=False, workspace=None, out=None):
-    """Top-k KV blocks per query block. Returns idx int32 [B,H,NB,topk] (and FP64 scores if asked)."""
+    """Top-k KV blocks per query block. q, k: FP16 [B,H,L,D] contiguous. Returns idx int32
+    [B,H,NB,topk] (and FP64 scores [B,H,NB,NB] if asked)."""
     import torch
-    _need_cuda(q, k, out)
-    if not (q.is_contiguous() and k.is_contiguous()):
-        raise ValueError("q and k must be contiguous")
+    _want(q, "q", _f16(), ndim=4, contiguous=True)
     B, H, L, D = q.shape
+    _want(k, "k", _f16(), shape=q.shape, contiguous=True)
     NB = (L + block - 1) // block  # the last block may be partial
+    _want(out, "out", (torch.int32,), shape=(B, H, NB, topk), contiguous=True)
+    _need_cuda(q, k, out)
     idx = out
     if idx is None:
         idx = torch.empty((B, H, NB, topk), dtype=torch.int32, device=q.device)
-    elif tuple(idx.shape) != (B, H, NB, topk) or idx.dtype != torch.int32 or not idx.is_contiguous():
-        raise ValueError("out must be a contiguous int32 [B, H, L/block, topk] tensor")
     s = torch.empty((B, H, NB, NB), dtype=torch.float64, device=q.device) if scores else None
     ws = _workspace(int(load().vsa_block_select_workspace(B, H, L, D, block)), q.device, workspace)
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().vsa_block_select(q.data_ptr(), k.data_ptr(), B, H, L, D, block, topk, idx.data_ptr(),
-                                   _ptr(s), _ptr(ws), nbytes, _stream(q)))
+                                   _ptr(s), _ptr(ws), _nbytes(ws), _stream(q)))
     return (idx, s) if scores else idx
 
 
@@ -288,39 +361,26 @@ def vsa_block_sparse_attn_workspace(B, H, L, D, block, topk, dense_prefix_qblock
 
 def vsa_block_sparse_attn(q, k, v, idx, dense_prefix_qblocks=2, block=64, out=None, lse=None, scale=None,
                           workspace=None):
-    """Block-sparse attention over per-query-block KV block lists idx [B,H,L/block,topk]."""
+    """Block-sparse attention over per-query-block KV block lists idx [B,H,ceil(L/block),topk] (int32,
+    contiguous). q, k, v, out: FP16 [B,H,L,D] views; lse: optional float32 [B,H,L] contiguous."""
     import torch
-    _need_cuda(q, k, v, idx, out, lse)
+    _want(q, "q", _f16(), ndim=4, unit_d=True)
     B, H, L, D = q.shape
-    if not idx.is_contiguous() or idx.dtype != torch.int32:
-        raise ValueError("idx must be contiguous int32")
+    _want(k, "k", _f16(), shape=q.shape, unit_d=True)
+    _want(v, "v", _f16(), shape=q.shape, unit_d=True)
+    _want(idx, "idx", (torch.int32,), ndim=4, contiguous=True)
+    NB = (L + block - 1) // block
     topk = idx.shape[-1]
+    _want(idx, "idx", (torch.int32,), shape=(B, H, NB, topk))
+    _want(out, "out", _f16(), shape=q.shape, unit_d=True)
+    _lse_shape_ok(lse, (B, H, L))
+    _need_cuda(q, k, v, idx, out, lse)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     scale = default_scale(D) if scale is None else scale
     ws = _workspace(vsa_block_sparse_attn_workspace(B, H, L, D, block, topk, dense_prefix_qblocks), q.device,
                     workspace)
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().vsa_block_sparse_attn(_view(q), _view(k), _view(v), _view(out), idx.data_ptr(), _ptr(lse),
-                                        B, H, L, D, block, topk, dense_prefix_qblocks, scale, _ptr(ws), nbytes,
-                                        _stream(q)))
-    return out
-
-
-MFMA_CEILING_OUT = 512 * 256  # FP32 values fa_mfma_ceiling writes
-
-
-def mfma_ceiling_flop(iters: int) -> float:
-    """FLOP of one fa_mfma_ceiling launch."""
-    return 512.0 * 4 * iters * 4 * 32768
-
-
-def mfma_ceiling(out, iters: int):
-    """Launch the FP16 MFMA rate kernel (a measurement aid) on out's stream;
-    out: CUDA float32 tensor of at least MFMA_CEILING_OUT elements."""
-    _need_cuda(out)
-    import torch
-    if out.dtype != torch.float32 or out.numel() < MFMA_CEILING_OUT or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 tensor of MFMA_CEILING_OUT elements")
-    _check(load().fa_mfma_ceiling(int(iters), out.data_ptr(), _stream(out)))
+                                        B, H, L, D, block, topk, dense_prefix_qblocks, scale, _ptr(ws),
+                                        _nbytes(ws), _stream(q)))
     return out

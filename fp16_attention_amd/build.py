@@ -13,8 +13,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa16attn.so")
-SOURCES = ["abi.cpp", "attn_fwd.hip", "e4m3_bridge.hip", "mfma_ceiling.hip", "prefix_fp8.hip",
-           "vsa_select.hip"]
+SOURCES = ["abi.cpp", "attn_fwd.hip", "e4m3_bridge.hip", "prefix_fp8.hip", "vsa_select.hip"]
+# The measurement aid (FP16 MFMA ceiling) is a library of its own, so that the
+# attention library exports only the method's entry points.
+MEASURE_CSRC = os.path.join(HERE, "measure_csrc")
+MEASURE_SOURCES = ["mfma_ceiling.hip"]
+MEASURE_LIB = os.path.join(HERE, "libfa16measure.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming packed FP32 VALU ops.
@@ -28,16 +32,11 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I", os.path.join(ROOT, "include")]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link the shared library; returns its path."""
-    objs = []
-    bdir = os.path.join(ROOT, "_build")
-    os.makedirs(bdir, exist_ok=True)
-    procs = []
-    for src in SOURCES:
+def _compile(sources, csrc, bdir, verbose):
+    objs, procs = [], []
+    for src in sources:
         obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
-        lang = ["-x", "hip"]
-        cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(csrc, src), "-o", obj]
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         objs.append(obj)
     failed = False
@@ -51,9 +50,24 @@ def build(verbose: bool = False) -> str:
             sys.stderr.write(out + "\n")
     if failed:
         raise RuntimeError("hipcc failed")
-    tmp = LIB + ".tmp%d" % os.getpid()
+    return objs
+
+
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link the attention library and the
+    measurement library; returns the attention library's path."""
+    bdir = os.path.join(ROOT, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    _link(_compile(SOURCES, CSRC, bdir, verbose), LIB)
+    mdir = os.path.join(bdir, "measure")
+    os.makedirs(mdir, exist_ok=True)
+    _link(_compile(MEASURE_SOURCES, MEASURE_CSRC, mdir, verbose), MEASURE_LIB)
     return LIB
 
 

@@ -1,7 +1,8 @@
 // FP8 round trip of prefix keys with the valid-row gather ("[perf] FastH3
 // two-Spark: gather packed FP4 inputs before head projections",
-// prefix_quant.py: quantize_gather_prefix_kv, and the PREFIX_FP8 path of
-// qknorm_rope.py). For every (b, r, h), with x the FP32 values of K's token
+// prefix_quant.py: quantize_gather_prefix_kv; key_quant.py applies the same
+// key round trip in its prefix preparation). For every (b, r, h), with x the
+// FP32 values of K's token
 // index[r], head h (D = 128, bfloat16):
 //   scale = max |x| / 448, inv = scale == 0 ? 0 : 1 / scale,
 //   k_out = RNE_bf16( decode( RNE_e4m3( clamp(x * inv, +-448) ) ) * scale ),

@@ -11,7 +11,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "fa16attn.h"
+#include "fa16measure.h"
 
 namespace {
 
@@ -59,9 +59,9 @@ __global__ __launch_bounds__(kThreads) void mfma_ceiling_kernel(float* out, int 
 
 extern "C" int fa_mfma_ceiling(int iters, float* out, void* stream)
 {
-    if (!out) return FA_ERR_NULL;
-    if (iters < 1 || iters > (1 << 20)) return FA_ERR_SHAPE;
+    if (!out) return FAM_ERR_NULL;
+    if (iters < 1 || iters > (1 << 20)) return FAM_ERR_SHAPE;
     hipLaunchKernelGGL(mfma_ceiling_kernel, dim3(kBlocks), dim3(kThreads), 0, (hipStream_t)stream, out, iters);
     const hipError_t e = hipGetLastError();
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP + (int)e;
+    return e == hipSuccess ? FAM_OK : FAM_ERR_HIP + (int)e;
 }

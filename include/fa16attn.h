@@ -193,8 +193,8 @@ int kv_e4m3_paged_to_fp16(const uint8_t* k_cache, const uint8_t* v_cache, const 
 
 /*
  * FP8 round trip of prefix keys with the valid-row gather ([P5]
- * prefix_quant.py, quantize_gather_prefix_kv; qknorm_rope.py, the PREFIX_FP8
- * path). k, v: bfloat16 [B, N, H, D] contiguous; index: int32 [rows], the
+ * prefix_quant.py, quantize_gather_prefix_kv; key_quant.py applies the same
+ * key round trip in its prefix preparation). k, v: bfloat16 [B, N, H, D] contiguous; index: int32 [rows], the
  * source token of each output row (clamped into [0, N)). For every (b, r, h),
  * with x the FP32 values of k[b, index[r], h, :]:
  *   scale = max |x| / 448, inv = (scale == 0 ? 0 : 1 / scale),
@@ -261,17 +261,6 @@ int vsa_block_sparse_attn(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, co
                           int dense_prefix_qblocks, float scale, void* workspace,
                           size_t workspace_bytes, void* stream);
 
-/*
- * Measurement aid, not part of the attention method: one launch of a kernel
- * that issues only FP16 MFMAs (v_mfma_f32_32x32x16_f16) on operands that
- * vary from lane to lane, 512 workgroups of 256 threads (two per CU), each
- * wave running iters x 4 MFMAs, i.e. 512 * 4 * iters * 4 * 32768 FLOP. Its
- * rate is the FP16 matrix throughput the chip sustains on varied data, which
- * the benchmark reports beside the published peak.
- * out: device FP32 [512 * 256] (one value per thread, caller-owned).
- * Domain: 1 <= iters <= 2^20.
- */
-int fa_mfma_ceiling(int iters, float* out, void* stream);
 
 #ifdef __cplusplus
 }

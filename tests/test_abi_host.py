@@ -14,13 +14,14 @@ import fp16_attention_amd as fa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa16attn.h")
+MEASURE_HEADER = os.path.join(ROOT, "include", "fa16measure.h")
 
 # fake, 256-byte aligned, distinct host addresses: only ever validated, never dereferenced
 A, B_, C, O, L, W = (0x10000000 * (i + 1) for i in range(6))
 
 
-def _declared():
-    with open(HEADER) as f:
+def _declared(header=HEADER):
+    with open(header) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return set(re.findall(r"\b([a-z_0-9]+)\s*\([^;{]*\)\s*;", text)) - {"if", "while"}
@@ -36,6 +37,19 @@ def test_header_declarations_are_all_exported():
     for name in declared:
         assert hasattr(lib, name)
     assert lib.fa_abi_version() == 1
+
+
+def test_measurement_library_is_separate():
+    """The measurement aid has a header and library of its own; the attention
+    library neither declares nor exports it."""
+    from fp16_attention_amd import measure
+    declared = _declared(MEASURE_HEADER)
+    assert declared == set(measure.EXPORTS)
+    out = subprocess.check_output(["nm", "-D", "--defined-only", measure.LIB_PATH]).decode()
+    assert declared <= {line.split()[-1] for line in out.splitlines()}
+    attn = subprocess.check_output(["nm", "-D", "--defined-only", fa.LIB_PATH]).decode()
+    assert "fa_mfma_ceiling" not in attn
+    assert not (declared & _declared())
 
 
 def test_library_has_no_undefined_kernel_stubs():
@@ -259,9 +273,74 @@ def test_vsa_keep_ratio():
 
 
 def test_mfma_ceiling_rejections():
-    lib = fa.load()
-    assert lib.fa_mfma_ceiling(16, None, None) == fa.FA_ERR_NULL
+    from fp16_attention_amd import measure
+    lib = measure.load()
+    assert lib.fa_mfma_ceiling(16, None, None) == measure.FAM_ERR_NULL
     # the pointer is never dereferenced on the host, and no launch happens
-    assert lib.fa_mfma_ceiling(0, 256, None) == fa.FA_ERR_SHAPE
-    assert lib.fa_mfma_ceiling((1 << 20) + 1, 256, None) == fa.FA_ERR_SHAPE
-    assert fa.mfma_ceiling_flop(1000) == 512.0 * 4 * 1000 * 4 * 32768
+    assert lib.fa_mfma_ceiling(0, 256, None) == measure.FAM_ERR_SHAPE
+    assert lib.fa_mfma_ceiling((1 << 20) + 1, 256, None) == measure.FAM_ERR_SHAPE
+    assert measure.mfma_ceiling_flop(1000) == 512.0 * 4 * 1000 * 4 * 32768
+
+
+def test_binding_validates_every_tensor_before_the_library():
+    """The C side receives bare pointers and cannot check dtypes or extents, so
+    the binding rejects bad outputs, LSE buffers, operands and workspaces first
+    (CPU tensors here: every check runs before the device check and before any
+    library call)."""
+    import torch
+    h, f32, bf = torch.float16, torch.float32, torch.bfloat16
+    q = torch.zeros(1, 2, 64, 128, dtype=h)
+    k = torch.zeros(1, 2, 96, 128, dtype=h)
+
+    def rejects(fn, match):
+        with pytest.raises(ValueError, match=match):
+            fn()
+
+    d = fa.attn_fwd_dense
+    rejects(lambda: d(q, k, k, lse=torch.zeros(1, 2, 64, dtype=h)), "lse must be float32")
+    rejects(lambda: d(q, k, k, lse=torch.zeros(1, 2, 63, dtype=f32)), "lse must have shape")
+    rejects(lambda: d(q, k, k, lse=torch.zeros(1, 2, 128, dtype=f32)[..., ::2]), "lse must be contiguous")
+    rejects(lambda: d(q, k, k, out=torch.zeros(1, 2, 64, 128, dtype=bf)), "out must be float16")
+    rejects(lambda: d(q, k, k, out=torch.zeros(1, 2, 32, 128, dtype=h)), "out must have shape")
+    rejects(lambda: d(q, k, k, out=torch.zeros(1, 2, 128, 64, dtype=h).transpose(2, 3)), "stride 1")
+    rejects(lambda: d(q, k.to(bf), k), "k must be float16")
+    rejects(lambda: d(q, k, k[:, :, :90]), "v must have shape")
+    rejects(lambda: d(q.float(), k, k), "q must be float16 or bfloat16")
+    rejects(lambda: d(q, k, k), "CUDA")  # well-formed CPU tensors still never reach the library
+
+    c = fa.attn_fwd_prefix_causal
+    kc = torch.zeros(1, 1, 96, 128, dtype=h)
+    rejects(lambda: c(q.to(bf), kc, kc, 64), "q must be float16")
+    rejects(lambda: c(q, kc, kc, 64, lse=torch.zeros(1, 2, 64, dtype=torch.float64)), "lse must be float32")
+    rejects(lambda: c(q, kc, kc, 64, out=torch.zeros(1, 1, 64, 128, dtype=h)), "out must have shape")
+
+    cache = torch.zeros(4, 32, 1, 128, dtype=torch.uint8)
+    table = torch.zeros(1, 4, dtype=torch.int32)
+    p = fa.attn_fwd_paged_e4m3
+    rejects(lambda: p(q.to(bf), cache, cache, table, 96, 64), "q must be float16")
+    rejects(lambda: p(q, cache.to(torch.int8), cache, table, 96, 64), "k_cache must be uint8")
+    rejects(lambda: p(q, cache, cache[:2], table, 96, 64), "v_cache must have shape")
+    rejects(lambda: p(q, cache, cache, table.long(), 96, 64), "page_table must be int32")
+    rejects(lambda: p(q, cache, cache, table, 96, 64, lse=torch.zeros(1, 2, 64, dtype=h)), "lse must be float32")
+
+    b = fa.kv_e4m3_paged_to_fp16
+    rejects(lambda: b(cache, cache, table, 1, 96, k_out=torch.zeros(1, 1, 96, 128, dtype=f32)), "k_out must be")
+    rejects(lambda: b(cache, cache, table, 1, 96, v_out=torch.zeros(1, 1, 95, 128, dtype=h)), "v_out must have")
+
+    s = fa.vsa_block_sparse_attn
+    qv = torch.zeros(1, 2, 128, 128, dtype=h)
+    idx = torch.zeros(1, 2, 2, 1, dtype=torch.int32)
+    rejects(lambda: s(qv, qv, qv, idx.long()), "idx must be int32")
+    rejects(lambda: s(qv, qv, qv, torch.zeros(1, 2, 3, 1, dtype=torch.int32)), "idx must have shape")
+    rejects(lambda: s(qv.to(bf), qv, qv, idx), "q must be float16")
+    rejects(lambda: s(qv, qv, qv, idx, lse=torch.zeros(1, 2, 128, dtype=h)), "lse must be float32")
+    rejects(lambda: fa.vsa_block_select(qv, qv, 1, out=torch.zeros(1, 2, 2, 2, dtype=torch.int32)),
+            "out must have shape")
+    rejects(lambda: fa.vsa_block_select(qv.to(bf), qv, 1), "q must be float16")
+
+    g = fa.kv_prefix_fp8_gather
+    kb = torch.zeros(1, 8, 2, 128, dtype=bf)
+    ix = torch.zeros(4, dtype=torch.int32)
+    rejects(lambda: g(kb.to(h), kb, ix), "k must be bfloat16")
+    rejects(lambda: g(kb, kb, ix.long()), "index must be int32")
+    rejects(lambda: g(kb, kb, ix, k_out=torch.zeros(1, 3, 2, 128, dtype=bf)), "k_out must have shape")
