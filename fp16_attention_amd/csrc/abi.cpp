@@ -19,10 +19,12 @@ namespace {
 
 using fa::AttnArgs;
 
-constexpr int kRowsPerTile = 128;  // query rows per workgroup (dense / causal)
-constexpr int kComputeUnits = 256; // MI355X
-constexpr int kMaxSeg = 16;        // key segments per query tile, at most
-constexpr int kMinSegUnits = 16;   // at least 1024 keys per segment
+using fa::kDecodeRows;
+using fa::kRowsPerTile;
+using fa::plan_decode;
+using fa::plan_split;
+using fa::plan_vsa;
+using fa::SplitPlan;
 
 struct Span {
     uintptr_t lo, hi;  // [lo, hi) in bytes
@@ -63,70 +65,6 @@ void fill_view(const fa_tensor& t, const _Float16*& p, int64_t& sb, int64_t& sh,
     ss = t.stride_s;
 }
 
-// Split-KV policy for the causal prefill: a pure function of the shape, so the
-// workspace query and the launch agree and results are reproducible. Each
-// query tile's key range is cut into nseg near-equal segments; nseg is the
-// smallest count whose work items fill the resident workgroup slots of the
-// chip (one per CU at D = 256, two at D = 128) in whole rounds best, since a
-// last, partly filled round costs far more than its share of the work (about
-// half a round's time at a quarter filled, with two slots per CU).
-struct SplitPlan {
-    int n_qt, nseg;
-    size_t workspace;
-};
-
-SplitPlan plan_split(int B, int Hq, int D, int q_rows, int kv_len)
-{
-    SplitPlan p;
-    p.n_qt = (q_rows + kRowsPerTile - 1) / kRowsPerTile;
-    const int max_units = (kv_len + fa::kTileN - 1) / fa::kTileN;
-    const int64_t items = (int64_t)B * Hq * p.n_qt;
-    const int64_t slots = (int64_t)kComputeUnits * (D == 128 ? 2 : 1);
-    auto fill = [&](int n) {
-        const int64_t work = items * n;
-        const int64_t rounds = (work + slots - 1) / slots;
-        return (double)work / (double)(rounds * slots);
-    };
-    p.nseg = 1;
-    double best = fill(1);
-    for (int n = 2; n <= kMaxSeg && fa::seg_units(max_units, n) >= kMinSegUnits; ++n) {
-        const double f = fill(n);
-        if (f > best * 1.01) {
-            best = f;
-            p.nseg = n;
-        }
-    }
-    if (p.nseg <= 1) {
-        p.nseg = 1;
-        p.workspace = 0;
-    } else {
-        size_t rows = (size_t)p.nseg * B * Hq * q_rows;
-        size_t o_bytes = rows * (size_t)D * 4;
-        o_bytes = (o_bytes + 255) & ~(size_t)255;
-        p.workspace = o_bytes + rows * 2 * 4;
-    }
-    return p;
-}
-
-// Split-KV policy for decode: one work item per (b, kv head, segment), as many
-// segments (of at least 1024 keys) as it takes to give every CU its own
-// stream of the cache; a pure function of the shape.
-constexpr int kDecodeRows = 128;  // packed (head, position) rows per work item
-SplitPlan plan_decode(int B, int Hq, int Hkv, int D, int q_rows, int kv_len)
-{
-    SplitPlan p;
-    p.n_qt = 1;
-    const int max_units = (kv_len + fa::kTileN - 1) / fa::kTileN;
-    const int64_t slots = (int64_t)kComputeUnits * (D == 128 ? 2 : 1);
-    const int64_t want = (slots + (int64_t)B * Hkv - 1) / ((int64_t)B * Hkv);
-    const int cap = std::max(1, max_units / kMinSegUnits);
-    p.nseg = (int)std::min<int64_t>(std::max<int64_t>(1, want), cap);
-    size_t rows = (size_t)p.nseg * B * Hq * q_rows;
-    size_t o_bytes = ((rows * (size_t)D * 4) + 255) & ~(size_t)255;
-    p.workspace = o_bytes + rows * 2 * 4;
-    return p;
-}
-
 int check_decode_domain(int B, int Hq, int Hkv, int D, int q_rows, int q_real, int kv_len)
 {
     if (D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
@@ -135,27 +73,6 @@ int check_decode_domain(int B, int Hq, int Hkv, int D, int q_rows, int q_real, i
     if (q_real < 1 || q_real > q_rows) return FA_ERR_SHAPE;
     if (kv_len <= q_real || kv_len > 262144 || kv_len % 32 != 0) return FA_ERR_SHAPE;
     return FA_OK;
-}
-
-// Split of the dense-prefix query blocks of a block-sparse launch into key
-// segments of max(topk, ceil(NB / 16)) blocks, so that no work item is much
-// longer than a sparse query block's list; also a pure function of the shape.
-SplitPlan plan_vsa(int B, int H, int D, int NB, int topk, int dense_prefix)
-{
-    SplitPlan p;
-    p.n_qt = NB;
-    const int len = std::max(topk, (NB + 15) / 16);
-    p.nseg = (NB + len - 1) / len;
-    if (dense_prefix == 0 || p.nseg <= 1) {
-        p.nseg = 1;
-        p.workspace = 0;
-        return p;
-    }
-    size_t rows = (size_t)p.nseg * B * H * dense_prefix * fa::kTileN;
-    size_t o_bytes = rows * (size_t)D * 4;
-    o_bytes = (o_bytes + 255) & ~(size_t)255;
-    p.workspace = o_bytes + rows * 2 * 4;
-    return p;
 }
 
 int check_vsa_domain(int B, int H, int L, int D, int block, int topk, int dense_prefix)
@@ -177,13 +94,6 @@ int check_causal_domain(int B, int Hq, int Hkv, int D, int q_rows, int q_real, i
     return FA_OK;
 }
 
-int set_grid(AttnArgs& a, int64_t items, bool xcd)
-{
-    if (items <= 0 || items > (int64_t)1 << 30) return FA_ERR_SHAPE;
-    a.n_items = (int)items;
-    a.per_xcd = xcd ? (int)((items + 7) / 8) : 0;
-    return FA_OK;
-}
 
 // Shared body of the causal entry points (prefill and decode).
 int run_causal(AttnArgs& a, fa::KvSource src, fa::KeyMode mode, const SplitPlan& p, int D, int q_rows,
@@ -198,20 +108,16 @@ int run_causal(AttnArgs& a, fa::KvSource src, fa::KeyMode mode, const SplitPlan&
             if (overlap(ws, inputs[i])) return FA_ERR_ALIAS;
         if (overlap(ws, out_span) || (a.lse && overlap(ws, lse_span))) return FA_ERR_ALIAS;
     }
-    a.n_qt = p.n_qt;
-    a.nseg = p.nseg;
-    a.part_lq = q_rows;
     const bool decode = mode == fa::KEYS_DECODE;
+    if (!fa::causal_geometry(a, p, a.B, a.Hq, a.Hkv, q_rows, (int)(a.Lkv - a.offset), a.Lkv, decode))
+        return FA_ERR_SHAPE;
     const bool split = p.nseg > 1 || decode;
     if (split) {
-        size_t rows = (size_t)p.nseg * a.B * a.Hq * q_rows;
-        size_t o_bytes = ((rows * (size_t)D * 4) + 255) & ~(size_t)255;
+        size_t o_bytes;
+        fa::partial_bytes((size_t)p.nseg * a.B * a.Hq * q_rows, D, &o_bytes);
         a.o_part = (float*)workspace;
         a.ml_part = (float*)((char*)workspace + o_bytes);
     }
-    const int64_t items = decode ? (int64_t)a.B * a.Hkv * p.nseg : (int64_t)a.B * a.Hq * p.n_qt * p.nseg;
-    int rc = set_grid(a, items, true);
-    if (rc) return rc;
     hipError_t e = fa::launch_attn(a, D, src, mode, split, stream);
     if (e != hipSuccess || !split) return hip_status(e);
     fa::MergeArgs m;
@@ -292,17 +198,9 @@ int run_dense(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse, in
     a.o_sh = o.stride_h;
     a.o_ss = o.stride_s;
     a.lse = lse;
-    a.B = B;
-    a.Hq = H;
-    a.Hkv = H;
-    a.group = 1;
-    a.Lq = Lq;
-    a.Lkv = Lkv;
+    if (!fa::dense_geometry(a, B, H, Lq, Lkv)) return FA_ERR_SHAPE;
     a.c = scale * 1.4426950408889634f;
     a.oscale = 1.f;
-    a.n_qt = (Lq + kRowsPerTile - 1) / kRowsPerTile;
-    a.nseg = 1;
-    if ((rc = set_grid(a, (int64_t)B * H * a.n_qt, true))) return rc;
     return hip_status(fa::launch_attn(a, D, src, fa::KEYS_DENSE, false, (hipStream_t)stream));
 }
 
@@ -627,29 +525,16 @@ int vsa_block_sparse_attn(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, co
     a.o_ss = o.stride_s;
     a.lse = lse;
     a.idx = idx;
-    a.topk = topk;
-    a.dense_prefix = dense_prefix_qblocks;
-    a.nqb = NB;
-    a.B = B;
-    a.Hq = H;
-    a.Hkv = H;
-    a.group = 1;
-    a.Lq = L;
-    a.Lkv = L;
+    if (!fa::vsa_geometry(a, p, B, H, L, block, topk, dense_prefix_qblocks)) return FA_ERR_SHAPE;
     a.c = scale * 1.4426950408889634f;
     a.oscale = 1.f;
-    a.n_qt = NB;
-    a.nseg = p.nseg;
-    a.part_lq = std::min(dense_prefix_qblocks * block, L);  // rows past L do not exist
     const bool split = p.nseg > 1;
     if (split) {
-        size_t rows = (size_t)p.nseg * B * H * a.part_lq;
-        size_t o_bytes = ((rows * (size_t)D * 4) + 255) & ~(size_t)255;
+        size_t o_bytes;
+        fa::partial_bytes((size_t)p.nseg * B * H * a.part_lq, D, &o_bytes);
         a.o_part = (float*)workspace;
         a.ml_part = (float*)((char*)workspace + o_bytes);
     }
-    const int64_t per_bh = (int64_t)dense_prefix_qblocks * p.nseg + (NB - dense_prefix_qblocks);
-    if ((rc = set_grid(a, (int64_t)B * H * per_bh, true))) return rc;
     hipError_t e = fa::launch_attn(a, D, fa::KV_FP16, fa::KEYS_BLOCKS, split, (hipStream_t)stream);
     if (e != hipSuccess || !split) return hip_status(e);
     // the dense-prefix rows: merge the key segments (every key is visible, so

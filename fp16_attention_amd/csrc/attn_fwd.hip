@@ -334,78 +334,19 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     const int hlf = lane >> 5;
 
     // ---- work item -> (b, h, query tile, key range) ----------------------
-    int item = blockIdx.x;
-    if (a.per_xcd > 0) item = (blockIdx.x & 7) * a.per_xcd + (blockIdx.x >> 3);
-    if (item >= a.n_items) return;
-
-    int b, h, qt, seg = 0;
+    // (the decode every launcher and the host-side checker share)
+    const int item = item_of_block(a, blockIdx.x);
+    if (item < 0) return;
     constexpr bool CAUSAL = MODE == KEYS_CAUSAL || MODE == KEYS_DECODE;
-    if (MODE == KEYS_DECODE) {
-        // (b, kv head, key segment); h is the group's first query head
-        seg = item % a.nseg;
-        const int r = item / a.nseg;
-        b = r / a.Hkv;
-        h = (r % a.Hkv) * a.group;
-        qt = 0;
-    } else if (MODE == KEYS_CAUSAL) {
-        int j = item % a.group;
-        int r = item / a.group;
-        qt = r % a.n_qt;
-        r /= a.n_qt;
-        seg = r % a.nseg;
-        r /= a.nseg;
-        int g = r % a.Hkv;
-        b = r / a.Hkv;
-        h = g * a.group + j;
-    } else if (MODE == KEYS_BLOCKS) {
-        // items of one (b, h) are consecutive: the dense-prefix query blocks,
-        // each split into nseg key segments, then the sparse query blocks
-        const int n_dense = a.dense_prefix * a.nseg;
-        const int per_bh = n_dense + (a.nqb - a.dense_prefix);
-        const int bh = item / per_bh;
-        const int r = item % per_bh;
-        if (r < n_dense) {
-            qt = r / a.nseg;
-            seg = r % a.nseg;
-        } else {
-            qt = a.dense_prefix + (r - n_dense);
-        }
-        h = bh % a.Hq;
-        b = bh / a.Hq;
-    } else {
-        qt = item % a.n_qt;
-        int r = item / a.n_qt;
-        h = r % a.Hq;
-        b = r / a.Hq;
-    }
+    const Item wi = decode_item(MODE, a, item, M);
+    if (wi.empty) return;  // a segment past the key range: the merge skips it
+    const int b = wi.b, h = wi.h, qt = wi.qt, seg = wi.seg;
     const int g = h / a.group;
     const int q0 = qt * M;
-
     // keys [key_begin, key_stop) are streamed; key_end bounds every row's keys
-    int key_begin = 0, key_stop = a.Lkv, key_end = a.Lkv, n_tiles;
-    const int32_t* blist = nullptr;
-    if (CAUSAL) {
-        const int last_row = min(q0 + M, a.Lq) - 1;
-        key_end = (int)min((int64_t)a.Lkv, a.offset + last_row + 1);
-        const int len = seg_units((key_end + kTileN - 1) / kTileN, a.nseg) * kTileN;
-        key_begin = seg * len;
-        key_stop = min(key_end, (seg + 1) * len);
-        if (key_begin >= key_stop) return;  // the merge skips segments past the key range
-        n_tiles = (key_stop - key_begin + KT - 1) / KT;
-    } else if (MODE == KEYS_BLOCKS) {
-        if (qt < a.dense_prefix) {
-            const int len = seg_units((a.Lkv + kTileN - 1) / kTileN, a.nseg) * kTileN;
-            key_begin = seg * len;
-            key_stop = min(a.Lkv, (seg + 1) * len);
-            if (key_begin >= key_stop) return;
-            n_tiles = (key_stop - key_begin + KT - 1) / KT;
-        } else {
-            n_tiles = a.topk * (kTileN / KT);
-            blist = a.idx + (((int64_t)b * a.Hq + h) * a.nqb + qt) * a.topk;
-        }
-    } else {
-        n_tiles = (a.Lkv + KT - 1) / KT;
-    }
+    const int key_begin = wi.key_begin, key_stop = wi.key_stop, key_end = wi.key_end;
+    const int32_t* blist = wi.list ? a.idx + (((int64_t)b * a.Hq + h) * a.nqb + qt) * a.topk : nullptr;
+    const int n_tiles = wi.list ? a.topk * (kTileN / KT) : (key_stop - key_begin + KT - 1) / KT;
     const int key_last = key_end - 1;
     const int nblk = (a.Lkv + kTileN - 1) / kTileN;  // the last block may be partial
 

@@ -5,24 +5,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace fa {
+#include "work_items.h"
 
-// Keys per K/V tile staged in LDS.
-constexpr int kTileN = 64;
-// Query rows per wave (one 32-wide MFMA column block).
-constexpr int kRowsPerWave = 32;
+namespace fa {
 
 // KV_BF16: Q, K, V and O are BF16 (dense attention only); it streams like
 // KV_FP16 and differs in the MFMA type and the rounding of P and O.
 enum KvSource { KV_FP16 = 0, KV_E4M3_PAGED = 1, KV_BF16 = 2 };
-// KEYS_DECODE: causal rows of a few query positions (Lq <= 16), with the
-// rows of every query head of a kv-head group packed into one tile, so each
-// K/V byte is read once per group.
-enum KeyMode { KEYS_DENSE = 0, KEYS_CAUSAL = 1, KEYS_BLOCKS = 2, KEYS_DECODE = 3 };
 
 // Everything one attention launch needs; passed by value as the kernel
-// argument. Strides are in elements.
-struct AttnArgs {
+// argument. Strides are in elements. The Geometry part (shape, split and
+// work items) is what the work-item decode reads.
+struct AttnArgs : Geometry {
     const _Float16* q;
     int64_t q_sb, q_sh, q_ss;
     const _Float16* k;
@@ -42,10 +36,7 @@ struct AttnArgs {
     int page_shift;  // log2(page_size)
 
     // block lists
-    const int32_t* idx;  // [B, Hq, Lq / 64, topk]
-    int topk;
-    int dense_prefix;
-    int nqb;  // Lq / 64
+    const int32_t* idx;  // [B, Hq, nqb, topk]
 
     // split-KV partial states (FP32): o_part [nseg][B*Hq][part_lq][D]
     // unnormalised, ml_part [nseg][B*Hq][part_lq][2] = (running max in log2
@@ -54,18 +45,9 @@ struct AttnArgs {
     // keys span nt 64-key units has segments of seg_units(nt, nseg) units.
     float* o_part;
     float* ml_part;
-    int nseg;
-    int part_lq;
 
-    int B, Hq, Hkv, group;
-    int Lq, Lkv;
-    int64_t offset;  // causal: kv_len - q_real
-    float c;         // softmax scale * log2(e) (times k_scale for E4M3)
-    float oscale;    // output scale (v_scale for E4M3, else 1)
-
-    int n_qt;     // query tiles per (b, h)
-    int n_items;  // work items
-    int per_xcd;  // work items per XCD slice (0: identity mapping)
+    float c;       // softmax scale * log2(e) (times k_scale for E4M3)
+    float oscale;  // output scale (v_scale for E4M3, else 1)
 };
 
 struct MergeArgs {
@@ -80,11 +62,6 @@ struct MergeArgs {
     int Lkv;
     float oscale;
 };
-
-// Length, in 64-key units, of the key segments of a query tile whose keys span
-// nt units, when it is split into at most nseg segments; the last one may be
-// shorter, and the number that exist is ceil(nt / seg_units).
-__host__ __device__ inline int seg_units(int nt, int nseg) { return (nt + nseg - 1) / nseg; }
 
 hipError_t launch_attn(const AttnArgs& a, int D, KvSource src, KeyMode mode, bool split,
                        hipStream_t stream);
