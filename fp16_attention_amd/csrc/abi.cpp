@@ -330,10 +330,18 @@ int run_paged(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_cache, const
     a.Lq = q_rows;
     a.Lkv = kv_len;
     a.offset = (int64_t)kv_len - q_real;
-    a.c = scale * k_scale * 1.4426950408889634f;
+    // K is attended as the converted cache's FP16 values RNE16(RNE32(decode *
+    // k_scale)). A power-of-two k_scale in [2^-15, 2^7] keeps every such product
+    // an exact FP16 value, so the exact decode is used and k_scale folds into the
+    // softmax constant; any other k_scale converts each K operand in registers.
+    int k_exp;
+    const bool k_pow2 = frexpf(k_scale, &k_exp) == 0.5f && k_scale >= 0x1p-15f && k_scale <= 128.f;
+    const fa::KvSource src = k_pow2 ? fa::KV_E4M3_PAGED : fa::KV_E4M3_PAGED_SCALED;
+    a.c = scale * (k_pow2 ? k_scale : 1.f) * 1.4426950408889634f;
+    a.kscale = k_scale;
     a.oscale = v_scale;
     const SplitPlan p = decode ? plan_decode(B, Hq, Hkv, D, q_rows, kv_len) : plan_split(B, Hq, D, q_rows, kv_len);
-    return run_causal(a, fa::KV_E4M3_PAGED, decode ? fa::KEYS_DECODE : fa::KEYS_CAUSAL, p, D, q_rows,
+    return run_causal(a, src, decode ? fa::KEYS_DECODE : fa::KEYS_CAUSAL, p, D, q_rows,
                       workspace, workspace_bytes, (hipStream_t)stream, in, 4, so, sl);
 }
 

@@ -61,6 +61,7 @@ typedef short s4 __attribute__((ext_vector_type(4)));
 typedef float f16x __attribute__((ext_vector_type(16)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s4 lds_s4_t;
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -144,7 +145,11 @@ __device__ __forceinline__ float wave_half_sum(float x) { return x + __shfl_xor(
 __device__ __forceinline__ float vmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // Four E4M3 bytes -> four FP16 values, exactly (scale 1: every E4M3 value is
-// an FP16 value, so no rounding happens).
+// an FP16 value, so no rounding happens). The packed pairs are only ever
+// moved as whole dwords: extracting one half of this builtin's result with
+// .x / .y was compiled into a copy of the low half into both halves. The
+// conversion's scale operand only applies its power-of-two part, so any other
+// scale is applied separately (convert8 below).
 __device__ __forceinline__ u2 e4m3x4_to_f16(uint32_t w)
 {
     h2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
@@ -284,7 +289,10 @@ struct Tiling {
     static constexpr int KT = WIDE ? 64 : 32;
     // decode items stream only a few dozen tiles each: there the two-slot
     // ring's shorter unrolled loop measured faster than four slots
-    static constexpr int R = WIDE ? 2 : (MODE != KEYS_BLOCKS && MODE != KEYS_DECODE) ? 4 : 2;
+    // (the scaled E4M3 source converts K two tiles ahead, so it needs four)
+    static constexpr int R = WIDE ? 2
+                             : (SRC == KV_E4M3_PAGED_SCALED || (MODE != KEYS_BLOCKS && MODE != KEYS_DECODE)) ? 4
+                                                                                                              : 2;
     static constexpr int PH = R;  // phases of the unrolled loop
 };
 
@@ -297,8 +305,14 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     constexpr int KS = KT / 16;   // 16-key PV k-steps per tile
     constexpr int KK = D / 16;    // MFMA k-steps over D for S
     constexpr int DB = D / 32;    // 32-wide d blocks of O^T
-    constexpr bool DIRECT = SRC != KV_E4M3_PAGED;  // 16-bit K/V (else E4M3 codes, decoded in registers)
-    constexpr int ROW = (DIRECT ? 2 : 1) * D;      // bytes per LDS row
+    // 16-bit K/V (else E4M3 codes, decoded in registers)
+    constexpr bool DIRECT = SRC != KV_E4M3_PAGED && SRC != KV_E4M3_PAGED_SCALED;
+    // The scaled E4M3 source converts each K code tile once per workgroup into
+    // an FP16 tile (each wave a quarter of it, between its PV MFMAs), from
+    // which every wave reads its K operands as the 16-bit sources do.
+    constexpr bool KCONV = SRC == KV_E4M3_PAGED_SCALED;
+    constexpr int ROW = (DIRECT ? 2 : 1) * D;      // bytes per LDS row of the ring slots
+    constexpr int KROW = (DIRECT || KCONV ? 2 : 1) * D;  // bytes per row of the K operand tiles
     constexpr int TB = KT * ROW;
     constexpr int R = Tiling<D, SRC, MODE>::R;
     // D = 256: the loads of a ring group are spread over the next iteration's
@@ -318,10 +332,14 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     __shared__ __attribute__((aligned(1024))) unsigned char vslot1[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char vslot2[R > 2 ? TB : 16];
     __shared__ __attribute__((aligned(1024))) unsigned char vslot3[R > 3 ? TB : 16];
-    // s_waitcnt that leaves the (ring depth - 2) most recent load groups in flight
+    // FP16 K tiles of the scaled E4M3 source: K(j) in khalf(j % 2)
+    __shared__ __attribute__((aligned(1024))) unsigned char khalf0[KCONV ? KT * 2 * D : 16];
+    __shared__ __attribute__((aligned(1024))) unsigned char khalf1[KCONV ? KT * 2 * D : 16];
+    // s_waitcnt that leaves the (ring depth - 2) most recent load groups in
+    // flight (ring depth - 3 when K is converted a tile earlier)
     constexpr int kGroupLoads =
         2 * (DIRECT ? DirectLoader<D, WAVES, KT>::kLoads : ByteLoader<D, WAVES, KT>::kLoads);
-    constexpr int kVmLeft = (R - 2) * kGroupLoads;
+    constexpr int kVmLeft = (R - (KCONV ? 3 : 2)) * kGroupLoads;
     static_assert(kVmLeft < 64, "vmcnt range");
     constexpr int kWaitGroups = (kVmLeft & 15) | ((kVmLeft >> 4) << 14) | 0x0070;  // and lgkmcnt(0)
 
@@ -468,7 +486,8 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     } else {
         const int vrow = 4 * (grp >> 1) + ((sl >> 1) & 3) + 8 * (sl >> 3);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) koff_s[kk] = btile_off<D>(l32, 16 * kk + 8 * hlf);
+        for (int kk = 0; kk < KK; ++kk)
+            koff_s[kk] = KCONV ? tile_off<D>(l32, 2 * kk + hlf) : btile_off<D>(l32, 16 * kk + 8 * hlf);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             voff_a[db] = btile_off<D>(vrow, 32 * db + 16 * (grp & 1) + 8 * (sl & 1));
@@ -489,15 +508,70 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     // consumes them, so the read stays in flight meanwhile. Row offsets of
     // score block kb and k-step kstep are multiples of 16 rows, where both
     // swizzles repeat.
-    using KRaw = std::conditional_t<DIRECT, h8, u2>;
-    auto kfetch = [&](const unsigned char* kt, int kb, int kk) -> KRaw {
-        return *(const KRaw*)(kt + koff_s[kk] + kb * 32 * ROW);
+    using KRaw = std::conditional_t<DIRECT, h8, u2>;                // V operand reads
+    using KRawK = std::conditional_t<DIRECT || KCONV, h8, u2>;      // K operand reads
+    auto kfetch = [&](const unsigned char* kt, int kb, int kk) -> KRawK {
+        return *(const KRawK*)(kt + koff_s[kk] + kb * 32 * KROW);
     };
     auto decode8 = [](u2 w) -> h8 {
         const u2 lo = e4m3x4_to_f16(w.x), hi = e4m3x4_to_f16(w.y);
         return __builtin_bit_cast(h8, u4{lo.x, lo.y, hi.x, hi.y});
     };
-    auto opuse = [&](const KRaw& r) -> h8 {
+    // Scaled K codes -> RNE16(RNE32(decode * k_scale)), the converted cache's
+    // values: exact FP32 decode, FP32 multiply, FP16 pack rounding to nearest
+    // even (the products are pinned in VGPRs so that the compiler cannot fuse
+    // multiply and conversion into one rounding). Two codes per call.
+    const float kscale = a.kscale;
+    auto convert2 = [kscale](f2 d) -> uint32_t {
+        float x0 = d.x * kscale, x1 = d.y * kscale;
+        asm volatile("" : "+v"(x0), "+v"(x1));
+        return __builtin_bit_cast(uint32_t, h2{(_Float16)x0, (_Float16)x1});
+    };
+    auto opuse_k = [&](const KRawK& r) -> h8 {
+        if constexpr (DIRECT || KCONV)
+            return r;
+        else
+            return decode8(r);
+    };
+    // Conversion of one K code tile into its FP16 tile, in 16-code chunks:
+    // wave w converts chunks (w + WAVES * j) * 64 + lane, j < CV. A chunk is
+    // read from the byte tile (row-major, bswz-swizzled), converted in eight
+    // pairs and written as two 8-value chunks of the FP16 tile (tile_off
+    // layout, as the 16-bit sources' tiles).
+    constexpr int CV = KCONV ? (KT * D / 16) / (WAVES * 64) : 1;  // chunks per lane per tile
+    static_assert(!KCONV || (KT * D / 16) % (WAVES * 64) == 0, "K conversion chunks");
+    auto cv_row = [&](int j) { return ((wave + WAVES * j) * 64 + lane) / (D / 16); };
+    auto cv_chunk = [&](int j) { return ((wave + WAVES * j) * 64 + lane) % (D / 16); };
+    auto cv_read = [&](const unsigned char* bs, int j) -> u4 {
+        const int row = cv_row(j);
+        return *(const u4*)(bs + row * D + ((cv_chunk(j) ^ bswz<D>(row)) << 4));
+    };
+    // pair u (0..7) of a chunk: codes 2u, 2u+1
+    auto cv_pair = [&](const u4& w, int u) -> uint32_t {
+        const uint32_t word = u < 2 ? w.x : u < 4 ? w.y : u < 6 ? w.z : w.w;
+        return (u & 1) ? convert2(__builtin_amdgcn_cvt_pk_f32_fp8(word, true))
+                       : convert2(__builtin_amdgcn_cvt_pk_f32_fp8(word, false));
+    };
+    auto cv_write = [&](unsigned char* hs, int j, const u4& lo, const u4& hi) {
+        const int row = cv_row(j), c = cv_chunk(j);
+        *(u4*)(hs + tile_off<D>(row, 2 * c)) = lo;
+        *(u4*)(hs + tile_off<D>(row, 2 * c + 1)) = hi;
+    };
+    // the whole conversion at once (prologue)
+    auto convert_tile = [&](const unsigned char* bs, unsigned char* hs) {
+#pragma unroll
+        for (int j = 0; j < CV; ++j) {
+            const u4 w = cv_read(bs, j);
+            u4 lo, hi;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) lo[u] = cv_pair(w, u);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) hi[u] = cv_pair(w, u + 4);
+            cv_write(hs, j, lo, hi);
+        }
+    };
+
+    auto opuse_v = [&](const KRaw& r) -> h8 {
         if constexpr (DIRECT)
             return r;
         else
@@ -514,7 +588,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
             for (int kb = 0; kb < NSB; ++kb) {
-                s[kb] = mma<BF>(opuse(kfetch(kt, kb, kk)), qf[kk], s[kb]);
+                s[kb] = mma<BF>(opuse_k(kfetch(kt, kb, kk)), qf[kk], s[kb]);
             }
     };
 
@@ -534,7 +608,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 #pragma unroll
         for (int i = 0; i < KS * DB; ++i) {
             const int kstep = i / DB, db = i % DB;
-            oacc[db] = mma<BF>(opuse(vread(vt, i)), pk[kstep], oacc[db]);
+            oacc[db] = mma<BF>(opuse_v(vread(vt, i)), pk[kstep], oacc[db]);
         }
     };
 
@@ -641,25 +715,53 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         else if constexpr (S == 2) return vslot2;
         else return vslot3;
     };
+    // KCONV: the FP16 K tile of K(j) is khslot(j % 2)
+    auto khslot = [&](auto p) -> unsigned char* {
+        if constexpr (decltype(p)::value % 2 == 0)
+            return khalf0;
+        else
+            return khalf1;
+    };
+    // the tile the K operands of S(j) are read from
+    auto ktile = [&](auto p) -> const unsigned char* {
+        if constexpr (KCONV)
+            return khslot(p);
+        else
+            return kslot(p);
+    };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     using P2 = std::integral_constant<int, 2>;
     using P3 = std::integral_constant<int, 3>;
     using P4 = std::integral_constant<int, 4>;
 
+    // Prologue. KCONV also loads group 1 up front and converts K(0) and K(1);
+    // thereafter iteration it converts K(it+2) between its PV MFMAs, so the
+    // ring wait keeps one group fewer in flight (K(it+2)'s codes must be in LDS
+    // when iteration it starts).
     issue_k(0, kslot0);
     issue_v(0, vslot0);
     issue_k(1, kslot1);
+    if constexpr (KCONV) {
+        issue_k(2, kslot(P2{}));
+        issue_v(1, vslot(P1{}));
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+    if constexpr (KCONV) {
+        convert_tile(kslot0, khalf0);
+        convert_tile(kslot1, khalf1);
+        __syncthreads();
+    }
     f16x scur[NSB];
-    compute_s(kslot0, scur);
+    compute_s(ktile(P0{}), scur);
     raise_max(row_max(scur, tile_key0(0), true));
     __syncthreads();
     {
-        // groups 1 .. R-1 (SPREAD: 1 .. R-2; iteration 0 issues group R-1)
+        // groups 1 .. R-1 (SPREAD: 1 .. R-2; iteration 0 issues group R-1;
+        // KCONV: group 1 is already in)
         constexpr int last = SPREAD ? R - 2 : R - 1;
-        if constexpr (last >= 1) {
+        if constexpr (last >= 1 && !KCONV) {
             issue_k(2, kslot(P2{}));
             issue_v(1, vslot(P1{}));
         }
@@ -711,7 +813,8 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     // already in the last steps of block B.
     auto iteration_main = [&](auto p, int it) {
         using PN = std::integral_constant<int, decltype(p)::value + 1>;
-        const unsigned char* kt = kslot(PN{});
+        using PK2 = std::integral_constant<int, decltype(p)::value + 2>;
+        const unsigned char* kt = ktile(PN{});
         const unsigned char* vt = vslot(p);
         constexpr int NB = NSB * KK;  // score MFMAs
         constexpr int NC = KS * DB;   // PV MFMAs
@@ -729,9 +832,11 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 
         // ---- block B ----
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        KRaw kop[NB];
+        KRawK kop[NB];
         auto kread = [&](int i) { return kfetch(kt, i / KK, i % KK); };
-        constexpr int PB = D == 256 ? 4 : 3;  // K operand reads in flight
+        // K operand reads in flight (FP16 K operands of the scaled E4M3 source
+        // take twice the registers of codes: one fewer at D = 256)
+        constexpr int PB = D == 256 ? (KCONV ? 3 : 4) : 3;
 #pragma unroll
         for (int i = 0; i < PB; ++i) kop[i] = kread(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -739,7 +844,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         for (int i = 0; i < NB; ++i) {
             if (i + PB < NB) kop[i + PB] = kread(i + PB);
             const int kb = i / KK, kk = i % KK;
-            sn[kb] = mma<BF>(opuse(kop[i]), qf[kk], kk == 0 ? f16x{} : sn[kb]);
+            sn[kb] = mma<BF>(opuse_k(kop[i]), qf[kk], kk == 0 ? f16x{} : sn[kb]);
             if (i >= NB - PC) vop[i - (NB - PC)] = vread(vt, i - (NB - PC));
             if constexpr (SPREAD) {
                 if (i % (NB / NL) == 1) DL::issue_one(sg.k, dl.koff, kslot(p), wave, i / (NB / NL));
@@ -762,11 +867,41 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         constexpr bool XCHG_EARLY = D == 256;
         constexpr int MX0 = XCHG_EARLY ? 1 : 2;
         constexpr int MXS = XCHG_EARLY ? NC / 2 : NC - 2;
+        // KCONV: this wave's chunks of K(it+2) are read at step 0 and converted
+        // pair by pair over steps CU0 .. CU0+CUS-1, each chunk written to the
+        // FP16 tile K(it) vacated once its eight pairs are done
+        constexpr int NCU = 8 * CV;
+        constexpr int CU0 = 2;
+        constexpr int CUS = NC - 3;
+        u4 cw[CV], clo[CV], chi[CV];
+        // the step of chunk j's first pair, less two
+        auto cv_read_step = [](int j) {
+            int i = CU0;
+            while (((i - CU0 + 1) * NCU) / CUS <= 8 * j) ++i;
+            return i - 2 < 0 ? 0 : i - 2;
+        };
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             if (i + PC < NC) vop[i + PC] = vread(vt, i + PC);
             const int kstep = i / DB, db = i % DB;
-            oacc[db] = mma<BF>(opuse(vop[i]), pk[kstep], oacc[db]);
+            oacc[db] = mma<BF>(opuse_v(vop[i]), pk[kstep], oacc[db]);
+            if constexpr (KCONV) {
+                // chunk j's codes are read two steps before its first pair
+#pragma unroll
+                for (int j = 0; j < CV; ++j)
+                    if (i == cv_read_step(j)) cw[j] = cv_read(kslot(PK2{}), j);
+                if (i >= CU0 && i < CU0 + CUS) {
+#pragma unroll
+                    for (int u = ((i - CU0) * NCU) / CUS; u < ((i - CU0 + 1) * NCU) / CUS; ++u) {
+                        const int j = u / 8, pr = u % 8;
+                        if (pr < 4)
+                            clo[j][pr] = cv_pair(cw[j], pr);
+                        else
+                            chi[j][pr - 4] = cv_pair(cw[j], pr);
+                        if (pr == 7) cv_write(khslot(p), j, clo[j], chi[j]);
+                    }
+                }
+            }
             if constexpr (SPREAD) {
                 if (i % (NC / NL) == 1) DL::issue_one(sg.v, dl.voff, vslot(PV{}), wave, i / (NC / NL));
             }
@@ -803,9 +938,15 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 #pragma unroll
         for (int kb = 0; kb < NSB; ++kb) sn[kb] = f16x{};
         h8 pk[KS];
-        if (it + 1 < n_tiles) compute_s(kslot(PN{}), sn);
+        if (it + 1 < n_tiles) compute_s(ktile(PN{}), sn);
         exp_tile(scur, pk);
         compute_pv(vslot(p), pk);
+        if constexpr (KCONV) {
+            // K(it+2) into the FP16 tile K(it) vacated (past the last tile the
+            // codes are the zeros of an empty load; they are never used)
+            using PK2 = std::integral_constant<int, decltype(p)::value + 2>;
+            convert_tile(kslot(PK2{}), khslot(p));
+        }
         if (it + 1 < n_tiles) raise_max(row_max(sn, tile_key0(it + 1), true));
         refill(p, it);
 #pragma unroll
@@ -1027,6 +1168,9 @@ static hipError_t launch_d(const AttnArgs& a, KvSource src, KeyMode mode, bool s
     if (src == KV_FP16)
         return split ? launch_one<D, 4, KV_FP16, KEYS_CAUSAL, true>(a, stream)
                      : launch_one<D, 4, KV_FP16, KEYS_CAUSAL, false>(a, stream);
+    if (src == KV_E4M3_PAGED_SCALED)
+        return split ? launch_one<D, 4, KV_E4M3_PAGED_SCALED, KEYS_CAUSAL, true>(a, stream)
+                     : launch_one<D, 4, KV_E4M3_PAGED_SCALED, KEYS_CAUSAL, false>(a, stream);
     return split ? launch_one<D, 4, KV_E4M3_PAGED, KEYS_CAUSAL, true>(a, stream)
                  : launch_one<D, 4, KV_E4M3_PAGED, KEYS_CAUSAL, false>(a, stream);
 }
@@ -1036,7 +1180,13 @@ hipError_t launch_attn(const AttnArgs& a, int D, KvSource src, KeyMode mode, boo
 {
     if (mode == KEYS_DECODE) {
         // always split: the merge writes the output
-        if (src != KV_E4M3_PAGED || !split) return hipErrorInvalidValue;
+        if (!split) return hipErrorInvalidValue;
+        if (src == KV_E4M3_PAGED_SCALED) {
+            if (D == 128) return launch_one<128, 4, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(a, stream);
+            if (D == 256) return launch_one<256, 4, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(a, stream);
+            return hipErrorInvalidValue;
+        }
+        if (src != KV_E4M3_PAGED) return hipErrorInvalidValue;
         if (D == 128) return launch_one<128, 4, KV_E4M3_PAGED, KEYS_DECODE, true>(a, stream);
         if (D == 256) return launch_one<256, 4, KV_E4M3_PAGED, KEYS_DECODE, true>(a, stream);
         return hipErrorInvalidValue;
@@ -1070,6 +1220,12 @@ template __global__ void attn_fwd_kernel<128, 2, KV_FP16, KEYS_BLOCKS, false>(co
 template __global__ void attn_fwd_kernel<128, 2, KV_FP16, KEYS_BLOCKS, true>(const AttnArgs);
 template __global__ void attn_fwd_kernel<128, 4, KV_E4M3_PAGED, KEYS_DECODE, true>(const AttnArgs);
 template __global__ void attn_fwd_kernel<256, 4, KV_E4M3_PAGED, KEYS_DECODE, true>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 4, KV_E4M3_PAGED_SCALED, KEYS_CAUSAL, false>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 4, KV_E4M3_PAGED_SCALED, KEYS_CAUSAL, true>(const AttnArgs);
+template __global__ void attn_fwd_kernel<256, 4, KV_E4M3_PAGED_SCALED, KEYS_CAUSAL, false>(const AttnArgs);
+template __global__ void attn_fwd_kernel<256, 4, KV_E4M3_PAGED_SCALED, KEYS_CAUSAL, true>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 4, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(const AttnArgs);
+template __global__ void attn_fwd_kernel<256, 4, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(const AttnArgs);
 
 hipError_t launch_merge(const MergeArgs& m, int D, hipStream_t stream)
 {

@@ -11,7 +11,13 @@ namespace fa {
 
 // KV_BF16: Q, K, V and O are BF16 (dense attention only); it streams like
 // KV_FP16 and differs in the MFMA type and the rounding of P and O.
-enum KvSource { KV_FP16 = 0, KV_E4M3_PAGED = 1, KV_BF16 = 2 };
+// KV_E4M3_PAGED: E4M3 codes decoded exactly to FP16 in registers; used when
+// k_scale is a power of two that keeps every decode * k_scale an exact FP16
+// value, so folding k_scale into the softmax constant changes nothing.
+// KV_E4M3_PAGED_SCALED: the K operands are converted in registers to exactly
+// the FP16 value the conversion defines, RNE16(RNE32(decode * k_scale)), for
+// any other k_scale.
+enum KvSource { KV_FP16 = 0, KV_E4M3_PAGED = 1, KV_BF16 = 2, KV_E4M3_PAGED_SCALED = 3 };
 
 // Everything one attention launch needs; passed by value as the kernel
 // argument. Strides are in elements. The Geometry part (shape, split and
@@ -46,8 +52,9 @@ struct AttnArgs : Geometry {
     float* o_part;
     float* ml_part;
 
-    float c;       // softmax scale * log2(e) (times k_scale for E4M3)
+    float c;       // softmax scale * log2(e) (times k_scale for KV_E4M3_PAGED)
     float oscale;  // output scale (v_scale for E4M3, else 1)
+    float kscale;  // KV_E4M3_PAGED_SCALED: the K conversion scale
 };
 
 struct MergeArgs {
