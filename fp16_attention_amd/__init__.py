@@ -24,6 +24,7 @@ EXPORTS = ("fa_abi_version", "fa_error_string", "attn_fwd_dense", "attn_fwd_dens
            "attn_fwd_prefix_causal_workspace",
            "attn_fwd_prefix_causal", "attn_fwd_paged_e4m3_workspace", "attn_fwd_paged_e4m3",
            "attn_fwd_paged_e4m3_decode_workspace", "attn_fwd_paged_e4m3_decode",
+           "attn_fwd_paged_e4m3_decode_noalloc",
            "kv_e4m3_paged_to_fp16", "kv_prefix_fp8_gather", "vsa_topk_for_sparsity", "vsa_block_select_workspace",
            "vsa_block_select",
            "vsa_block_sparse_attn_workspace", "vsa_block_sparse_attn")
@@ -55,6 +56,8 @@ _SIGS = {
     "attn_fwd_paged_e4m3_decode_workspace": (_sz, [_i] * 6),
     "attn_fwd_paged_e4m3_decode": (_i, [FaTensor, _vp, _vp, _vp, _i64, _i, _i, _f, _f, FaTensor, _vp]
                                    + [_i] * 7 + [_f, _vp, _sz, _vp]),
+    "attn_fwd_paged_e4m3_decode_noalloc": (_i, [FaTensor, _vp, _vp, _vp, _i64, _i, _i, _f, _f, FaTensor, _vp]
+                                           + [_i] * 7 + [_f, _vp]),
     "kv_e4m3_paged_to_fp16": (_i, [_vp, _vp, _vp, _i64] + [_i] * 6 + [_f, _f, _vp, _vp, _vp]),
     "kv_prefix_fp8_gather": (_i, [_vp, _vp] + [_i] * 4 + [_vp, _i, _vp, _vp, _vp]),
     "vsa_topk_for_sparsity": (_i, [_i, _i, ctypes.c_double]),
@@ -252,7 +255,21 @@ def attn_fwd_paged_e4m3_decode(q, k_cache, v_cache, page_table, kv_len, q_real=N
                   workspace)
 
 
-def _paged(decode, q, k_cache, v_cache, page_table, kv_len, q_real, k_scale, v_scale, out, lse, scale, workspace):
+NOALLOC_SCRATCH_BYTES = 32 << 20  # FA_NOALLOC_SCRATCH_BYTES
+
+
+def attn_fwd_paged_e4m3_decode_noalloc(q, k_cache, v_cache, page_table, kv_len, out, q_real=None, k_scale=1.0,
+                                       v_scale=1.0, lse=None, scale=None):
+    """attn_fwd_paged_e4m3_decode without a workspace: the split-KV partial states go to the
+    library's own per-GPU scratch array (no device allocation in the call). out must be given
+    (a caller that cannot allocate owns it); calls that overlap on one GPU race."""
+    q_real = q.shape[2] if q_real is None else q_real
+    return _paged(True, q, k_cache, v_cache, page_table, kv_len, q_real, k_scale, v_scale, out, lse, scale,
+                  None, noalloc=True)
+
+
+def _paged(decode, q, k_cache, v_cache, page_table, kv_len, q_real, k_scale, v_scale, out, lse, scale, workspace,
+           noalloc=False):
     import torch
     _want(q, "q", _f16(), ndim=4, unit_d=True)
     B, Hq, q_rows, D = q.shape
@@ -267,10 +284,18 @@ def _paged(decode, q, k_cache, v_cache, page_table, kv_len, q_real, k_scale, v_s
     _want(out, "out", _f16(), shape=(B, Hq, q_rows, D), unit_d=True)
     _lse_shape_ok(lse, (B, Hq, q_rows))
     _need_cuda(q, k_cache, v_cache, page_table, out, lse)
-    if out is None:
-        out = torch.empty_like(q, memory_format=torch.contiguous_format)
     scale = default_scale(D) if scale is None else scale
     lib = load()
+    if noalloc:
+        if out is None:
+            raise ValueError("the allocation-free decode writes into a caller-provided out")
+        _check(lib.attn_fwd_paged_e4m3_decode_noalloc(
+            _view(q), k_cache.data_ptr(), v_cache.data_ptr(), page_table.data_ptr(), page_table.stride(0), pages,
+            page_size, k_scale, v_scale, _view(out), _ptr(lse), B, Hq, Hkv, D, q_rows, q_real, kv_len, scale,
+            _stream(q)))
+        return out
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
     wsq = lib.attn_fwd_paged_e4m3_decode_workspace if decode else lib.attn_fwd_paged_e4m3_workspace
     fn = lib.attn_fwd_paged_e4m3_decode if decode else lib.attn_fwd_paged_e4m3
     ws = _workspace(int(wsq(B, Hq, Hkv, D, q_rows, kv_len)), q.device, workspace)

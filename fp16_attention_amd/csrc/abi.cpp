@@ -98,8 +98,12 @@ int check_causal_domain(int B, int Hq, int Hkv, int D, int q_rows, int q_real, i
 // Shared body of the causal entry points (prefill and decode).
 int run_causal(AttnArgs& a, fa::KvSource src, fa::KeyMode mode, const SplitPlan& p, int D, int q_rows,
                void* workspace, size_t workspace_bytes, hipStream_t stream, const Span* inputs,
-               int n_inputs, Span out_span, Span lse_span)
+               int n_inputs, Span out_span, Span lse_span, const fa::WorkspaceSource* wsrc = nullptr)
 {
+    if (p.workspace > 0 && wsrc) {
+        const int rc = wsrc->get(p.workspace, &workspace, &workspace_bytes);
+        if (rc) return rc;
+    }
     if (p.workspace > 0) {
         if (!workspace || workspace_bytes < p.workspace) return FA_ERR_WORKSPACE;
         if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
@@ -282,7 +286,8 @@ namespace {
 int run_paged(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_cache, const int32_t* page_table,
               int64_t table_stride, int num_phys_pages, int page_size, float k_scale, float v_scale,
               fa_tensor o, float* lse, int B, int Hq, int Hkv, int D, int q_rows, int q_real, int kv_len,
-              float scale, void* workspace, size_t workspace_bytes, void* stream, bool decode)
+              float scale, void* workspace, size_t workspace_bytes, void* stream, bool decode,
+              const fa::WorkspaceSource* wsrc = nullptr)
 {
     int rc;
     if ((rc = check_view(q)) || (rc = check_view(o))) return rc;
@@ -342,10 +347,21 @@ int run_paged(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_cache, const
     a.oscale = v_scale;
     const SplitPlan p = decode ? plan_decode(B, Hq, Hkv, D, q_rows, kv_len) : plan_split(B, Hq, D, q_rows, kv_len);
     return run_causal(a, src, decode ? fa::KEYS_DECODE : fa::KEYS_CAUSAL, p, D, q_rows,
-                      workspace, workspace_bytes, (hipStream_t)stream, in, 4, so, sl);
+                      workspace, workspace_bytes, (hipStream_t)stream, in, 4, so, sl, wsrc);
 }
 
 }  // namespace
+
+int fa::paged_decode_from(const WorkspaceSource* wsrc, const void* q, int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                          const uint8_t* k_cache, const uint8_t* v_cache, const int32_t* page_table,
+                          int64_t table_stride, int num_phys_pages, int page_size, float k_scale, float v_scale,
+                          void* o, int64_t o_sb, int64_t o_sh, int64_t o_ss, float* lse, int B, int Hq, int Hkv,
+                          int D, int q_rows, int q_real, int kv_len, float scale, void* stream)
+{
+    const fa_tensor qt = {(void*)q, q_sb, q_sh, q_ss}, ot = {o, o_sb, o_sh, o_ss};
+    return run_paged(qt, k_cache, v_cache, page_table, table_stride, num_phys_pages, page_size, k_scale, v_scale,
+                     ot, lse, B, Hq, Hkv, D, q_rows, q_real, kv_len, scale, nullptr, 0, stream, true, wsrc);
+}
 
 extern "C" {
 

@@ -70,6 +70,21 @@ struct MergeArgs {
     float oscale;
 };
 
+// Supplies a call's workspace once all its arguments are validated: used by
+// the allocation-free decode entry point to hand in the library's own scratch
+// array; returns 0 or an fa_status code.
+struct WorkspaceSource {
+    int (*get)(size_t need, void** ptr, size_t* bytes);
+};
+
+// The paged E4M3 decode of attn_fwd_paged_e4m3_decode with its workspace
+// taken from `wsrc` (abi.cpp).
+int paged_decode_from(const WorkspaceSource* wsrc, const void* q, int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                      const uint8_t* k_cache, const uint8_t* v_cache, const int32_t* page_table,
+                      int64_t table_stride, int num_phys_pages, int page_size, float k_scale, float v_scale,
+                      void* o, int64_t o_sb, int64_t o_sh, int64_t o_ss, float* lse, int B, int Hq, int Hkv, int D,
+                      int q_rows, int q_real, int kv_len, float scale, void* stream);
+
 hipError_t launch_attn(const AttnArgs& a, int D, KvSource src, KeyMode mode, bool split,
                        hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& m, int D, hipStream_t stream);

@@ -175,6 +175,29 @@ int attn_fwd_paged_e4m3_decode(fa_tensor q, const uint8_t* k_cache, const uint8_
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_fwd_paged_e4m3_decode for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Arguments, layouts, domain and results as
+ * attn_fwd_paged_e4m3_decode, without the workspace: the split-KV partial
+ * states go to a device array of the library, FA_NOALLOC_SCRATCH_BYTES per
+ * GPU, held from the library's load on that GPU until the process ends. The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library call);
+ * on its first call on a GPU it looks up the array's device address there.
+ * Returns FA_ERR_WORKSPACE, before any HIP call, when the shape's partial
+ * states, attn_fwd_paged_e4m3_decode_workspace(...) bytes, exceed
+ * FA_NOALLOC_SCRATCH_BYTES (the decode at KV 256000, Hq 6, Hkv 1, D 256,
+ * 16 positions takes 24.8 MB). All calls on one GPU share its array: calls
+ * that overlap on one GPU (other streams, other host threads) race, and a
+ * caller must order them.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_fwd_paged_e4m3_decode_noalloc(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                       const int32_t* page_table, int64_t table_stride, int num_phys_pages,
+                                       int page_size, float k_scale, float v_scale, fa_tensor o, float* lse,
+                                       int B, int Hq, int Hkv, int D, int q_rows, int q_real, int kv_len,
+                                       float scale, void* stream);
+
+/*
  * Exact paged E4M3 -> FP16 conversion ([P4] Implementation, the "exact E4M3
  * bridge"). For every logical token t < kv_len of row b and kv head g:
  *   k_out[b,g,t,:] = RNE16(RNE32(decode(k_cache[page][t % page_size][g][:]) * k_scale))

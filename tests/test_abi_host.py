@@ -345,3 +345,29 @@ def test_binding_validates_every_tensor_before_the_library():
     rejects(lambda: g(kb.to(h), kb, ix), "k must be bfloat16")
     rejects(lambda: g(kb, kb, ix.long()), "index must be int32")
     rejects(lambda: g(kb, kb, ix, k_out=torch.zeros(1, 3, 2, 128, dtype=bf)), "k_out must have shape")
+
+
+def test_noalloc_decode_rejects_before_any_hip_call():
+    """The allocation-free decode validates every argument, and that the
+    shape's partial states fit its fixed scratch, before any HIP call (these
+    calls run without a GPU)."""
+    lib = fa.load()
+
+    def call(**kw):
+        a = dict(q_rows=16, q_real=16, Hq=6, Hkv=1, D=256, kv_len=4096, page_size=32, ks=1.0, kc=B_,
+                 stride=262144 // 32)
+        a.update(kw)
+        return lib.attn_fwd_paged_e4m3_decode_noalloc(T(A), a["kc"], C, L, a["stride"], 9000, a["page_size"],
+                                                      a["ks"], 1.0, T(O), None, 1, a["Hq"], a["Hkv"], a["D"],
+                                                      a["q_rows"], a["q_real"], a["kv_len"], 0.0625, None)
+    scratch = fa.NOALLOC_SCRATCH_BYTES
+    assert scratch == 32 << 20
+    # the workload decode fits; 8 heads at the longest cache do not
+    assert lib.attn_fwd_paged_e4m3_decode_workspace(1, 6, 1, 256, 16, 256000) <= scratch
+    assert lib.attn_fwd_paged_e4m3_decode_workspace(1, 8, 1, 256, 16, 262144) > scratch
+    assert call(Hq=8, kv_len=262144) == fa.FA_ERR_WORKSPACE
+    assert call(q_rows=17, q_real=17) == fa.FA_ERR_SHAPE
+    assert call(kc=0) == fa.FA_ERR_NULL
+    assert call(page_size=16) == fa.FA_ERR_UNSUPPORTED
+    assert call(ks=float("nan")) == fa.FA_ERR_SHAPE
+    assert call(kc=B_ + 4) == fa.FA_ERR_ALIGN
