@@ -73,6 +73,8 @@ def _load():
         lib.or_vsa_scores.restype = None
         lib.or_vsa_scores.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 4 + [
             ctypes.c_void_p]
+        lib.or_block_lists.restype = None
+        lib.or_block_lists.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 4 + [ctypes.c_void_p] * 4
         lib.or_vsa_topk.restype = None
         lib.or_vsa_topk.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 4 + [ctypes.c_void_p]
         _lib = lib
@@ -269,3 +271,28 @@ def vsa_select(q: np.ndarray, k: np.ndarray, block: int, topk: int):
     """Pool, score, select. Returns (idx int32 [B,H,NB,topk], scores f64 [B,H,NB,NB])."""
     s = vsa_scores(vsa_pool(q, block), vsa_pool(k, block))
     return vsa_topk(s, topk), s
+
+
+def block_lists(mask: np.ndarray, valid: np.ndarray, tile: int, quadrants: bool = True):
+    """128-token block lists from a square tile mask [B,H,T,T] (bool or uint8) and the
+    valid-token counts of the T tiles of `tile` tokens. Returns (idx int32 [B,H,NB,NB],
+    counts int32 [B,H,NB], kv_valid int32 [2*NB], quad uint8 [B,H,NB,NB] or None)."""
+    lib = _load()
+    m = np.ascontiguousarray(mask, dtype=np.uint8)
+    v = np.ascontiguousarray(valid, dtype=np.int32)
+    B, H, T, T2 = m.shape
+    assert T == T2 and v.shape == (T,) and tile % 64 == 0
+    nb = (T * (tile // 64) + 1) // 2
+    idx = np.empty((B, H, nb, nb), dtype=np.int32)
+    counts = np.empty((B, H, nb), dtype=np.int32)
+    kv = np.empty((2 * nb,), dtype=np.int32)
+    quad = np.empty((B, H, nb, nb), dtype=np.uint8) if quadrants else None
+    lib.or_block_lists(_ptr(m), _ptr(v), B, H, T, tile, _ptr(idx), _ptr(counts), _ptr(kv),
+                       _ptr(quad) if quad is not None else None)
+    return idx, counts, kv, quad
+
+
+def tile_means(x: np.ndarray, block: int) -> np.ndarray:
+    """FP32 means of the valid rows of each `block`-row tile of x [B,H,L,D] FP16 (the
+    exact sum divided by the count, rounded once): the pooled V of the VSA coarse branch."""
+    return vsa_pool(x, block)

@@ -532,3 +532,82 @@ void or_vsa_topk(const double* s, int B, int H, int NB, int topk, int32_t* idx)
     }
     free(taken);
 }
+
+/* ------------------------------------------------------------------------ */
+/* VSA block lists of 128-token blocks ([P5] block_lists.py,                */
+/* tile_mask_to_fp4_blocks: the native kernel's descending block lists).     */
+/*                                                                            */
+/* Inputs: a square tile mask mask[b][h][i][j] (1 byte per entry; nonzero =   */
+/* query tile i attends to key tile j) over T tiles of `tile` = 64 * HT      */
+/* tokens, and valid[t], the valid tokens of tile t. The sequence is cut into */
+/* 64-token halves (HT per tile, T * HT in all), and two consecutive halves   */
+/* form one of NB = ceil(T * HT / 2) blocks. For query block r (halves        */
+/* q0 = 2r, q1 = 2r + 1) and key block c (halves a = 2c, e = 2c + 1):         */
+/*   va = clamp(valid[a / HT] - (a % HT) * 64, 0, 64), ve likewise, and 0     */
+/*        for a half past the sequence;                                       */
+/*   m(q, k) = mask[q / HT][k / HT] for halves inside the sequence, else 0;   */
+/*   a query half q1 past the sequence (an odd count of halves) sees key     */
+/*   half 0 only: m(q1, k) = (k == 0);                                        */
+/*   quad = [m(q0,a) & va>0] + 2 [m(q0,e) & ve>0] + 4 [m(q1,a) & va>0]        */
+/*          + 8 [m(q1,e) & ve>0].                                             */
+/* Outputs per (b, h, r): idx[..][0..n) = the key blocks c with quad != 0 in */
+/* descending order, idx[..][n..NB) = 0; quad_out likewise (its quad values); */
+/* counts = n. kv_valid[2c], kv_valid[2c+1] = va, ve (one vector for all     */
+/* (b, h)). quad_out may be NULL.                                             */
+/* ------------------------------------------------------------------------ */
+static int or_half_valid(const int32_t* valid, int T, int HT, int half)
+{
+    if (half >= T * HT)
+        return 0;
+    int v = valid[half / HT] - (half % HT) * 64;
+    return v < 0 ? 0 : (v > 64 ? 64 : v);
+}
+
+static int or_half_mask(const uint8_t* m, int T, int HT, int qh, int kh)
+{
+    if (qh >= T * HT)
+        return kh == 0; /* the padded odd query half sees key half 0 only */
+    if (kh >= T * HT)
+        return 0;
+    return m[(int64_t)(qh / HT) * T + kh / HT] != 0;
+}
+
+void or_block_lists(const uint8_t* mask, const int32_t* valid, int B, int H, int T, int tile, int32_t* idx,
+                    int32_t* counts, int32_t* kv_valid, uint8_t* quad_out)
+{
+    const int HT = tile / 64;
+    const int NB = (T * HT + 1) / 2;
+    for (int c = 0; c < NB; ++c) {
+        kv_valid[2 * c] = or_half_valid(valid, T, HT, 2 * c);
+        kv_valid[2 * c + 1] = or_half_valid(valid, T, HT, 2 * c + 1);
+    }
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            const uint8_t* m = mask + ((int64_t)b * H + h) * T * T;
+            for (int r = 0; r < NB; ++r) {
+                int32_t* list = idx + (((int64_t)b * H + h) * NB + r) * NB;
+                uint8_t* ql = quad_out ? quad_out + (((int64_t)b * H + h) * NB + r) * NB : NULL;
+                int n = 0;
+                for (int c = NB - 1; c >= 0; --c) {
+                    const int a = 2 * c, e = 2 * c + 1;
+                    const int va = kv_valid[a] > 0, ve = kv_valid[e] > 0;
+                    const int q0 = 2 * r, q1 = 2 * r + 1;
+                    const int bits = (or_half_mask(m, T, HT, q0, a) && va) + 2 * (or_half_mask(m, T, HT, q0, e) && ve) +
+                                     4 * (or_half_mask(m, T, HT, q1, a) && va) +
+                                     8 * (or_half_mask(m, T, HT, q1, e) && ve);
+                    if (bits) {
+                        list[n] = c;
+                        if (ql)
+                            ql[n] = (uint8_t)bits;
+                        ++n;
+                    }
+                }
+                for (int t = n; t < NB; ++t) {
+                    list[t] = 0;
+                    if (ql)
+                        ql[t] = 0;
+                }
+                counts[((int64_t)b * H + h) * NB + r] = n;
+            }
+        }
+}

@@ -3,6 +3,7 @@ top-k (no GPU). Anchors: an exact int64 fixed-point sum, exact small-integer
 dot products, numpy's lexsort as an independent ranking, and the planted,
 all-equal and full-set special cases."""
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -108,3 +109,109 @@ def test_select_picks_planted_dominant_block():
     assert np.all(idx == 5)
     idx3, _ = oracle.vsa_select(q, k, blk, 3)
     assert np.all(np.any(idx3 == 5, axis=-1)) and np.all(np.diff(idx3, axis=-1) > 0)
+
+
+# ---------------------------------------------------------------- block lists
+# The list format of "[perf] FastH3 two-Spark: gather packed FP4 inputs before
+# head projections", block_lists.py: 128-token blocks built from two 64-token
+# halves, descending variable-length key-block lists, per-half valid counts
+# and 4-bit quadrant masks (query half x 2 + key half).
+
+def test_block_lists_tile128_is_the_mask_itself():
+    """With 128-token tiles every tile is one block: a block is listed with all
+    four quadrant bits exactly when the mask selects the tile."""
+    rng = np.random.default_rng(3)
+    mask = rng.random((2, 3, 9, 9)) < 0.3
+    idx, counts, kv, quad = oracle.block_lists(mask, np.full(9, 128, np.int32), 128)
+    assert np.array_equal(counts, mask.sum(-1))
+    assert np.array_equal(kv, np.full(18, 64))
+    for b, h, r in np.ndindex(2, 3, 9):
+        want = np.nonzero(mask[b, h, r])[0][::-1]
+        n = len(want)
+        assert np.array_equal(idx[b, h, r, :n], want) and not idx[b, h, r, n:].any()
+        assert np.all(quad[b, h, r, :n] == 15) and not quad[b, h, r, n:].any()
+
+
+@pytest.mark.parametrize("i,j", [(0, 0), (0, 1), (1, 0), (1, 1), (6, 3), (3, 6)])
+def test_block_lists_one_selected_tile_sets_one_quadrant_bit(i, j):
+    """A single selected 64-token tile (query tile i, key tile j) lists exactly
+    key block j // 2 for query block i // 2, with quadrant bit
+    2 * (i % 2) + (j % 2): a transposed mask or swapped bits fail here."""
+    T = 8
+    mask = np.zeros((1, 1, T, T), bool)
+    mask[0, 0, i, j] = True
+    idx, counts, kv, quad = oracle.block_lists(mask, np.full(T, 64, np.int32), 64)
+    nz = np.argwhere(counts[0, 0] > 0).ravel()
+    assert list(nz) == [i // 2]
+    assert counts[0, 0, i // 2] == 1 and idx[0, 0, i // 2, 0] == j // 2
+    assert quad[0, 0, i // 2, 0] == 1 << (2 * (i % 2) + (j % 2))
+
+
+def test_block_lists_any_quadrant_lists_the_block_and_bits_count_pairs():
+    """64-token tiles, all valid, even count: a key block is listed iff any of
+    its four (query half, key half) tiles is selected, and the quadrant bits of
+    a row add up to the selected tile pairs of its two query tiles."""
+    rng = np.random.default_rng(4)
+    T = 12
+    mask = rng.random((1, 2, T, T)) < 0.15
+    idx, counts, kv, quad = oracle.block_lists(mask, np.full(T, 64, np.int32), 64)
+    nb = T // 2
+    pooled = mask.reshape(1, 2, nb, 2, nb, 2).any(axis=(3, 5))
+    assert np.array_equal(counts, pooled.sum(-1))
+    bits = np.unpackbits(quad[..., None], axis=-1).sum(-1)
+    assert np.array_equal(bits.sum(-1), mask.reshape(1, 2, nb, 2, T).sum(axis=(3, 4)))
+    for h, r in np.ndindex(2, nb):
+        n = counts[0, h, r]
+        assert np.all(np.diff(idx[0, h, r, :n]) < 0)  # strictly descending
+        assert set(idx[0, h, r, :n]) == set(np.nonzero(pooled[0, h, r])[0])
+
+
+def test_block_lists_valid_counts_and_empty_halves():
+    """Per-half valid counts come from the tiles' counts (64-token halves of a
+    128-token tile split them); a half with no valid token is never selected."""
+    # 128-token tiles, the last holding 70 tokens: halves 64 64 64 6
+    _, _, kv, _ = oracle.block_lists(np.ones((1, 1, 2, 2), bool), np.array([128, 70], np.int32), 128)
+    assert list(kv) == [64, 64, 64, 6]
+    # 64-token tiles, the second one empty: its half contributes no bit
+    mask = np.ones((1, 1, 4, 4), bool)
+    idx, counts, kv, quad = oracle.block_lists(mask, np.array([64, 0, 64, 30], np.int32), 64)
+    assert list(kv) == [64, 0, 64, 30]
+    assert list(idx[0, 0, 0, :2]) == [1, 0] and list(quad[0, 0, 0, :2]) == [15, 5]  # key half 1 has no token
+    assert int(kv.sum()) == 64 + 0 + 64 + 30
+
+
+def test_block_lists_odd_half_count_pads_with_key_half_zero():
+    """An odd count of 64-token halves: the last block's second query half is
+    padding that sees key half 0 only (whatever the mask says)."""
+    T = 5  # 64-token tiles: halves 0..4, blocks of halves (8, 9): half 9 is padding
+    mask = np.zeros((1, 1, T, T), bool)
+    idx, counts, kv, quad = oracle.block_lists(mask, np.full(T, 64, np.int32), 64)
+    assert list(kv) == [64] * 5 + [0]
+    assert counts[0, 0, :2].sum() == 0
+    assert counts[0, 0, 2] == 1 and idx[0, 0, 2, 0] == 0 and quad[0, 0, 2, 0] == 4
+    mask[0, 0, 4, 3] = True   # query half 8 -> key half 3 (block 1, second half)
+    idx, counts, _, quad = oracle.block_lists(mask, np.full(T, 64, np.int32), 64)
+    assert list(idx[0, 0, 2, :2]) == [1, 0] and list(quad[0, 0, 2, :2]) == [2, 4]
+
+
+def test_block_lists_of_a_topk_selection():
+    """Lists built from a top-k selection (64-token tiles): every listed block's
+    bits are exactly the selected tiles among its four, and the union of the
+    lists covers every selected tile."""
+    q = np.random.default_rng(5).standard_normal((1, 2, 64 * 10, 128)).astype(np.float16)
+    k = np.random.default_rng(6).standard_normal((1, 2, 64 * 10, 128)).astype(np.float16)
+    sel, _ = oracle.vsa_select(q, k, 64, 3)
+    mask = np.zeros((1, 2, 10, 10), bool)
+    for h, i in np.ndindex(2, 10):
+        mask[0, h, i, sel[0, h, i]] = True
+    idx, counts, _, quad = oracle.block_lists(mask, np.full(10, 64, np.int32), 64)
+    for h, r in np.ndindex(2, 5):
+        got = set()
+        for t in range(counts[0, h, r]):
+            c, bits = idx[0, h, r, t], quad[0, h, r, t]
+            for qh, kh in np.ndindex(2, 2):
+                on = bool(bits & (1 << (2 * qh + kh)))
+                assert on == mask[0, h, 2 * r + qh, 2 * c + kh]
+                if on:
+                    got.add((2 * r + qh, 2 * c + kh))
+        assert got == {(2 * r + qh, j) for qh in range(2) for j in sel[0, h, 2 * r + qh]}
