@@ -27,7 +27,8 @@ EXPORTS = ("fa_abi_version", "fa_error_string", "attn_fwd_dense", "attn_fwd_dens
            "attn_fwd_paged_e4m3_decode_noalloc",
            "kv_e4m3_paged_to_fp16", "kv_prefix_fp8_gather", "vsa_topk_for_sparsity", "vsa_block_select_workspace",
            "vsa_block_select",
-           "vsa_block_sparse_attn_workspace", "vsa_block_sparse_attn")
+           "vsa_block_sparse_attn_workspace", "vsa_block_sparse_attn", "vsa_tile_means",
+           "vsa_tile_mask_to_block_lists")
 
 
 class FaTensor(ctypes.Structure):
@@ -65,6 +66,8 @@ _SIGS = {
     "vsa_block_select": (_i, [_vp, _vp] + [_i] * 6 + [_vp, _vp, _vp, _sz, _vp]),
     "vsa_block_sparse_attn_workspace": (_sz, [_i] * 7),
     "vsa_block_sparse_attn": (_i, [FaTensor] * 4 + [_vp, _vp] + [_i] * 7 + [_f, _vp, _sz, _vp]),
+    "vsa_tile_means": (_i, [_vp] + [_i] * 5 + [_vp, _vp]),
+    "vsa_tile_mask_to_block_lists": (_i, [_vp, _vp] + [_i] * 4 + [_vp] * 5),
 }
 
 
@@ -409,3 +412,42 @@ def vsa_block_sparse_attn(q, k, v, idx, dense_prefix_qblocks=2, block=64, out=No
                                         B, H, L, D, block, topk, dense_prefix_qblocks, scale, _ptr(ws),
                                         _nbytes(ws), _stream(q)))
     return out
+
+
+def vsa_tile_means(x, block=64, out=None):
+    """FP32 means of each 64-row tile of x [B,H,L,128] FP16 contiguous (the last tile may be
+    partial): the pooled V of the VSA coarse branch. Returns float32 [B,H,ceil(L/64),128]."""
+    import torch
+    _want(x, "x", _f16(), ndim=4, contiguous=True)
+    B, H, L, D = x.shape
+    NB = (L + block - 1) // block
+    _want(out, "out", (torch.float32,), shape=(B, H, NB, D), contiguous=True)
+    _need_cuda(x, out)
+    if out is None:
+        out = torch.empty((B, H, NB, D), dtype=torch.float32, device=x.device)
+    _check(load().vsa_tile_means(x.data_ptr(), B, H, L, D, block, out.data_ptr(), _stream(x)))
+    return out
+
+
+def vsa_tile_mask_to_block_lists(mask, valid, tile, quadrants=True):
+    """128-token block lists from a square tile mask [B,H,T,T] (bool or uint8) and the valid
+    tokens of the T tiles (int32 [T]). Returns (indices int32 [B,H,NB,NB] descending then zero,
+    counts int32 [B,H,NB], kv_valid int32 [2*NB], quadrants uint8 [B,H,NB,NB] or None)."""
+    import torch
+    if mask.dtype == torch.bool:
+        mask = mask.view(torch.uint8)
+    _want(mask, "mask", (torch.uint8,), ndim=4, contiguous=True)
+    B, H, T, T2 = mask.shape
+    if T2 != T:
+        raise ValueError("mask must be square over the tiles")
+    _want(valid, "valid", (torch.int32,), shape=(T,), contiguous=True)
+    _need_cuda(mask, valid)
+    nb = (T * (tile // 64) + 1) // 2
+    dev = mask.device
+    idx = torch.empty((B, H, nb, nb), dtype=torch.int32, device=dev)
+    counts = torch.empty((B, H, nb), dtype=torch.int32, device=dev)
+    kv = torch.empty((2 * nb,), dtype=torch.int32, device=dev)
+    quad = torch.empty((B, H, nb, nb), dtype=torch.uint8, device=dev) if quadrants and tile == 64 else None
+    _check(load().vsa_tile_mask_to_block_lists(mask.data_ptr(), valid.data_ptr(), B, H, T, tile, idx.data_ptr(),
+                                               counts.data_ptr(), kv.data_ptr(), _ptr(quad), _stream(mask)))
+    return idx, counts, kv, quad

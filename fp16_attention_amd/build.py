@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa16attn.so")
-SOURCES = ["abi.cpp", "attn_fwd.hip", "e4m3_bridge.hip", "noalloc.hip", "prefix_fp8.hip", "vsa_select.hip"]
+SOURCES = ["abi.cpp", "attn_fwd.hip", "e4m3_bridge.hip", "noalloc.hip", "prefix_fp8.hip", "vsa_lists.hip",
+           "vsa_select.hip"]
 # The measurement aid (FP16 MFMA ceiling) is a library of its own, so that the
 # attention library exports only the method's entry points.
 MEASURE_CSRC = os.path.join(HERE, "measure_csrc")

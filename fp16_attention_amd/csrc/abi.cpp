@@ -585,4 +585,42 @@ int vsa_block_sparse_attn(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, co
     return hip_status(fa::launch_merge(m, D, (hipStream_t)stream));
 }
 
+int vsa_tile_means(const uint16_t* x, int B, int H, int L, int D, int block, float* out, void* stream)
+{
+    if (!x || !out) return FA_ERR_NULL;
+    if (D != 128 || block != 64) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || L < 1) return FA_ERR_SHAPE;
+    if (((uintptr_t)x & 15u) || ((uintptr_t)out & 15u)) return FA_ERR_ALIGN;
+    const int64_t NB = (L + block - 1) / block;
+    if (overlap(span_flat(x, (int64_t)B * H * L * D, 2), span_flat(out, (int64_t)B * H * NB * D, 4)))
+        return FA_ERR_ALIAS;
+    return hip_status(fa::launch_vsa_tile_means(x, B, H, L, D, out, (hipStream_t)stream));
+}
+
+int vsa_tile_mask_to_block_lists(const uint8_t* mask, const int32_t* valid, int B, int H, int T, int tile,
+                                 int32_t* indices, int32_t* counts, int32_t* kv_valid, uint8_t* quadrants,
+                                 void* stream)
+{
+    if (!mask || !valid || !indices || !counts || !kv_valid) return FA_ERR_NULL;
+    if (tile != 64 && tile != 128) return FA_ERR_UNSUPPORTED;
+    if (quadrants && tile != 64) return FA_ERR_UNSUPPORTED;  // quadrant masks belong to 64-token tiles
+    if (B < 1 || H < 1 || T < 1 || T * (tile / 64) > 1024) return FA_ERR_SHAPE;
+    if (((uintptr_t)valid & 3u) || ((uintptr_t)indices & 3u) || ((uintptr_t)counts & 3u) ||
+        ((uintptr_t)kv_valid & 3u))
+        return FA_ERR_ALIGN;
+    const int64_t NB = (T * (tile / 64) + 1) / 2;
+    const int64_t lists = (int64_t)B * H * NB * NB;
+    Span in[2] = {span_flat(mask, (int64_t)B * H * T * T, 1), span_flat(valid, T, 4)};
+    Span outs[4] = {span_flat(indices, lists, 4), span_flat(counts, (int64_t)B * H * NB, 4),
+                    span_flat(kv_valid, 2 * NB, 4), quadrants ? span_flat(quadrants, lists, 1) : Span{0, 0}};
+    for (int i = 0; i < 4; ++i) {
+        for (const Span& s : in)
+            if (overlap(outs[i], s)) return FA_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return FA_ERR_ALIAS;
+    }
+    return hip_status(fa::launch_vsa_block_lists(mask, valid, B, H, T, tile, indices, counts, kv_valid, quadrants,
+                                                 (hipStream_t)stream));
+}
+
 }  // extern "C"

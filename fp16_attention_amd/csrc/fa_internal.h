@@ -105,4 +105,13 @@ hipError_t launch_vsa_select(const uint16_t* q, const uint16_t* k, int B, int H,
                              int topk, int32_t* idx_out, double* scores, float* pooled,
                              hipStream_t stream);
 
+// Pooled FP32 tile means [B*H*NB][D] of x [B,H,L,D] FP16 (64-row tiles).
+hipError_t launch_vsa_tile_means(const uint16_t* x, int B, int H, int L, int D, float* out, hipStream_t stream);
+
+// 128-token block lists from a [B,H,T,T] tile mask over tiles of `tile`
+// tokens: idx [B,H,NB,NB], counts [B,H,NB], kv_valid [2*NB], quad (nullable).
+hipError_t launch_vsa_block_lists(const uint8_t* mask, const int32_t* valid, int B, int H, int T, int tile,
+                                  int32_t* idx, int32_t* counts, int32_t* kv_valid, uint8_t* quad,
+                                  hipStream_t stream);
+
 }  // namespace fa

@@ -267,6 +267,20 @@ __global__ __launch_bounds__(256) void vsa_topk_kernel(const double* __restrict_
     }
 }
 
+// The pooled tile means of one tensor (the pooled V of the VSA coarse
+// branch): the pooling kernel with only its first (y = 0) input.
+hipError_t launch_vsa_tile_means(const uint16_t* x, int B, int H, int L, int D, float* out, hipStream_t stream)
+{
+    if (D != kD) return hipErrorInvalidValue;
+    const int NB = (L + kBlock - 1) / kBlock;
+    const int64_t n_bhb = (int64_t)B * H * NB;
+    if (n_bhb <= 0) return hipSuccess;
+    if ((n_bhb + 3) / 4 > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(vsa_pool_kernel, dim3((unsigned)((n_bhb + 3) / 4), 1), dim3(256), 0, stream, x, x, n_bhb, L,
+                       NB, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_vsa_select(const uint16_t* q, const uint16_t* k, int B, int H, int L, int D,
                              int topk, int32_t* idx_out, double* scores, float* pooled,
                              hipStream_t stream)

@@ -261,6 +261,38 @@ int vsa_block_select(const uint16_t* q, const uint16_t* k, int B, int H, int L, 
                      size_t workspace_bytes, void* stream);
 
 /*
+ * Pooled tile means ([P5] kv_pool.py: the FP32 value tile means, the tile's
+ * valid-row sum divided by its valid count with one rounding; the same means
+ * as vsa_block_select's): out[b,h,t,:] = RNE32(sum of the tile's rows / their
+ * count) over tiles of `block` rows, the last holding L - (NB - 1) * block.
+ * Used for the pooled V of the VSA coarse branch.
+ * x: FP16 [B,H,L,D] contiguous; out: FP32 [B,H,NB,D] contiguous, NB =
+ * ceil(L / block). Domain: D == 128; block == 64; B, H, L >= 1.
+ */
+int vsa_tile_means(const uint16_t* x, int B, int H, int L, int D, int block, float* out, void* stream);
+
+/*
+ * VSA 128-token block lists from a tile mask ([P5] block_lists.py,
+ * tile_mask_to_fp4_blocks). mask: uint8 [B,H,T,T] contiguous, nonzero when
+ * query tile i attends to key tile j; tiles hold `tile` = 64 * HT tokens
+ * (64 or 128); valid: int32 [T], the valid tokens of each tile. The sequence
+ * splits into 64-token halves (T * HT) and blocks of two halves,
+ * NB = ceil(T * HT / 2). With va = clamp(valid[a / HT] - (a % HT) * 64, 0, 64)
+ * for half a (0 past the sequence) and m(q, k) = mask[q / HT][k / HT] (a
+ * padded odd last query half sees key half 0 only), query block r (halves
+ * 2r, 2r+1) and key block c (halves a = 2c, e = 2c+1) have the quadrant mask
+ *   [m(2r,a) & va>0] + 2 [m(2r,e) & ve>0] + 4 [m(2r+1,a) & va>0] + 8 [m(2r+1,e) & ve>0].
+ * Outputs: indices int32 [B,H,NB,NB]: per (b, h, r) the key blocks with a
+ * nonzero mask in descending order, then zeros; counts int32 [B,H,NB]: their
+ * number; kv_valid int32 [2 * NB]: va per half; quadrants uint8 [B,H,NB,NB]
+ * (optional, 64-token tiles only): the masks in list order, then zeros.
+ * Domain: tile in {64, 128}; B, H, T >= 1; T * tile / 64 <= 1024.
+ */
+int vsa_tile_mask_to_block_lists(const uint8_t* mask, const int32_t* valid, int B, int H, int T, int tile,
+                                 int32_t* indices, int32_t* counts, int32_t* kv_valid, uint8_t* quadrants,
+                                 void* stream);
+
+/*
  * VSA block-sparse attention ([P3] Purpose). Query block bq = i / block of
  * head h attends to the keys of the blocks idx[b,h,bq,0..topk) when
  * bq >= dense_prefix_qblocks, and to every key when bq < dense_prefix_qblocks.

@@ -371,3 +371,33 @@ def test_noalloc_decode_rejects_before_any_hip_call():
     assert call(page_size=16) == fa.FA_ERR_UNSUPPORTED
     assert call(ks=float("nan")) == fa.FA_ERR_SHAPE
     assert call(kc=B_ + 4) == fa.FA_ERR_ALIGN
+
+
+def test_block_list_and_tile_mean_rejections():
+    lib = fa.load()
+
+    def lists(**kw):
+        a = dict(mask=A, valid=B_, T=576, tile=64, idx=O, counts=C, kv=L, quad=W)
+        a.update(kw)
+        return lib.vsa_tile_mask_to_block_lists(a["mask"], a["valid"], 1, 8, a["T"], a["tile"], a["idx"],
+                                                a["counts"], a["kv"], a["quad"], None)
+    assert lists(mask=0) == fa.FA_ERR_NULL
+    assert lists(tile=96) == fa.FA_ERR_UNSUPPORTED
+    assert lists(tile=128) == fa.FA_ERR_UNSUPPORTED      # quadrant masks only for 64-token tiles
+    assert lists(T=0) == fa.FA_ERR_SHAPE
+    assert lists(T=1025) == fa.FA_ERR_SHAPE
+    assert lists(tile=128, T=513, quad=0) == fa.FA_ERR_SHAPE
+    assert lists(counts=C + 2) == fa.FA_ERR_ALIGN
+    assert lists(counts=O + 64) == fa.FA_ERR_ALIAS       # counts inside the index lists
+    assert lists(idx=A) == fa.FA_ERR_ALIAS                # lists over the mask
+
+    def means(**kw):
+        a = dict(x=A, out=O, D=128, block=64, L=1000)
+        a.update(kw)
+        return lib.vsa_tile_means(a["x"], 1, 2, a["L"], a["D"], a["block"], a["out"], None)
+    assert means(x=0) == fa.FA_ERR_NULL
+    assert means(D=256) == fa.FA_ERR_UNSUPPORTED
+    assert means(block=128) == fa.FA_ERR_UNSUPPORTED
+    assert means(L=0) == fa.FA_ERR_SHAPE
+    assert means(out=O + 4) == fa.FA_ERR_ALIGN
+    assert means(out=A + 256) == fa.FA_ERR_ALIAS
