@@ -42,6 +42,9 @@ def _load():
         lib.or_f32_to_e4m3.argtypes = [ctypes.c_float]
         lib.or_f32_to_bf16.restype = ctypes.c_uint16
         lib.or_f32_to_bf16.argtypes = [ctypes.c_float]
+        lib.or_fp8_quantize_rows.restype = None
+        lib.or_fp8_quantize_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                             ctypes.c_void_p]
         lib.or_prefix_fp8_gather.restype = None
         lib.or_prefix_fp8_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 4 + [
             ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
@@ -159,6 +162,24 @@ def prefix_fp8_gather(k: np.ndarray, v: np.ndarray, index: np.ndarray):
     return ko, vo
 
 
+def fp8_quantize_rows(x: np.ndarray):
+    """Per-row E4M3 quantization of bfloat16 bit patterns x [..., D]: returns (codes uint8
+    [..., D], scales float32 [...]) with scale = max|x| / 448 (the round trip's first steps)."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    D = x.shape[-1]
+    rows = x.size // D
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[:-1], dtype=np.float32)
+    lib.or_fp8_quantize_rows(_ptr(x), rows, D, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def fp8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """float64 decode(code) * scale, exact (a 4-bit E4M3 significand times an FP32 scale)."""
+    return e4m3_decode_table()[codes] * scales.astype(np.float64)[..., None]
+
+
 def paged_gather(cache: np.ndarray, table: np.ndarray, kv_len: int) -> np.ndarray:
     """cache uint8 [pages, page_size, Hkv, D], table int32 [B, pages_per_seq]
     -> contiguous uint8 [B, Hkv, kv_len, D]."""
@@ -190,6 +211,7 @@ def attention(q, k, v, scale: float, mode: int = MODE_DENSE, offset: int = 0, id
     """FP64 attention of FP16 q [B,Hq,Lq,D], k/v [B,Hkv,Lkv,D] (any D-contiguous strides).
 
     bf16: the arrays are uint16 bit patterns of bfloat16 values instead.
+    float64 arrays (all three) are used as they are.
     rows: int32 [n,3] (b, h, i) triples to compute (default: all rows).
     Returns (out float64 [n, D], lse float64 [n]) in the order of rows.
     """
@@ -197,7 +219,10 @@ def attention(q, k, v, scale: float, mode: int = MODE_DENSE, offset: int = 0, id
     q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
-    want = np.uint16 if bf16 else np.float16
+    if q.dtype == np.float64:
+        fmt, want = 2, np.float64
+    else:
+        fmt, want = (1, np.uint16) if bf16 else (0, np.float16)
     for name, a in (("q", q), ("k", k), ("v", v)):
         if a.dtype != want or a.ndim != 4:
             raise TypeError(f"{name} must be a 4-D {np.dtype(want).name} array")
@@ -218,7 +243,7 @@ def attention(q, k, v, scale: float, mode: int = MODE_DENSE, offset: int = 0, id
     rc = lib.or_attention(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), B, Hq, Hkv,
                           Lq, Lkv, D, float(scale), mode, int(offset),
                           _ptr(idx_arr) if idx_arr is not None else None, block, topk, dense_prefix,
-                          _ptr(rows), n, _ptr(out), _ptr(lse), _threads(threads), int(bool(bf16)))
+                          _ptr(rows), n, _ptr(out), _ptr(lse), _threads(threads), fmt)
     if rc:
         raise ValueError("invalid oracle arguments")
     return out, lse

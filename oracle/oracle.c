@@ -189,30 +189,57 @@ uint16_t or_f32_to_bf16(float x)
  * each operation rounding once in FP32; vo is V's row copied. Outputs are
  * [B, rows, H, D] bfloat16.
  */
+/* The per-row E4M3 quantization of the round trip: x holds D bfloat16 values;
+ * scale = max |x| / 448 (FP32), inv = scale == 0 ? 0 : 1 / scale,
+ * codes[d] = RNE_e4m3(clamp(x[d] * inv, +-448)), each step rounding once in
+ * FP32. Returns scale. */
+static float or_fp8_row(const uint16_t* x, int D, uint8_t* codes)
+{
+    volatile float amax = 0.0f;
+    for (int d = 0; d < D; ++d) {
+        float a = fabsf((float)or_bf16_to_f64(x[d]));
+        if (a > amax)
+            amax = a;
+    }
+    volatile float scale = amax / 448.0f;
+    volatile float inv = scale == 0.0f ? 0.0f : 1.0f / scale;
+    for (int d = 0; d < D; ++d) {
+        volatile float y = (float)or_bf16_to_f64(x[d]) * inv;
+        float c = y < -448.0f ? -448.0f : (y > 448.0f ? 448.0f : y);
+        codes[d] = or_f32_to_e4m3(c);
+    }
+    return scale;
+}
+
 void or_prefix_fp8_gather(const uint16_t* k, const uint16_t* v, int B, int N, int H, int D,
                           const int32_t* index, int rows, uint16_t* ko, uint16_t* vo)
 {
+    uint8_t* codes = (uint8_t*)malloc((size_t)D);
     for (int b = 0; b < B; ++b)
         for (int r = 0; r < rows; ++r)
             for (int h = 0; h < H; ++h) {
                 const int64_t src = (((int64_t)b * N + index[r]) * H + h) * D;
                 const int64_t dst = (((int64_t)b * rows + r) * H + h) * D;
-                volatile float amax = 0.0f;
+                const float scale = or_fp8_row(k + src, D, codes);
                 for (int d = 0; d < D; ++d) {
-                    float a = fabsf((float)or_bf16_to_f64(k[src + d]));
-                    if (a > amax)
-                        amax = a;
-                }
-                volatile float scale = amax / 448.0f;
-                volatile float inv = scale == 0.0f ? 0.0f : 1.0f / scale;
-                for (int d = 0; d < D; ++d) {
-                    volatile float x = (float)or_bf16_to_f64(k[src + d]) * inv;
-                    float c = x < -448.0f ? -448.0f : (x > 448.0f ? 448.0f : x);
-                    volatile float y = (float)or_e4m3_decode(or_f32_to_e4m3(c)) * scale;
+                    volatile float y = (float)or_e4m3_decode(codes[d]) * scale;
                     ko[dst + d] = or_f32_to_bf16(y);
                     vo[dst + d] = v[src + d];
                 }
             }
+    free(codes);
+}
+
+/*
+ * E4M3 quantization of rows of D bfloat16 values with a per-row amax / 448
+ * scale ([P5] query_pool.py, the PREFIX_FP8 round trip of the prefix
+ * queries; prefix_quant.py, the same for the prefix keys): codes [rows][D]
+ * and scales [rows], the steps of or_fp8_row.
+ */
+void or_fp8_quantize_rows(const uint16_t* x, int64_t rows, int D, uint8_t* codes, float* scales)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        scales[r] = or_fp8_row(x + r * D, D, codes + r * D);
 }
 
 /*
@@ -258,9 +285,9 @@ int or_paged_gather(const uint8_t* cache, int64_t num_pages, int page_size, cons
 /* ------------------------------------------------------------------------ */
 
 typedef struct {
-    const uint16_t* q;
-    const uint16_t* k;
-    const uint16_t* v;
+    const void* q;
+    const void* k;
+    const void* v;
     int64_t qs[3], ks[3], vs[3]; /* element strides (batch, head, row); D stride 1 */
     int B, Hq, Hkv, Lq, Lkv, D;
     double scale;
@@ -272,10 +299,19 @@ typedef struct {
     int64_t n_rows;
     double* out; /* [n_rows, D] */
     double* lse; /* [n_rows] */
-    double (*elem)(uint16_t); /* q, k, v element format: FP16 or BF16 */
+    int fmt; /* q, k, v element format: 0 FP16, 1 BF16, 2 FP64 */
     int64_t next;
     pthread_mutex_t lock;
 } attn_job;
+
+/* element i (an element offset) of an operand in the job's format */
+static double elem(const attn_job* J, const void* base, int64_t i)
+{
+    if (J->fmt == 2)
+        return ((const double*)base)[i];
+    const uint16_t h = ((const uint16_t*)base)[i];
+    return J->fmt == 1 ? or_bf16_to_f64(h) : or_f16_to_f64(h);
+}
 
 static int64_t claim(attn_job* J)
 {
@@ -329,16 +365,16 @@ static void* attn_worker(void* arg)
             break;
         int b = J->rows[3 * r], h = J->rows[3 * r + 1], i = J->rows[3 * r + 2];
         int g = h / group;
-        const uint16_t* qrow = J->q + b * J->qs[0] + h * J->qs[1] + (int64_t)i * J->qs[2];
+        const int64_t qrow = b * J->qs[0] + h * J->qs[1] + (int64_t)i * J->qs[2];
         for (int d = 0; d < D; ++d)
-            qd[d] = J->elem(qrow[d]);
+            qd[d] = elem(J, J->q, qrow + d);
         int64_t n = keys_of_row(J, b, h, i, keys);
         double m = -INFINITY;
         for (int64_t t = 0; t < n; ++t) {
-            const uint16_t* krow = J->k + b * J->ks[0] + g * J->ks[1] + keys[t] * J->ks[2];
+            const int64_t krow = b * J->ks[0] + g * J->ks[1] + keys[t] * J->ks[2];
             double dot = 0.0;
             for (int d = 0; d < D; ++d)
-                dot += qd[d] * J->elem(krow[d]);
+                dot += qd[d] * elem(J, J->k, krow + d);
             s[t] = J->scale * dot;
             if (s[t] > m)
                 m = s[t];
@@ -349,9 +385,9 @@ static void* attn_worker(void* arg)
         for (int64_t t = 0; t < n; ++t) {
             double p = exp(s[t] - m);
             denom += p;
-            const uint16_t* vrow = J->v + b * J->vs[0] + g * J->vs[1] + keys[t] * J->vs[2];
+            const int64_t vrow = b * J->vs[0] + g * J->vs[1] + keys[t] * J->vs[2];
             for (int d = 0; d < D; ++d)
-                acc[d] += p * J->elem(vrow[d]);
+                acc[d] += p * elem(J, J->v, vrow + d);
         }
         for (int d = 0; d < D; ++d)
             J->out[r * D + d] = acc[d] / denom;
@@ -364,13 +400,13 @@ static void* attn_worker(void* arg)
     return NULL;
 }
 
-/* Returns 0, or -1 for an invalid argument. bf16: q, k, v hold bfloat16
-   values instead of FP16. */
-int or_attention(const uint16_t* q, const int64_t* qs, const uint16_t* k, const int64_t* ks,
-                 const uint16_t* v, const int64_t* vs, int B, int Hq, int Hkv, int Lq, int Lkv,
+/* Returns 0, or -1 for an invalid argument. fmt: the element format of q, k
+   and v: 0 FP16, 1 bfloat16 (both as 16-bit patterns), 2 FP64 values. */
+int or_attention(const void* q, const int64_t* qs, const void* k, const int64_t* ks,
+                 const void* v, const int64_t* vs, int B, int Hq, int Hkv, int Lq, int Lkv,
                  int D, double scale, int mode, int64_t offset, const int32_t* idx, int block,
                  int topk, int dense_prefix, const int32_t* rows, int64_t n_rows, double* out,
-                 double* lse, int threads, int bf16)
+                 double* lse, int threads, int fmt)
 {
     if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || (mode == 2 && (block <= 0 || !idx)))
         return -1;
@@ -399,7 +435,9 @@ int or_attention(const uint16_t* q, const int64_t* qs, const uint16_t* k, const 
     J.n_rows = n_rows;
     J.out = out;
     J.lse = lse;
-    J.elem = bf16 ? or_bf16_to_f64 : or_f16_to_f64;
+    if (fmt < 0 || fmt > 2)
+        return -1;
+    J.fmt = fmt;
     J.next = 0;
     pthread_mutex_init(&J.lock, NULL);
     if (threads < 1)

@@ -217,3 +217,19 @@ def test_row_subset_matches_full_run():
     sub, lse = oracle.attention(q, k, v, 0.3, rows=rows)
     flat = rows[:, 1] * 40 + rows[:, 2]
     assert np.array_equal(sub, full[flat]) and np.array_equal(lse, lse_full[flat])
+
+
+def test_float64_operands_match_torch_sdpa():
+    """FP64 operands (the FP8 path's dequantized queries and keys) against
+    torch float64 scaled_dot_product_attention, dense and causal."""
+    rng = np.random.default_rng(41)
+    q = rng.standard_normal((1, 3, 21, 64)) * 3.0
+    k = rng.standard_normal((1, 3, 40, 64))
+    v = rng.standard_normal((1, 3, 40, 64))
+    out, lse = oracle.attention(q, k, v, 0.125)
+    ref = _sdpa(q, k, v, 0.125)
+    assert np.abs(out.reshape(ref.shape) - ref).max() < 1e-12
+    mask = np.arange(40)[None, :] <= (40 - 21) + np.arange(21)[:, None]
+    out_c, _ = oracle.attention(q, k, v, 0.125, mode=oracle.MODE_CAUSAL, offset=40 - 21)
+    ref_c = _sdpa(q, k, v, 0.125, mask)
+    assert np.abs(out_c.reshape(ref_c.shape) - ref_c).max() < 1e-12

@@ -188,3 +188,29 @@ def test_prefix_fp8_gather_matches_torch_dtype_casts():
     ref = (q8 * scale).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(ko, ref)
     assert np.array_equal(vo, vb[:, index])
+
+
+def test_fp8_quantize_rows_matches_torch_dtype_casts():
+    """The per-row E4M3 quantization (prefix queries and keys) against torch
+    float32 arithmetic and its float8_e4m3fn cast; its dequantized values,
+    rounded to bfloat16, are the round trip's output."""
+    rng = np.random.default_rng(29)
+    t = torch.from_numpy(rng.standard_normal((3, 50, 128)) * rng.uniform(0.01, 40, (3, 50, 1))).to(torch.bfloat16)
+    t[1, 7] = 0  # an all-zero row: scale 0, codes 0
+    xb = t.view(torch.int16).numpy().view(np.uint16)
+    codes, scales = oracle.fp8_quantize_rows(xb)
+    x = t.float()
+    scale = x.abs().amax(-1, keepdim=True) / 448.0
+    inv = torch.where(scale == 0, torch.zeros_like(scale), 1.0 / scale)
+    q8 = torch.clamp(x * inv, -448.0, 448.0).to(torch.float8_e4m3fn)
+    assert np.array_equal(codes, q8.view(torch.uint8).numpy())
+    assert np.array_equal(scales, scale[..., 0].numpy())
+    assert scales[1, 7] == 0 and not codes[1, 7].any()
+    # the dequantized values, exact in float64, equal the FP8 round trip before its bfloat16 storage
+    deq = oracle.fp8_dequant(codes, scales)
+    assert np.array_equal(deq, (q8.double() * scale.double()).numpy())
+    # ... and rounded to bfloat16 they are the prefix round trip's keys
+    ko, _ = oracle.prefix_fp8_gather(xb.reshape(1, 3 * 50, 1, 128), xb.reshape(1, 3 * 50, 1, 128),
+                                     np.arange(150, dtype=np.int32))
+    ref = torch.from_numpy(deq).float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ko.reshape(3, 50, 128), ref)
