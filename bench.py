@@ -20,6 +20,8 @@ path, each timed with HIP events on the launch stream:
     E4M3 cache, GB/s over the cache read once (HBM-bound);
   * the FP8 round trip of prefix keys with the valid-row gather (B1 N36864
     H8, 32768 rows), GB/s over K and V rows read and written;
+  * the FP8-MFMA prefix attention (per-row E4M3 queries and keys, BF16 V) at
+    the video shape, TFLOP/s and its fraction of the mixed FP8/BF16 peak;
   * VSA block selection (pool, score, top-k), GB/s over Q and K read once
     plus the indices written, and VSA block-sparse attention, TFLOP/s over
     the selected pairs.
@@ -201,6 +203,35 @@ def bench_ragged(fa, torch, iters, timer):
     return res, bf
 
 
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published
+
+
+def bench_prefix_fp8_attn(fa, torch, iters, timer):
+    """The FP8-MFMA prefix attention (per-row E4M3 queries and keys, BF16 values) at the
+    video shape: B1 H8 D128 Lq = Lkv = 36864, the dense workload's draws rounded to BF16.
+    Half of the algorithmic FLOPs (QK^T) run at the FP8 rate, half (PV) at the BF16 rate,
+    so the mixed peak is 1 / (0.5 / 5.0 + 0.5 / 2.5) PFLOP/s = 3.33 PFLOP/s. The timed call
+    includes the per-row quantization of Q and K."""
+    import synth.workloads as wl
+    w = wl.VIDEO_DENSE
+    log("generating", w["name"], "(BF16 operands for the FP8 prefix path)")
+    q, k, v = wl.dense_inputs(w)
+    dq, dk, dv = (torch.from_numpy(x).cuda().to(torch.bfloat16) for x in (q, k, v))
+    del q, k, v
+    out = torch.empty_like(dq)
+    ws = torch.empty(fa.prefix_fp8_workspace(w["B"], w["H"], w["Lq"], w["Lkv"]), dtype=torch.uint8, device="cuda")
+    ms, _ = timer.run(lambda: fa.attn_fwd_prefix_fp8(dq, dk, dv, out=out, workspace=ws), iters, 2)
+    f = dense_flops(w)
+    tf = f / (np.median(ms) * 1e-3) / 1e12
+    mixed_peak = 1.0 / (0.5 / FP8_PEAK_TFLOPS + 0.5 / MFMA_F16_PEAK_TFLOPS)
+    log(f"prefix fp8 attention: {np.median(ms):.3f} ms  {tf:.1f} TFLOP/s = {100 * tf / mixed_peak:.1f}% of "
+        f"the mixed FP8/BF16 peak")
+    return {"workload": "FP8-QK prefix attention B1 H8 D128 Lq36864 Lkv36864, BF16 operands, per-row E4M3 Q and K "
+                        "(quantization included)", "flop": f, **stats(ms), "tflops": tf,
+            "peak_tflops": mixed_peak, "frac_mixed_peak": tf / mixed_peak,
+            "frac_fp16_peak": tf / MFMA_F16_PEAK_TFLOPS}
+
+
 def bench_causal(fa, torch, iters, timer):
     import synth.workloads as wl
     w = wl.PREFIX_CAUSAL
@@ -380,7 +411,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--iters", type=int, default=10, help="timed launches of each extra workload")
-    ap.add_argument("--only", choices=["dense", "causal", "ragged", "paged", "prefix", "vsa", "copy", "ceiling"], default=None,
+    ap.add_argument("--only", choices=["dense", "causal", "ragged", "paged", "prefix", "fp8", "vsa", "copy", "ceiling"],
+                    default=None,
                     help="run one workload only (for profiling); 'copy' runs the plain 1 GiB "
                          "device copy that calibrates the HBM byte counters")
     ap.add_argument("--no-extra", action="store_true", help="skip the non-headline workloads")
@@ -482,6 +514,9 @@ def main():
             extra["paged_e4m3"], extra["e4m3_bridge"], extra["paged_e4m3_decode"] = bench_paged(
                 fa, torch, args.iters, timer, flush)
             torch.cuda.empty_cache()
+        if args.only in (None, "fp8"):
+            extra["prefix_fp8_attention"] = bench_prefix_fp8_attn(fa, torch, args.iters, timer)
+            torch.cuda.empty_cache()
         if args.only in (None, "prefix"):
             extra["prefix_fp8_gather"] = bench_prefix_fp8(fa, torch, args.iters, timer, flush)
             torch.cuda.empty_cache()
@@ -494,7 +529,7 @@ def main():
         return
     # FP16 MFMA-bound workloads against the same measured (FP16) ceiling as the headline
     for rec in extra.values():
-        if "tflops" in rec and "BF16" not in rec["workload"]:
+        if "tflops" in rec and "BF16" not in rec["workload"] and "peak_tflops" not in rec:
             rec["frac_of_measured_ceiling"] = rec["tflops"] / result["mfma_ceiling"]["value"]
     result["extra"] = extra
     result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),

@@ -21,6 +21,7 @@ FA_ERR_HIP = 1000
 
 # Every symbol include/fa16attn.h declares.
 EXPORTS = ("fa_abi_version", "fa_error_string", "attn_fwd_dense", "attn_fwd_dense_bf16",
+           "attn_fwd_prefix_fp8_workspace", "attn_fwd_prefix_fp8",
            "attn_fwd_prefix_causal_workspace",
            "attn_fwd_prefix_causal", "attn_fwd_paged_e4m3_workspace", "attn_fwd_paged_e4m3",
            "attn_fwd_paged_e4m3_decode_workspace", "attn_fwd_paged_e4m3_decode",
@@ -49,6 +50,8 @@ _SIGS = {
     "fa_error_string": (ctypes.c_char_p, [_i]),
     "attn_fwd_dense": (_i, [FaTensor] * 4 + [_vp] + [_i] * 5 + [_f, _vp]),
     "attn_fwd_dense_bf16": (_i, [FaTensor] * 4 + [_vp] + [_i] * 5 + [_f, _vp]),
+    "attn_fwd_prefix_fp8_workspace": (_sz, [_i] * 5),
+    "attn_fwd_prefix_fp8": (_i, [FaTensor] * 4 + [_vp] + [_i] * 5 + [_f, _vp, _sz, _vp]),
     "attn_fwd_prefix_causal_workspace": (_sz, [_i] * 6),
     "attn_fwd_prefix_causal": (_i, [FaTensor] * 4 + [_vp] + [_i] * 7 + [_f, _vp, _sz, _vp]),
     "attn_fwd_paged_e4m3_workspace": (_sz, [_i] * 6),
@@ -193,6 +196,33 @@ def attn_fwd_dense(q, k, v, out=None, lse=None, scale=None):
     scale = default_scale(D) if scale is None else scale
     fn = load().attn_fwd_dense_bf16 if dt == torch.bfloat16 else load().attn_fwd_dense
     _check(fn(_view(q), _view(k), _view(v), _view(out), _ptr(lse), B, H, Lq, Lkv, D, scale, _stream(q)))
+    return out
+
+
+def prefix_fp8_workspace(B, H, Lq, Lkv, D=128) -> int:
+    return int(load().attn_fwd_prefix_fp8_workspace(B, H, Lq, Lkv, D))
+
+
+def attn_fwd_prefix_fp8(q, k, v, out=None, lse=None, scale=None, workspace=None):
+    """Dense attention with FP8 (E4M3, per-row amax/448 scale) queries and keys on the FP8
+    matrix cores; q [B,H,Lq,128], k/v [B,H,Lkv,128] bfloat16 -> out bfloat16."""
+    import torch
+    bf = (torch.bfloat16,)
+    _want(q, "q", bf, ndim=4, unit_d=True)
+    B, H, Lq, D = q.shape
+    _want(k, "k", bf, ndim=4, unit_d=True)
+    Lkv = k.shape[2]
+    _want(k, "k", bf, shape=(B, H, Lkv, D))
+    _want(v, "v", bf, shape=(B, H, Lkv, D), unit_d=True)
+    _want(out, "out", bf, shape=(B, H, Lq, D), unit_d=True)
+    _lse_shape_ok(lse, (B, H, Lq))
+    _need_cuda(q, k, v, out, lse)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    scale = default_scale(D) if scale is None else scale
+    ws = _workspace(prefix_fp8_workspace(B, H, Lq, Lkv, D), q.device, workspace)
+    _check(load().attn_fwd_prefix_fp8(_view(q), _view(k), _view(v), _view(out), _ptr(lse), B, H, Lq, Lkv, D, scale,
+                                      _ptr(ws), _nbytes(ws), _stream(q)))
     return out
 
 

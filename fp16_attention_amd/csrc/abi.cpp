@@ -623,4 +623,77 @@ int vsa_tile_mask_to_block_lists(const uint8_t* mask, const int32_t* valid, int 
                                                  (hipStream_t)stream));
 }
 
+// Workspace of attn_fwd_prefix_fp8: the E4M3 codes of Q [B,H,Lq,D] and K
+// [B,H,Lkv,D] (each 256-byte aligned), then their FP32 row scales.
+static size_t fp8_codes_bytes(int64_t rows, int D) { return ((size_t)rows * D + 255) & ~(size_t)255; }
+static size_t fp8_scales_bytes(int64_t rows) { return ((size_t)rows * 4 + 255) & ~(size_t)255; }
+
+size_t attn_fwd_prefix_fp8_workspace(int B, int H, int Lq, int Lkv, int D)
+{
+    if (D != 128 || B < 1 || H < 1 || Lq < 1 || Lkv < 1) return 0;
+    const int64_t bh = (int64_t)B * H;
+    return fp8_codes_bytes(bh * Lq, D) + fp8_codes_bytes(bh * Lkv, D) + fp8_scales_bytes(bh * Lq) +
+           fp8_scales_bytes(bh * Lkv);
+}
+
+int attn_fwd_prefix_fp8(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse, int B, int H, int Lq,
+                        int Lkv, int D, float scale, void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc;
+    if ((rc = check_view(q)) || (rc = check_view(k)) || (rc = check_view(v)) || (rc = check_view(o)))
+        return rc;
+    if (D != 128) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || Lq < 0 || Lkv < 1) return FA_ERR_SHAPE;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SHAPE;
+    if (Lq == 0) return FA_OK;
+    Span in[3] = {span_of(q.data, q.stride_b, q.stride_h, q.stride_s, B, H, Lq, D, 2),
+                  span_of(k.data, k.stride_b, k.stride_h, k.stride_s, B, H, Lkv, D, 2),
+                  span_of(v.data, v.stride_b, v.stride_h, v.stride_s, B, H, Lkv, D, 2)};
+    Span so = span_of(o.data, o.stride_b, o.stride_h, o.stride_s, B, H, Lq, D, 2);
+    Span sl = lse ? span_flat(lse, (int64_t)B * H * Lq, 4) : Span{0, 0};
+    for (const Span& s : in) {
+        if (overlap(so, s)) return FA_ERR_ALIAS;
+        if (lse && overlap(sl, s)) return FA_ERR_ALIAS;
+    }
+    if (lse && overlap(sl, so)) return FA_ERR_ALIAS;
+    const size_t need = attn_fwd_prefix_fp8_workspace(B, H, Lq, Lkv, D);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 255u) return FA_ERR_ALIGN;
+    Span ws = span_flat(workspace, (int64_t)need, 1);
+    for (const Span& s : in)
+        if (overlap(ws, s)) return FA_ERR_ALIAS;
+    if (overlap(ws, so) || (lse && overlap(ws, sl))) return FA_ERR_ALIAS;
+
+    const int64_t bh = (int64_t)B * H;
+    uint8_t* qc = (uint8_t*)workspace;
+    uint8_t* kc = qc + fp8_codes_bytes(bh * Lq, D);
+    float* qsc = (float*)(kc + fp8_codes_bytes(bh * Lkv, D));
+    float* ksc = (float*)((char*)qsc + fp8_scales_bytes(bh * Lq));
+    hipError_t e = fa::launch_fp8_rows_quantize((const uint16_t*)q.data, q.stride_b, q.stride_h, q.stride_s, B, H, Lq,
+                                                qc, qsc, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+    e = fa::launch_fp8_rows_quantize((const uint16_t*)k.data, k.stride_b, k.stride_h, k.stride_s, B, H, Lkv, kc, ksc,
+                                     (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+
+    AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    fill_view(q, a.q, a.q_sb, a.q_sh, a.q_ss);
+    fill_view(k, a.k, a.k_sb, a.k_sh, a.k_ss);
+    fill_view(v, a.v, a.v_sb, a.v_sh, a.v_ss);
+    a.o = (_Float16*)o.data;
+    a.o_sb = o.stride_b;
+    a.o_sh = o.stride_h;
+    a.o_ss = o.stride_s;
+    a.lse = lse;
+    a.qc = qc;
+    a.qsc = qsc;
+    a.kc = kc;
+    a.ksc = ksc;
+    if (!fa::dense_geometry(a, B, H, Lq, Lkv)) return FA_ERR_SHAPE;
+    a.c = scale * 1.4426950408889634f;
+    a.oscale = 1.f;
+    return hip_status(fa::launch_attn(a, D, fa::KV_FP8QK, fa::KEYS_DENSE, false, (hipStream_t)stream));
+}
+
 }  // extern "C"

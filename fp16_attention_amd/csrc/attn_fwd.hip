@@ -59,6 +59,7 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef float f16x __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef float f2 __attribute__((ext_vector_type(2)));
@@ -305,29 +306,41 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     constexpr int KS = KT / 16;   // 16-key PV k-steps per tile
     constexpr int KK = D / 16;    // MFMA k-steps over D for S
     constexpr int DB = D / 32;    // 32-wide d blocks of O^T
-    // 16-bit K/V (else E4M3 codes, decoded in registers)
-    constexpr bool DIRECT = SRC != KV_E4M3_PAGED && SRC != KV_E4M3_PAGED_SCALED;
+    // FP8 source: Q and K are E4M3 codes with per-row scales (QK^T on the FP8
+    // matrix cores, 32x32x64), V is BF16 and streams as the 16-bit sources do
+    constexpr bool F8 = SRC == KV_FP8QK;
+    // 16-bit V tiles (else E4M3 codes, decoded in registers)
+    constexpr bool VDIRECT = SRC != KV_E4M3_PAGED && SRC != KV_E4M3_PAGED_SCALED;
+    // 16-bit K and V tiles
+    constexpr bool DIRECT = VDIRECT && !F8;
     // The scaled E4M3 source converts each K code tile once per workgroup into
     // an FP16 tile (each wave a quarter of it, between its PV MFMAs), from
     // which every wave reads its K operands as the 16-bit sources do.
     constexpr bool KCONV = SRC == KV_E4M3_PAGED_SCALED;
-    constexpr int ROW = (DIRECT ? 2 : 1) * D;      // bytes per LDS row of the ring slots
+    constexpr int ROW = (VDIRECT ? 2 : 1) * D;      // bytes per LDS row of the V ring slots
+    constexpr int KRROW = (DIRECT ? 2 : 1) * D;     // bytes per LDS row of the K ring slots
     constexpr int KROW = (DIRECT || KCONV ? 2 : 1) * D;  // bytes per row of the K operand tiles
-    constexpr int TB = KT * ROW;
+    constexpr int TB = KT * ROW;                    // V slot bytes
+    constexpr int TBK = KT * KRROW;                 // K slot bytes
     constexpr int R = Tiling<D, SRC, MODE>::R;
     // D = 256: the loads of a ring group are spread over the next iteration's
     // MFMA steps instead of being issued together after the barrier (the
     // tile's bytes then arrive in LDS spread out too; measured 3-4% faster on
     // the causal prefill, neutral at D = 128)
     constexpr bool SPREAD = DIRECT && D == 256;
-    constexpr bool BF = SRC == KV_BF16;
+    // P, the PV product and O in BF16
+    constexpr bool BF = SRC == KV_BF16 || F8;
     constexpr int PH = Tiling<D, SRC, MODE>::PH;
     static_assert(R >= 2 && R <= 4, "ring depth");
-    static_assert(DIRECT || KT == 32, "an E4M3 tile is one 32-token page");
-    __shared__ __attribute__((aligned(1024))) unsigned char kslot0[TB];
-    __shared__ __attribute__((aligned(1024))) unsigned char kslot1[TB];
-    __shared__ __attribute__((aligned(1024))) unsigned char kslot2[R > 2 ? TB : 16];
-    __shared__ __attribute__((aligned(1024))) unsigned char kslot3[R > 3 ? TB : 16];
+    static_assert(VDIRECT || KT == 32, "an E4M3 tile is one 32-token page");
+    static_assert(!F8 || (D == 128 && KT == 64 && R == 2 && MODE == KEYS_DENSE), "FP8 source: dense D128");
+    __shared__ __attribute__((aligned(1024))) unsigned char kslot0[TBK];
+    __shared__ __attribute__((aligned(1024))) unsigned char kslot1[TBK];
+    __shared__ __attribute__((aligned(1024))) unsigned char kslot2[R > 2 ? TBK : 16];
+    __shared__ __attribute__((aligned(1024))) unsigned char kslot3[R > 3 ? TBK : 16];
+    // F8: the FP32 scales of K(j)'s keys, one copy per wave, in kscl(j % R)
+    __shared__ __attribute__((aligned(16))) float kscl0[F8 ? WAVES * KT : 4];
+    __shared__ __attribute__((aligned(16))) float kscl1[F8 ? WAVES * KT : 4];
     __shared__ __attribute__((aligned(1024))) unsigned char vslot0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char vslot1[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char vslot2[R > 2 ? TB : 16];
@@ -337,8 +350,9 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     __shared__ __attribute__((aligned(1024))) unsigned char khalf1[KCONV ? KT * 2 * D : 16];
     // s_waitcnt that leaves the (ring depth - 2) most recent load groups in
     // flight (ring depth - 3 when K is converted a tile earlier)
-    constexpr int kGroupLoads =
-        2 * (DIRECT ? DirectLoader<D, WAVES, KT>::kLoads : ByteLoader<D, WAVES, KT>::kLoads);
+    constexpr int kGroupLoads = (DIRECT ? DirectLoader<D, WAVES, KT>::kLoads : ByteLoader<D, WAVES, KT>::kLoads) +
+                                (VDIRECT ? DirectLoader<D, WAVES, KT>::kLoads : ByteLoader<D, WAVES, KT>::kLoads) +
+                                (F8 ? 1 : 0);
     constexpr int kVmLeft = (R - (KCONV ? 3 : 2)) * kGroupLoads;
     static_assert(kVmLeft < 64, "vmcnt range");
     constexpr int kWaitGroups = (kVmLeft & 15) | ((kVmLeft >> 4) << 14) | 0x0070;  // and lgkmcnt(0)
@@ -384,13 +398,21 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     const int32_t* table = nullptr;
     DirectLoader<D, WAVES, KT> dl;
     ByteLoader<D, WAVES, KT> bl;
-    if (DIRECT) {
+    // F8: K codes and scales of this (b, kv head), contiguous rows of D codes
+    const uint8_t* kcbase = nullptr;
+    const float* kscbase = nullptr;
+    if (VDIRECT) {
         kbase = a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh;
         vbase = a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh;
         dl.init(a.k_ss, a.v_ss, wave, lane);
     } else {
         table = a.table + (int64_t)b * a.table_stride;
         bl.init(a.Hkv * D, wave, lane);
+    }
+    if constexpr (F8) {
+        kcbase = a.kc + ((int64_t)b * a.Hkv + g) * a.Lkv * D;
+        kscbase = a.ksc + ((int64_t)b * a.Hkv + g) * a.Lkv;
+        bl.init(D, wave, lane);
     }
     // Every load group issues the same number of loads, so that s_waitcnt
     // counts stay exact: a tile past the end is loaded with zero valid rows
@@ -409,7 +431,18 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         bl.issue(cache + ((int64_t)page * 32 * a.Hkv + g) * D, rows * a.Hkv * D, slot, wave);
     };
     auto issue_k = [&](int it, unsigned char* slot) {
-        if constexpr (!DIRECT) {
+        if constexpr (F8) {
+            // the tile's codes, and its keys' scales (each wave its own copy of
+            // the KT scales, one dword per lane, in the scale slot of this K slot)
+            const bool ok = it < n_tiles;
+            const int key0 = tile_key0(ok ? it : n_tiles - 1);
+            const int rows = valid_rows(ok, key0);
+            bl.issue(kcbase + (int64_t)key0 * D, rows * D, slot, wave);
+            float* sc = slot == kslot0 ? kscl0 : kscl1;
+            const __amdgpu_buffer_rsrc_t r =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(kscbase + key0), 0, rows * 4, kRsrcWord3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(sc + wave * KT), 4, lane * 4, 0, 0, 0);
+        } else if constexpr (!DIRECT) {
             issue_b(a.kc, it, slot);
         } else {
             const bool ok = it < n_tiles;
@@ -419,7 +452,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         }
     };
     auto issue_v = [&](int it, unsigned char* slot) {
-        if constexpr (!DIRECT) {
+        if constexpr (!VDIRECT) {
             issue_b(a.vc, it, slot);
         } else {
             const bool ok = it < n_tiles;
@@ -442,8 +475,23 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     }
 
     // ---- Q fragment in registers: lane holds Q[row][16kk + 8hlf .. +7] ------
-    h8 qf[KK];
-    {
+    // (F8: codes d = 64kk + 32hlf .. +31 of the row, and its scale folded into
+    // the lane's softmax constant crow)
+    constexpr int KK8 = D / 64;  // FP8 MFMA k-steps over D
+    v8i qf8[F8 ? KK8 : 1];
+    float crow = a.c;
+    h8 qf[F8 ? 1 : KK];
+    if constexpr (F8) {
+        const int row = min(my_row, a.Lq - 1);
+        const int64_t qrow = ((int64_t)b * a.Hq + qh) * a.Lq + row;
+        const uint8_t* qp = a.qc + qrow * D;
+#pragma unroll
+        for (int kk = 0; kk < KK8; ++kk) {
+            const u4 lo = *(const u4*)(qp + 64 * kk + 32 * hlf), hi = *(const u4*)(qp + 64 * kk + 32 * hlf + 16);
+            qf8[kk] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        crow = a.c * a.qsc[qrow];
+    } else {
         int row = min(my_row, a.Lq - 1);
         const _Float16* qp = a.q + (int64_t)b * a.q_sb + (int64_t)qh * a.q_sh + (int64_t)row * a.q_ss;
 #pragma unroll
@@ -469,10 +517,20 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     // element j from source lanes 2j and 2j+1 of its group, column
     // d = 32db + 16(G%2) + t; so source lane s of group G points at 8 codes of
     // key row 4*(G/2) + (s/2)%4 + 8*(s/8), d = 32db + 16(G%2) + 8(s%2).
+    // F8 K operand of the 32x32x64 MFMA: row l32 (+32 per score block), the
+    // 32 codes d = 64kk + 32hlf .. +31 as two 16-code chunks (the query codes
+    // are held in the same d order, so every product pairs equal d).
     const int grp = lane >> 4, sl = lane & 15;
     int koff_s[KK];
+    int koff8[F8 ? KK8 : 1][2];
     int voff_a[DB], voff_b[DB];
-    if constexpr (DIRECT) {
+    if constexpr (F8) {
+#pragma unroll
+        for (int kk = 0; kk < KK8; ++kk)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) koff8[kk][c] = btile_off<D>(l32, 64 * kk + 32 * hlf + 16 * c);
+    }
+    if constexpr (VDIRECT) {
         const int vrow = 4 * (grp >> 1) + (sl >> 2);
         const int vbyte = (sl & 1) * 8;
         const int vchunk = 2 * (grp & 1) + ((sl & 3) >> 1);
@@ -508,10 +566,16 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     // consumes them, so the read stays in flight meanwhile. Row offsets of
     // score block kb and k-step kstep are multiples of 16 rows, where both
     // swizzles repeat.
-    using KRaw = std::conditional_t<DIRECT, h8, u2>;                // V operand reads
-    using KRawK = std::conditional_t<DIRECT || KCONV, h8, u2>;      // K operand reads
+    using KRaw = std::conditional_t<VDIRECT, h8, u2>;  // V operand reads
+    using KRawK = std::conditional_t<F8, v8i, std::conditional_t<DIRECT || KCONV, h8, u2>>;  // K operand reads
     auto kfetch = [&](const unsigned char* kt, int kb, int kk) -> KRawK {
-        return *(const KRawK*)(kt + koff_s[kk] + kb * 32 * KROW);
+        if constexpr (F8) {
+            const u4 lo = *(const u4*)(kt + koff8[kk][0] + kb * 32 * KROW);
+            const u4 hi = *(const u4*)(kt + koff8[kk][1] + kb * 32 * KROW);
+            return __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+            return *(const KRawK*)(kt + koff_s[kk] + kb * 32 * KROW);
+        }
     };
     auto decode8 = [](u2 w) -> h8 {
         const u2 lo = e4m3x4_to_f16(w.x), hi = e4m3x4_to_f16(w.y);
@@ -530,6 +594,8 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     auto opuse_k = [&](const KRawK& r) -> h8 {
         if constexpr (DIRECT || KCONV)
             return r;
+        else if constexpr (F8)
+            return h8{};  // unused: F8 codes go to the FP8 MFMA as they are
         else
             return decode8(r);
     };
@@ -572,10 +638,21 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     };
 
     auto opuse_v = [&](const KRaw& r) -> h8 {
-        if constexpr (DIRECT)
+        if constexpr (VDIRECT)
             return r;
         else
             return decode8(r);
+    };
+
+    // one MFMA of S^T = K Q^T at k-step kk: FP16/BF16 32x32x16, or F8 32x32x64
+    // on E4M3 codes (the unscaled form: scale operands 0)
+    constexpr int KKS = F8 ? KK8 : KK;  // k-steps of S over D
+    constexpr bool BFS = SRC == KV_BF16;
+    auto mma_s = [&](const KRawK& kop, int kk, f16x acc) -> f16x {
+        if constexpr (F8)
+            return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qf8[kk], acc, 0, 0, 0, 0, 0, 0);
+        else
+            return mma<BFS>(opuse_k(kop), qf[kk], acc);
     };
 
     // S^T = K Q^T for KT keys x 32 queries (NSB blocks of 32 x 32)
@@ -585,17 +662,35 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
+        for (int kk = 0; kk < KKS; ++kk)
 #pragma unroll
             for (int kb = 0; kb < NSB; ++kb) {
-                s[kb] = mma<BF>(opuse_k(kfetch(kt, kb, kk)), qf[kk], s[kb]);
+                s[kb] = mma_s(kfetch(kt, kb, kk), kk, s[kb]);
             }
+    };
+
+    // F8: the scores of a tile times their keys' scales (register r of score
+    // block kb holds key 32kb + 8(r/4) + 4hlf + r%4); sc: this wave's copy of
+    // the tile's KT scales. Applied before masking, so masked keys stay -inf.
+    auto kscale_tile = [&](f16x (&s)[NSB], const float* sc) {
+        if constexpr (F8) {
+#pragma unroll
+            for (int kb = 0; kb < NSB; ++kb)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const float4 v = *(const float4*)(sc + 32 * kb + 8 * gq + 4 * hlf);
+                    s[kb][4 * gq] *= v.x;
+                    s[kb][4 * gq + 1] *= v.y;
+                    s[kb][4 * gq + 2] *= v.z;
+                    s[kb][4 * gq + 3] *= v.w;
+                }
+        }
     };
 
     // O^T += V^T P^T
     auto vread = [&](const unsigned char* vt, int i) -> KRaw {
         const int kstep = i / DB, db = i % DB;
-        if constexpr (DIRECT) {
+        if constexpr (VDIRECT) {
             s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + voff_a[db]));
             s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vt + kstep * 16 * ROW + voff_b[db]));
             return __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -645,7 +740,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
             for (int i = 0; i < 5; ++i) t[i] = vmax3(s[0][3 * i], s[0][3 * i + 1], s[0][3 * i + 2]);
             mx = vmax3(vmax3(t[0], t[1], t[2]), vmax3(t[3], t[4], s[0][15]), t[0]);
         }
-        return wave_half_max(mx) * a.c;
+        return wave_half_max(mx) * crow;
     };
 
     // Raise the reference maximum of the rows whose scores exceed it by more
@@ -673,8 +768,8 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     const bf2 ones_bf = {(__bf16)1.f, (__bf16)1.f};
     auto exp_unit = [&](const f16x (&s)[NSB], int u, float m_use, h8* pk) {
         const int kb = u / 8, r = 2 * (u % 8);
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], a.c, -m_use));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], a.c, -m_use));
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], crow, -m_use));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], crow, -m_use));
         h2 p;
         if constexpr (BF) {
             const bf2 pb = {(__bf16)e0, (__bf16)e1};
@@ -701,6 +796,13 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     // group has R-1 iterations to arrive. Invariant entering iteration it:
     // S(it) is in scur with its maximum folded into m_run; K(it+1) and V(it)
     // are in LDS; groups it+1 .. it+R-1 are in flight.
+    // F8: the scales of K(j) are in kscl(j % 2) (the dense ring has two slots)
+    auto kscl = [&](auto p) -> const float* {
+        if constexpr (decltype(p)::value % 2 == 0)
+            return kscl0;
+        else
+            return kscl1;
+    };
     auto kslot = [&](auto p) -> unsigned char* {
         constexpr int S = decltype(p)::value % R;
         if constexpr (S == 0) return kslot0;
@@ -755,6 +857,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     }
     f16x scur[NSB];
     compute_s(ktile(P0{}), scur);
+    kscale_tile(scur, kscl0 + wave * KT);
     raise_max(row_max(scur, tile_key0(0), true));
     __syncthreads();
     {
@@ -816,7 +919,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         using PK2 = std::integral_constant<int, decltype(p)::value + 2>;
         const unsigned char* kt = ktile(PN{});
         const unsigned char* vt = vslot(p);
-        constexpr int NB = NSB * KK;  // score MFMAs
+        constexpr int NB = NSB * KKS;  // score MFMAs
         constexpr int NC = KS * DB;   // PV MFMAs
         f16x sn[NSB];
         h8 pk[KS];
@@ -833,7 +936,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         // ---- block B ----
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         KRawK kop[NB];
-        auto kread = [&](int i) { return kfetch(kt, i / KK, i % KK); };
+        auto kread = [&](int i) { return kfetch(kt, i / KKS, i % KKS); };
         // K operand reads in flight (FP16 K operands of the scaled E4M3 source
         // take twice the registers of codes: one fewer at D = 256)
         constexpr int PB = D == 256 ? (KCONV ? 3 : 4) : 3;
@@ -843,8 +946,8 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             if (i + PB < NB) kop[i + PB] = kread(i + PB);
-            const int kb = i / KK, kk = i % KK;
-            sn[kb] = mma<BF>(opuse_k(kop[i]), qf[kk], kk == 0 ? f16x{} : sn[kb]);
+            const int kb = i / KKS, kk = i % KKS;
+            sn[kb] = mma_s(kop[i], kk, kk == 0 ? f16x{} : sn[kb]);
             if (i >= NB - PC) vop[i - (NB - PC)] = vread(vt, i - (NB - PC));
             if constexpr (SPREAD) {
                 if (i % (NB / NL) == 1) DL::issue_one(sg.k, dl.koff, kslot(p), wave, i / (NB / NL));
@@ -910,13 +1013,21 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 #pragma unroll
                 for (int u = ((i - MX0) * NMX) / MXS; u < ((i - MX0 + 1) * NMX) / MXS; ++u) {
                     const int e = 2 * u;  // scores e, e+1 of the flattened NSB x 16 registers
+                    if constexpr (F8) {
+                        // keys 32kb + 8(r/4) + 4hlf + r%4 and the next: two consecutive scales
+                        const int kb = e / 16, r = e % 16;
+                        const float2 sc = *(const float2*)(kscl(PN{}) + wave * KT + 32 * kb + 8 * (r >> 2) +
+                                                           4 * hlf + (r & 3));
+                        sn[kb][r] *= sc.x;
+                        sn[kb][r + 1] *= sc.y;
+                    }
                     macc = vmax3(macc, sn[e / 16][e % 16], sn[(e + 1) / 16][(e + 1) % 16]);
                 }
             }
             if (XCHG_EARLY && i == MX0 + MXS - 1) mpart = __shfl_xor(macc, 32);
             __builtin_amdgcn_sched_barrier(0);
         }
-        raise_max((XCHG_EARLY ? fmaxf(macc, mpart) : wave_half_max(macc)) * a.c);
+        raise_max((XCHG_EARLY ? fmaxf(macc, mpart) : wave_half_max(macc)) * crow);
         refill(p, it);
 #pragma unroll
         for (int kb = 0; kb < NSB; ++kb) scur[kb] = sn[kb];
@@ -938,7 +1049,10 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
 #pragma unroll
         for (int kb = 0; kb < NSB; ++kb) sn[kb] = f16x{};
         h8 pk[KS];
-        if (it + 1 < n_tiles) compute_s(ktile(PN{}), sn);
+        if (it + 1 < n_tiles) {
+            compute_s(ktile(PN{}), sn);
+            kscale_tile(sn, kscl(PN{}) + wave * KT);
+        }
         exp_tile(scur, pk);
         compute_pv(vslot(p), pk);
         if constexpr (KCONV) {
@@ -1160,6 +1274,12 @@ template <int D>
 static hipError_t launch_d(const AttnArgs& a, KvSource src, KeyMode mode, bool split,
                            hipStream_t stream)
 {
+    if (mode == KEYS_DENSE && src == KV_FP8QK) {
+        if constexpr (D == 128)
+            return launch_one<D, 4, KV_FP8QK, KEYS_DENSE, false>(a, stream);
+        else
+            return hipErrorInvalidValue;
+    }
     if (mode == KEYS_DENSE)
         return src == KV_BF16 ? launch_one<D, 4, KV_BF16, KEYS_DENSE, false>(a, stream)
                               : launch_one<D, 4, KV_FP16, KEYS_DENSE, false>(a, stream);
@@ -1208,6 +1328,7 @@ template __global__ void attn_fwd_kernel<128, 4, KV_FP16, KEYS_DENSE, false>(con
 template __global__ void attn_fwd_kernel<256, 4, KV_FP16, KEYS_DENSE, false>(const AttnArgs);
 template __global__ void attn_fwd_kernel<128, 4, KV_BF16, KEYS_DENSE, false>(const AttnArgs);
 template __global__ void attn_fwd_kernel<256, 4, KV_BF16, KEYS_DENSE, false>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 4, KV_FP8QK, KEYS_DENSE, false>(const AttnArgs);
 template __global__ void attn_fwd_kernel<128, 4, KV_FP16, KEYS_CAUSAL, false>(const AttnArgs);
 template __global__ void attn_fwd_kernel<128, 4, KV_FP16, KEYS_CAUSAL, true>(const AttnArgs);
 template __global__ void attn_fwd_kernel<256, 4, KV_FP16, KEYS_CAUSAL, false>(const AttnArgs);

@@ -17,7 +17,10 @@ namespace fa {
 // KV_E4M3_PAGED_SCALED: the K operands are converted in registers to exactly
 // the FP16 value the conversion defines, RNE16(RNE32(decode * k_scale)), for
 // any other k_scale.
-enum KvSource { KV_FP16 = 0, KV_E4M3_PAGED = 1, KV_BF16 = 2, KV_E4M3_PAGED_SCALED = 3 };
+// KV_FP8QK: dense attention whose queries and keys are E4M3 codes with an
+// FP32 scale per row (QK^T on the FP8 matrix cores, the row scales applied to
+// the FP32 scores); V, P and O are BF16.
+enum KvSource { KV_FP16 = 0, KV_E4M3_PAGED = 1, KV_BF16 = 2, KV_E4M3_PAGED_SCALED = 3, KV_FP8QK = 4 };
 
 // Everything one attention launch needs; passed by value as the kernel
 // argument. Strides are in elements. The Geometry part (shape, split and
@@ -43,6 +46,12 @@ struct AttnArgs : Geometry {
 
     // block lists
     const int32_t* idx;  // [B, Hq, nqb, topk]
+
+    // FP8 queries and keys (KV_FP8QK): codes [B, Hq, Lq, D] (kc: [B, Hkv, Lkv, D])
+    // contiguous, FP32 row scales [B, Hq, Lq] and [B, Hkv, Lkv]
+    const uint8_t* qc;
+    const float* qsc;
+    const float* ksc;
 
     // split-KV partial states (FP32): o_part [nseg][B*Hq][part_lq][D]
     // unnormalised, ml_part [nseg][B*Hq][part_lq][2] = (running max in log2
@@ -93,6 +102,10 @@ hipError_t launch_e4m3_bridge(const uint8_t* kc, const uint8_t* vc, const int32_
                               int64_t table_stride, int num_pages, int B, int Hkv, int D,
                               int kv_len, float k_scale, float v_scale, uint16_t* k_out,
                               uint16_t* v_out, hipStream_t stream);
+
+// E4M3 codes and FP32 scales of the rows of a bfloat16 [B, H, L, 128] view.
+hipError_t launch_fp8_rows_quantize(const uint16_t* x, int64_t x_sb, int64_t x_sh, int64_t x_ss, int B, int H, int L,
+                                    uint8_t* codes, float* scales, hipStream_t stream);
 
 // K: FP8 round trip per (row, head) with the row gather; V: the gather.
 hipError_t launch_prefix_fp8_gather(const uint16_t* k, const uint16_t* v, int B, int N, int H,

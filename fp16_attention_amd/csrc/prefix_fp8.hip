@@ -75,6 +75,63 @@ __global__ __launch_bounds__(256) void prefix_fp8_gather_kernel(const uint16_t* 
     *(u4*)(vo + out_off) = vw;
 }
 
+// Per-row E4M3 quantization of the prefix attention's queries and keys
+// ([P5] query_pool.py, the PREFIX_FP8 round trip of the prefix queries;
+// prefix_quant.py, the same for the keys): per (b, h, row) of a bfloat16
+// [B, H, L, 128] view, scale = max |x| / 448, inv = scale == 0 ? 0 : 1 / scale,
+// code = RNE_e4m3(clamp(x * inv, +-448)), each step rounding once in FP32 (the
+// round trip of prefix_fp8_gather_kernel without its decode). Codes go to a
+// contiguous [B, H, L, 128] byte array, scales to FP32 [B, H, L].
+// grid: ceil(B * H * L / 16); one 16-lane group per row, lane l holding
+// elements 8l .. 8l+7.
+__global__ __launch_bounds__(256) void fp8_rows_quantize_kernel(const uint16_t* __restrict__ x, int64_t x_sb,
+                                                                int64_t x_sh, int64_t x_ss, int H, int L,
+                                                                int64_t n_rows, uint8_t* __restrict__ codes,
+                                                                float* __restrict__ scales)
+{
+    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (b * H + h) * L + i
+    const int l = threadIdx.x & 15;
+    if (row >= n_rows) return;  // a group is all in or all out
+    const int i = (int)(row % L);
+    const int64_t bh = row / L;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+    const u4 w = *(const u4*)(x + b * x_sb + h * x_sh + i * x_ss + l * 8);
+    float v[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                  bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const float scale = amax / 448.f;
+    const float inv = scale == 0.f ? 0.f : 1.f / scale;
+    uint32_t c[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const float x0 = fminf(fmaxf(v[4 * p] * inv, -448.f), 448.f);
+        const float x1 = fminf(fmaxf(v[4 * p + 1] * inv, -448.f), 448.f);
+        const float x2 = fminf(fmaxf(v[4 * p + 2] * inv, -448.f), 448.f);
+        const float x3 = fminf(fmaxf(v[4 * p + 3] * inv, -448.f), 448.f);
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+        c[p] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, lo, true);
+    }
+    *(uint2*)(codes + row * kPD + l * 8) = make_uint2(c[0], c[1]);
+    if (l == 0) scales[row] = scale;
+}
+
+hipError_t launch_fp8_rows_quantize(const uint16_t* x, int64_t x_sb, int64_t x_sh, int64_t x_ss, int B, int H, int L,
+                                    uint8_t* codes, float* scales, hipStream_t stream)
+{
+    const int64_t n_rows = (int64_t)B * H * L;
+    if (n_rows <= 0) return hipSuccess;
+    const int64_t grid = (n_rows + 15) / 16;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fp8_rows_quantize_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, x_sb, x_sh, x_ss, H,
+                       L, n_rows, codes, scales);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefix_fp8_gather(const uint16_t* k, const uint16_t* v, int B, int N, int H,
                                     const int32_t* index, int rows, uint16_t* k_out, uint16_t* v_out,
                                     hipStream_t stream)

@@ -108,6 +108,31 @@ int attn_fwd_dense_bf16(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, floa
                         int Lq, int Lkv, int D, float scale, void* stream);
 
 /*
+ * Dense attention of the prefix with FP8 queries and keys ([P5]
+ * query_pool.py: the PREFIX_FP8 round trip of the prefix queries with a
+ * per-(row, head) amax / 448 scale; prefix_quant.py: the same for the prefix
+ * keys; the example configuration's prefix_precision: fp8).
+ * q, k, v: bfloat16 [B,H,Lq,D], [B,H,Lkv,D], [B,H,Lkv,D] views; o: bfloat16
+ * [B,H,Lq,D]; lse: optional FP32 [B,H,Lq] contiguous.
+ * Every row x of q and of k is quantized as the round trip does:
+ * scale = max |x| / 448, code = RNE_e4m3(clamp(x * (scale == 0 ? 0 :
+ * 1 / scale), +-448)), in FP32. QK^T runs on the FP8 matrix cores on the codes
+ * (exact products, FP32 accumulation) and the FP32 scores are multiplied by
+ * the query's and the key's scale: the attention is over the dequantized
+ * values decode(code) * scale, without the round trip's bfloat16 storage
+ * rounding of them. The softmax runs in FP32, P is rounded to bfloat16, PV
+ * accumulates in FP32 on bfloat16 matrix cores and O is rounded to bfloat16.
+ * workspace: attn_fwd_prefix_fp8_workspace(...) bytes, 256-byte aligned, not
+ * overlapping any operand: the codes of q [B,H,Lq,D] and of k [B,H,Lkv,D]
+ * (each padded to 256 bytes), then the scales of q [B,H,Lq] and of k
+ * [B,H,Lkv] (FP32, each padded to 256 bytes).
+ * Domain: D == 128; B, H >= 1; Lq >= 0 (0 is a no-op); Lkv >= 1.
+ */
+size_t attn_fwd_prefix_fp8_workspace(int B, int H, int Lq, int Lkv, int D);
+int attn_fwd_prefix_fp8(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse, int B, int H, int Lq,
+                        int Lkv, int D, float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Causal prefill against a prefix KV with grouped-query heads ([P4]
  * Implementation). Query row i (0 <= i < q_rows) of query head h sees keys
  * j <= (kv_len - q_real) + i of kv head h / (Hq / Hkv). Rows i >= q_real are
