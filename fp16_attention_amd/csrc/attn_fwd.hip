@@ -334,6 +334,9 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     static_assert(R >= 2 && R <= 4, "ring depth");
     static_assert(VDIRECT || KT == 32, "an E4M3 tile is one 32-token page");
     static_assert(!F8 || (D == 128 && KT == 64 && R == 2 && MODE == KEYS_DENSE), "FP8 source: dense D128");
+    // One array per ring slot: the compiler then sees that the LDS reads of
+    // one slot do not alias the loads in flight into another (with one array
+    // per ring it waits for every load into LDS, vmcnt(0), before each read).
     __shared__ __attribute__((aligned(1024))) unsigned char kslot0[TBK];
     __shared__ __attribute__((aligned(1024))) unsigned char kslot1[TBK];
     __shared__ __attribute__((aligned(1024))) unsigned char kslot2[R > 2 ? TBK : 16];
