@@ -387,8 +387,64 @@ def cpu_baseline(w, qkv, out_gpu, rows_per_head):
     cpu = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
            "sample": f"{len(rows)} query rows ({rows_per_head} per head, seeded) of the headline workload, "
                      f"each against all {w['Lkv']} keys, FP64; {dt:.2f} s wall",
-           "seconds": dt, "host_cpus_online": os.cpu_count(), "cpu_model": _cpu_model()}
+           "seconds": dt, "host_cpus_online": os.cpu_count(), "cpu_model": _cpu_model(),
+           "extrapolated_full_problem_s": dense_flops(w) / (flop / dt),
+           "extrapolation": "the whole workload's FLOP at the sampled rate (an extrapolation, not a measurement)"}
     return cpu, parity
+
+
+def cpu_extra_baselines(rows_per_head: int = 8):
+    """The FP64 oracle timed on three more workloads: a seeded sample of query
+    rows of the causal prefill, and the whole paged E4M3 -> FP16 bridge and
+    the whole VSA block selection (each a few seconds of CPU work)."""
+    import oracle
+    import synth.workloads as wl
+    oracle.build()
+    threads = max(1, min(16, os.cpu_count() or 1))
+    res = {}
+
+    w = wl.PREFIX_CAUSAL
+    q, k, v = wl.causal_inputs(w)
+    rng = np.random.default_rng(4321)
+    off = w["kv_len"] - w["q_real"]
+    rows = []
+    for h in range(w["Hq"]):
+        sel = {0, w["q_real"] - 1, *rng.integers(0, w["q_real"], rows_per_head - 2).tolist()}
+        rows += [(0, h, i) for i in sorted(sel)]
+    rows = np.array(rows, dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, float(np.float32(1.0 / np.sqrt(w["D"]))), mode=oracle.MODE_CAUSAL, offset=off,
+                     rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    flop = 4 * w["D"] * int(np.minimum(off + rows[:, 2].astype(np.int64) + 1, w["kv_len"]).sum())
+    res["prefix_causal"] = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                            "sample": f"{len(rows)} query rows ({rows_per_head} per head, seeded) of {w['name']}, "
+                                      f"each against its visible keys, FP64; {dt:.2f} s wall",
+                            "seconds": dt, "extrapolated_full_problem_s": causal_flops(w) / (flop / dt)}
+    del q, k, v
+
+    w = wl.PAGED_E4M3
+    _, kc, vc, table, ks, vs = wl.paged_inputs(w, unit_scales=False)
+    t0 = time.perf_counter()
+    for cache, sc in ((kc, ks), (vc, vs)):
+        oracle.e4m3_to_f16(oracle.paged_gather(cache, table, w["kv_len"]), sc)
+    dt = time.perf_counter() - t0
+    nb = bridge_bytes(w)
+    res["e4m3_bridge"] = {"value": nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                          "sample": f"the whole bridge of {w['name']} (K and V), {dt:.2f} s wall",
+                          "seconds": dt}
+    del kc, vc
+
+    w = wl.VSA
+    q, k, _ = wl.vsa_inputs(w)
+    t0 = time.perf_counter()
+    oracle.vsa_select(q, k, w["block"], w["topk"])
+    dt = time.perf_counter() - t0
+    nb = select_bytes(w)
+    res["vsa_select"] = {"value": nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                         "sample": f"the whole block selection (pool, FP64 scores, top-k) of {w['name']}, "
+                                   f"{dt:.2f} s wall", "seconds": dt}
+    return res
 
 
 def _cpu_model() -> str:
@@ -527,6 +583,9 @@ def main():
     if result is None:
         print(json.dumps({"metric": METRIC, "partial": True, "only": args.only, "extra": extra}), flush=True)
         return
+    if not args.no_cpu and not args.no_extra and args.only is None:
+        log("cpu oracle: causal prefill sample, bridge, VSA selection")
+        result["cpu_baseline_extra"] = cpu_extra_baselines()
     # FP16 MFMA-bound workloads against the same measured (FP16) ceiling as the headline
     for rec in extra.values():
         if "tflops" in rec and "BF16" not in rec["workload"] and "peak_tflops" not in rec:
