@@ -162,6 +162,22 @@ def stats(ms):
 
 # --------------------------------------------------------------------------- workloads
 
+def bench_copy(torch, timer, iters, flush=None):
+    """The runtime's device copy of 1 GiB: the measured HBM copy rate that
+    the HBM-bound kernels are also reported against."""
+    src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms, _ = timer.run(lambda: dst.copy_(src), iters, 2, flush=flush)
+    gbs = 2 * src.numel() / (np.median(ms) * 1e-3) / 1e9
+    log(f"copy 1 GiB: {np.median(ms):.3f} ms  {gbs:.0f} GB/s")
+    rec = {"workload": "device copy of 1 GiB (read 1 GiB, write 1 GiB)", "bytes_read": src.numel(),
+           "bytes_written": dst.numel(), **stats(ms), "gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+           "llc_flushed": flush is not None}
+    del src, dst
+    torch.cuda.empty_cache()
+    return rec
+
+
 def bench_dense(fa, torch, W, steps, warmup, timer):
     import synth.workloads as wl
     w = wl.VIDEO_DENSE
@@ -370,7 +386,12 @@ def cpu_baseline(w, qkv, out_gpu, rows_per_head):
     rng = np.random.default_rng(1234)
     rows = []
     for h in range(w["H"]):
-        sel = {0, w["Lq"] - 1, *rng.integers(0, w["Lq"], rows_per_head - 2).tolist()}
+        # first and last rows, both sides of 16 seeded 128-row tile boundaries,
+        # then seeded random rows up to rows_per_head distinct rows
+        edges = 128 * rng.integers(1, w["Lq"] // 128, 16)
+        sel = {0, w["Lq"] - 1, *(edges - 1).tolist(), *edges.tolist()}
+        while len(sel) < rows_per_head:
+            sel.add(int(rng.integers(0, w["Lq"])))
         rows += [(0, h, i) for i in sorted(sel)]
     rows = np.array(rows, dtype=np.int32)
     threads = max(1, min(16, os.cpu_count() or 1))
@@ -385,7 +406,8 @@ def cpu_baseline(w, qkv, out_gpu, rows_per_head):
     parity = {"rows": int(len(rows)), "max_abs": float(np.abs(err).max()),
               "rel_l2": float(np.linalg.norm(err) / np.linalg.norm(ref))}
     cpu = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-           "sample": f"{len(rows)} query rows ({rows_per_head} per head, seeded) of the headline workload, "
+           "sample": f"{len(rows)} query rows ({rows_per_head} per head, seeded: first, last, both sides of 16 "
+                     f"tile boundaries, random) of the headline workload, "
                      f"each against all {w['Lkv']} keys, FP64; {dt:.2f} s wall",
            "seconds": dt, "host_cpus_online": os.cpu_count(), "cpu_model": _cpu_model(),
            "extrapolated_full_problem_s": dense_flops(w) / (flop / dt),
@@ -473,7 +495,7 @@ def main():
                          "device copy that calibrates the HBM byte counters")
     ap.add_argument("--no-extra", action="store_true", help="skip the non-headline workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=384, help="oracle rows per head for cpu_baseline")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="oracle rows per head for cpu_baseline")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch of the dense kernel (from rocprofv3 PMC runs)")
     args = ap.parse_args()
@@ -513,14 +535,8 @@ def main():
     if args.only == "copy":
         # A plain copy of a known size: the kernel whose FETCH_SIZE / WRITE_SIZE
         # readings scale the attention kernel's counters to bytes.
-        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        ms, _ = timer.run(lambda: dst.copy_(src), args.iters, 2)
-        gbs = 2 * src.numel() / (np.median(ms) * 1e-3) / 1e9
-        log(f"copy 1 GiB: {np.median(ms):.3f} ms  {gbs:.0f} GB/s")
-        print(json.dumps({"metric": "device copy", "partial": True, "only": "copy",
-                          "bytes_read": src.numel(), "bytes_written": dst.numel(), **stats(ms),
-                          "gbs": gbs}), flush=True)
+        rec = bench_copy(torch, timer, args.iters)
+        print(json.dumps({"metric": "device copy", "partial": True, "only": "copy", **rec}), flush=True)
         return
     if args.only in (None, "dense"):
         w, qkv, out, ms, wall = bench_dense(fa, torch, None, args.steps, args.warmup, timer)
@@ -579,6 +595,11 @@ def main():
         if args.only in (None, "vsa"):
             extra["vsa_select"], extra["vsa_sparse_attn"] = bench_vsa(fa, torch, args.iters, timer, flush)
             torch.cuda.empty_cache()
+        if args.only is None:
+            extra["hbm_copy"] = copy = bench_copy(torch, timer, args.iters, flush)
+            for rec in extra.values():
+                if "gbs" in rec and rec is not copy:
+                    rec["frac_of_measured_copy"] = rec["gbs"] / copy["gbs"]
 
     if result is None:
         print(json.dumps({"metric": METRIC, "partial": True, "only": args.only, "extra": extra}), flush=True)

@@ -43,6 +43,10 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 // sum| are exact in FP64 (a 24-bit c times a 7-bit count).
 __device__ __forceinline__ float mean_rn(double sum, int count)
 {
+    // a power-of-two count (every full block): sum / count is exact in FP64
+    // (the sum is a multiple of 2^-24 below 2^22), so its one rounding to FP32
+    // is the answer
+    if ((count & (count - 1)) == 0) return (float)(sum * (1.0 / count));
     const float c0 = (float)(sum / count);
     const float cand[2] = {nextafterf(c0, -INFINITY), nextafterf(c0, INFINITY)};
     float best = c0;
