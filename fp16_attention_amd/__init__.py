@@ -23,7 +23,8 @@ FA_ERR_HIP = 1000
 EXPORTS = ("fa_abi_version", "fa_error_string", "attn_fwd_dense", "attn_fwd_dense_bf16",
            "attn_fwd_prefix_fp8_workspace", "attn_fwd_prefix_fp8",
            "attn_fwd_prefix_causal_workspace",
-           "attn_fwd_prefix_causal", "attn_fwd_paged_e4m3_workspace", "attn_fwd_paged_e4m3",
+           "attn_fwd_prefix_causal", "attn_fwd_paged_e4m3_workspace", "attn_fwd_paged_e4m3_bridged_workspace",
+           "attn_fwd_paged_e4m3",
            "attn_fwd_paged_e4m3_decode_workspace", "attn_fwd_paged_e4m3_decode",
            "attn_fwd_paged_e4m3_decode_noalloc",
            "kv_e4m3_paged_to_fp16", "kv_prefix_fp8_gather", "vsa_topk_for_sparsity", "vsa_block_select_workspace",
@@ -55,6 +56,7 @@ _SIGS = {
     "attn_fwd_prefix_causal_workspace": (_sz, [_i] * 6),
     "attn_fwd_prefix_causal": (_i, [FaTensor] * 4 + [_vp] + [_i] * 7 + [_f, _vp, _sz, _vp]),
     "attn_fwd_paged_e4m3_workspace": (_sz, [_i] * 6),
+    "attn_fwd_paged_e4m3_bridged_workspace": (_sz, [_i] * 6 + [_f]),
     "attn_fwd_paged_e4m3": (_i, [FaTensor, _vp, _vp, _vp, _i64, _i, _i, _f, _f, FaTensor, _vp]
                             + [_i] * 7 + [_f, _vp, _sz, _vp]),
     "attn_fwd_paged_e4m3_decode_workspace": (_sz, [_i] * 6),
@@ -273,11 +275,23 @@ def attn_fwd_prefix_causal(q, k, v, q_real, out=None, lse=None, scale=None, work
 
 
 def attn_fwd_paged_e4m3(q, k_cache, v_cache, page_table, kv_len, q_real, k_scale=1.0, v_scale=1.0,
-                        out=None, lse=None, scale=None, workspace=None):
+                        out=None, lse=None, scale=None, workspace=None, bridged=True):
     """Causal prefill reading an E4M3 paged cache [pages, 32, Hkv, D] (uint8) via an int32 page table
-    [B, pages_per_seq]."""
+    [B, pages_per_seq]. bridged: size the workspace this call allocates (when none is given) for the
+    bridged plan (FP16 K and V converted into the workspace first; used for a k_scale that is not a
+    power of two); False allocates only the split-KV states, so the cache is attended in place. A
+    given workspace selects the plan by its size (see paged_e4m3_workspace)."""
     return _paged(False, q, k_cache, v_cache, page_table, kv_len, q_real, k_scale, v_scale, out, lse, scale,
-                  workspace)
+                  workspace, bridged=bridged)
+
+
+def paged_e4m3_workspace(B, Hq, Hkv, D, q_rows, kv_len, k_scale=None) -> int:
+    """Workspace bytes of attn_fwd_paged_e4m3: the in-place plan's (k_scale None), or the size that
+    selects the bridged plan for that k_scale."""
+    lib = load()
+    if k_scale is None:
+        return int(lib.attn_fwd_paged_e4m3_workspace(B, Hq, Hkv, D, q_rows, kv_len))
+    return int(lib.attn_fwd_paged_e4m3_bridged_workspace(B, Hq, Hkv, D, q_rows, kv_len, k_scale))
 
 
 def attn_fwd_paged_e4m3_decode(q, k_cache, v_cache, page_table, kv_len, q_real=None, k_scale=1.0, v_scale=1.0,
@@ -302,7 +316,7 @@ def attn_fwd_paged_e4m3_decode_noalloc(q, k_cache, v_cache, page_table, kv_len, 
 
 
 def _paged(decode, q, k_cache, v_cache, page_table, kv_len, q_real, k_scale, v_scale, out, lse, scale, workspace,
-           noalloc=False):
+           noalloc=False, bridged=False):
     import torch
     _want(q, "q", _f16(), ndim=4, unit_d=True)
     B, Hq, q_rows, D = q.shape
@@ -329,9 +343,16 @@ def _paged(decode, q, k_cache, v_cache, page_table, kv_len, q_real, k_scale, v_s
         return out
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
-    wsq = lib.attn_fwd_paged_e4m3_decode_workspace if decode else lib.attn_fwd_paged_e4m3_workspace
     fn = lib.attn_fwd_paged_e4m3_decode if decode else lib.attn_fwd_paged_e4m3
-    ws = _workspace(int(wsq(B, Hq, Hkv, D, q_rows, kv_len)), q.device, workspace)
+    if decode:
+        need = lib.attn_fwd_paged_e4m3_decode_workspace(B, Hq, Hkv, D, q_rows, kv_len)
+    elif bridged and workspace is None:
+        # allocate what the bridged plan needs (a given workspace only has to hold the split-KV
+        # states: the library takes the bridged plan when it is large enough)
+        need = lib.attn_fwd_paged_e4m3_bridged_workspace(B, Hq, Hkv, D, q_rows, kv_len, k_scale)
+    else:
+        need = lib.attn_fwd_paged_e4m3_workspace(B, Hq, Hkv, D, q_rows, kv_len)
+    ws = _workspace(int(need), q.device, workspace)
     _check(fn(_view(q), k_cache.data_ptr(), v_cache.data_ptr(), page_table.data_ptr(), page_table.stride(0),
               pages, page_size, k_scale, v_scale, _view(out), _ptr(lse), B, Hq, Hkv, D, q_rows, q_real, kv_len,
               scale, _ptr(ws), _nbytes(ws), _stream(q)))

@@ -282,6 +282,22 @@ size_t attn_fwd_paged_e4m3_workspace(int B, int Hq, int Hkv, int D, int q_rows, 
 
 namespace {
 
+// A k_scale for which every decode(code) * k_scale is an FP16 value: a power
+// of two in [2^-15, 2^7].
+bool pow2_scale(float k_scale)
+{
+    int e;
+    return frexpf(k_scale, &e) == 0.5f && k_scale >= 0x1p-15f && k_scale <= 128.f;
+}
+
+// Bytes of the paged prefill's bridged plan: the split-KV partial states
+// (rounded up to 256 bytes), then the FP16 K and V the bridge writes.
+size_t bridged_bytes(int B, int Hq, int Hkv, int D, int q_rows, int kv_len, size_t* partial)
+{
+    *partial = (plan_split(B, Hq, D, q_rows, kv_len).workspace + 255) & ~(size_t)255;
+    return *partial + 2 * (size_t)B * Hkv * kv_len * D * sizeof(uint16_t);
+}
+
 // Shared body of the paged E4M3 entry points (prefill and decode).
 int run_paged(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_cache, const int32_t* page_table,
               int64_t table_stride, int num_phys_pages, int page_size, float k_scale, float v_scale,
@@ -338,9 +354,39 @@ int run_paged(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_cache, const
     // K is attended as the converted cache's FP16 values RNE16(RNE32(decode *
     // k_scale)). A power-of-two k_scale in [2^-15, 2^7] keeps every such product
     // an exact FP16 value, so the exact decode is used and k_scale folds into the
-    // softmax constant; any other k_scale converts each K operand in registers.
-    int k_exp;
-    const bool k_pow2 = frexpf(k_scale, &k_exp) == 0.5f && k_scale >= 0x1p-15f && k_scale <= 128.f;
+    // softmax constant; any other k_scale converts each K code tile once per
+    // workgroup into an FP16 tile in LDS.
+    const bool k_pow2 = pow2_scale(k_scale);
+    if (!decode && !k_pow2 && !wsrc) {
+        // The bridged plan, when the caller's workspace holds it: the exact
+        // bridge converts K and V into FP16 in the workspace, and the FP16
+        // causal kernel attends to them (the order of [P4] Implementation;
+        // faster than converting K in every workgroup's LDS).
+        size_t partial;
+        const size_t need = bridged_bytes(B, Hq, Hkv, D, q_rows, kv_len, &partial);
+        if (workspace && workspace_bytes >= need && (int64_t)B * Hkv * 2 <= 65535) {
+            if (((uintptr_t)workspace & 255u) != 0) return FA_ERR_ALIGN;
+            Span ws = span_flat(workspace, (int64_t)need, 1);
+            for (const Span& s : in)
+                if (overlap(ws, s)) return FA_ERR_ALIAS;
+            if (overlap(ws, so) || (lse && overlap(ws, sl))) return FA_ERR_ALIAS;
+            const int64_t n = (int64_t)B * Hkv * kv_len * D;
+            uint16_t* kf = (uint16_t*)((char*)workspace + partial);
+            uint16_t* vf = kf + n;
+            hipError_t e = fa::launch_e4m3_bridge(k_cache, v_cache, page_table, table_stride, num_phys_pages, B,
+                                                  Hkv, D, kv_len, k_scale, v_scale, kf, vf, (hipStream_t)stream);
+            if (e != hipSuccess) return hip_status(e);
+            a.k = (const _Float16*)kf;
+            a.v = (const _Float16*)vf;
+            a.k_sb = a.v_sb = (int64_t)Hkv * kv_len * D;
+            a.k_sh = a.v_sh = (int64_t)kv_len * D;
+            a.k_ss = a.v_ss = D;
+            a.c = scale * 1.4426950408889634f;
+            a.oscale = 1.f;
+            return run_causal(a, fa::KV_FP16, fa::KEYS_CAUSAL, plan_split(B, Hq, D, q_rows, kv_len), D, q_rows,
+                              workspace, partial, (hipStream_t)stream, in, 4, so, sl);
+        }
+    }
     const fa::KvSource src = k_pow2 ? fa::KV_E4M3_PAGED : fa::KV_E4M3_PAGED_SCALED;
     a.c = scale * (k_pow2 ? k_scale : 1.f) * 1.4426950408889634f;
     a.kscale = k_scale;
@@ -374,6 +420,15 @@ int attn_fwd_paged_e4m3(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_ca
     return run_paged(q, k_cache, v_cache, page_table, table_stride, num_phys_pages, page_size, k_scale, v_scale,
                      o, lse, B, Hq, Hkv, D, q_rows, q_real, kv_len, scale, workspace, workspace_bytes, stream,
                      false);
+}
+
+size_t attn_fwd_paged_e4m3_bridged_workspace(int B, int Hq, int Hkv, int D, int q_rows, int kv_len, float k_scale)
+{
+    if (check_causal_domain(B, Hq, Hkv, D, q_rows, 1, kv_len)) return 0;
+    if (!(k_scale > 0.f) || !isfinite(k_scale) || pow2_scale(k_scale))
+        return attn_fwd_paged_e4m3_workspace(B, Hq, Hkv, D, q_rows, kv_len);
+    size_t partial;
+    return bridged_bytes(B, Hq, Hkv, D, q_rows, kv_len, &partial);
 }
 
 size_t attn_fwd_paged_e4m3_decode_workspace(int B, int Hq, int Hkv, int D, int q_rows, int kv_len)

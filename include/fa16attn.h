@@ -163,13 +163,31 @@ int attn_fwd_prefix_causal(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, f
  * physical page of logical token t (t < kv_len). Entries must lie in
  * [0, num_phys_pages); an entry outside is clamped into range (no fault, the
  * result for that sequence is then unspecified).
- * Each code is decoded to FP16 exactly (every E4M3 value is an FP16 value)
- * in registers, as the MFMA operand; k_scale multiplies the scores and
- * v_scale the output in FP32.
+ * K is attended as the FP16 values of the exact conversion,
+ * RNE16(RNE32(decode(code) * k_scale)) ([P4] Implementation: the attention
+ * runs on the cache converted exactly to FP16 with its scale):
+ *  - k_scale a power of two in [2^-15, 2^7]: those are decode * k_scale
+ *    exactly, so each code is decoded to FP16 exactly in registers as the MFMA
+ *    operand and k_scale joins the softmax scale; V is decoded exactly and
+ *    v_scale multiplies the FP32 output;
+ *  - any other k_scale, with a workspace of at least
+ *    attn_fwd_paged_e4m3_bridged_workspace(..., k_scale) bytes: the exact
+ *    bridge (kv_e4m3_paged_to_fp16) writes FP16 K and V into the workspace and
+ *    the FP16 causal kernel attends to them (V too is then the bridge's FP16
+ *    values), the order the page converts in;
+ *  - any other k_scale with a smaller workspace: each workgroup converts every
+ *    K code tile once into an FP16 tile in LDS with the same two roundings; V
+ *    as in the first case.
  * Domain as attn_fwd_prefix_causal, plus page_size == 32,
  * table_stride >= kv_len / 32, num_phys_pages >= 1, finite scales > 0.
+ * workspace: at least attn_fwd_paged_e4m3_workspace(...) bytes (the split-KV
+ * states), 256-byte aligned; attn_fwd_paged_e4m3_bridged_workspace returns
+ * that size plus 4 * B * Hkv * kv_len * D bytes of FP16 K and V when k_scale
+ * is not a power of two in that range, and the same size otherwise.
  */
 size_t attn_fwd_paged_e4m3_workspace(int B, int Hq, int Hkv, int D, int q_rows, int kv_len);
+size_t attn_fwd_paged_e4m3_bridged_workspace(int B, int Hq, int Hkv, int D, int q_rows, int kv_len,
+                                             float k_scale);
 int attn_fwd_paged_e4m3(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_cache,
                         const int32_t* page_table, int64_t table_stride, int num_phys_pages,
                         int page_size, float k_scale, float v_scale, fa_tensor o, float* lse, int B,

@@ -150,6 +150,22 @@ def test_decode_rejections_and_workspace():
     assert lib.attn_fwd_paged_e4m3_decode_workspace(1, 6, 1, 256, 17, 256000) == 0   # invalid shape
 
 
+def test_paged_bridged_workspace():
+    """The bridged plan's size: the split-KV states rounded up to 256 bytes plus FP16 K and V, only for a
+    k_scale whose products with the E4M3 values are not all FP16 values (else the in-place size)."""
+    lib = fa.load()
+    shape = (1, 6, 1, 256, 8000, 256000)
+    base = lib.attn_fwd_paged_e4m3_workspace(*shape)
+    partial = (base + 255) // 256 * 256
+    assert lib.attn_fwd_paged_e4m3_bridged_workspace(*shape, 0.0703418) == partial + 4 * 256000 * 256
+    for pow2 in (1.0, 0.0625, 2.0 ** -15, 128.0):
+        assert lib.attn_fwd_paged_e4m3_bridged_workspace(*shape, pow2) == base
+    assert lib.attn_fwd_paged_e4m3_bridged_workspace(*shape, 256.0) == partial + 4 * 256000 * 256
+    assert lib.attn_fwd_paged_e4m3_bridged_workspace(1, 6, 1, 256, 100, 256000, 0.07) == 0  # invalid shape
+    assert fa.paged_e4m3_workspace(*shape) == base
+    assert fa.paged_e4m3_workspace(*shape, k_scale=0.0703418) == partial + 4 * 256000 * 256
+
+
 def test_workspace_queries_are_pure_functions_of_shape():
     lib = fa.load()
     a = lib.attn_fwd_prefix_causal_workspace(1, 6, 1, 256, 8000, 128000)

@@ -86,13 +86,13 @@ def test_prefix_causal_full(lib):
     assert np.abs(got_lse - ref_lse).max() < LSE_ABS
 
 
-@pytest.mark.parametrize("unit_scales", [True, False])
-def test_paged_e4m3_full(lib, unit_scales):
+@pytest.mark.parametrize("unit_scales,bridged", [(True, True), (False, True), (False, False)])
+def test_paged_e4m3_full(lib, unit_scales, bridged):
     w = wl.PAGED_E4M3
     q, kc, vc, table, ks, vs = wl.paged_inputs(w, unit_scales)
-    say("full paged", w["name"], "scales", ks, vs)
+    say("full paged", w["name"], "scales", ks, vs, "bridged", bridged)
     dq, dkc, dvc, dt = dev(q), dev(kc), dev(vc), dev(table)
-    out = lib.attn_fwd_paged_e4m3(dq, dkc, dvc, dt, w["kv_len"], w["q_real"], ks, vs)
+    out = lib.attn_fwd_paged_e4m3(dq, dkc, dvc, dt, w["kv_len"], w["q_real"], ks, vs, bridged=bridged)
     ko, vo = lib.kv_e4m3_paged_to_fp16(dkc, dvc, dt, w["B"], w["kv_len"], ks, vs)
     torch.cuda.synchronize()
     # the bridge, bit-exact over every converted element

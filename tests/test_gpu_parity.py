@@ -115,13 +115,15 @@ def _paged_inputs(seed, Hkv, D, kv_len, pages, ks, vs):
     (6, 1, 256, 128, 100, 2048, 80, 0.0371, 0.0815),
     (4, 2, 128, 192, 150, 1056, 40, 0.0371, 0.0815),   # D128 byte swizzle, two kv heads, a 32-key tail
 ])
-def test_paged_e4m3_parity(lib, Hq, Hkv, D, q_rows, q_real, kv_len, pages, ks, vs):
-    say(f"paged e4m3 Hq{Hq} Hkv{Hkv} D{D} q{q_rows} real{q_real} kv{kv_len} scales {ks} {vs}")
+@pytest.mark.parametrize("bridged", [True, False])  # with a non-power-of-two k_scale: the two plans
+def test_paged_e4m3_parity(lib, Hq, Hkv, D, q_rows, q_real, kv_len, pages, ks, vs, bridged):
+    say(f"paged e4m3 Hq{Hq} Hkv{Hkv} D{D} q{q_rows} real{q_real} kv{kv_len} scales {ks} {vs} bridged {bridged}")
     ks, vs = float(np.float32(ks)), float(np.float32(vs))
     q = synth.normal_f16(5, synth.TID_Q, (1, Hq, q_rows, D))
     kc, vc, table = _paged_inputs(5, Hkv, D, kv_len, pages, ks, vs)
     scale = lib.default_scale(D)
-    out = lib.attn_fwd_paged_e4m3(dev(q), dev(kc), dev(vc), dev(table), kv_len, q_real, ks, vs, scale=scale)
+    out = lib.attn_fwd_paged_e4m3(dev(q), dev(kc), dev(vc), dev(table), kv_len, q_real, ks, vs, scale=scale,
+                                  bridged=bridged)
     torch.cuda.synchronize()
     kf = oracle.e4m3_to_f16(oracle.paged_gather(kc, table, kv_len), ks).view(np.float16)
     vf = oracle.e4m3_to_f16(oracle.paged_gather(vc, table, kv_len), vs).view(np.float16)

@@ -346,10 +346,15 @@ def _decoded(kc, vc, table, kv_len, ks, vs):
     return kf, vf
 
 
-@pytest.mark.parametrize("case,ks,vs,D", [("q16", 0.0371, 0.0815, 256), ("planted", 0.0371, 0.0815, 256),
-                                          ("q16", 0.0625, 0.5, 256), ("q16", 0.0703418, 0.0493912, 128)])
-def test_paged_prefill_rescale(lib, case, ks, vs, D):
-    # power-of-two k_scale: the exact decode; otherwise the in-register K conversion
+@pytest.mark.parametrize("case,ks,vs,D,bridged", [("q16", 0.0371, 0.0815, 256, False),
+                                                  ("planted", 0.0371, 0.0815, 256, False),
+                                                  ("q16", 0.0625, 0.5, 256, False),
+                                                  ("q16", 0.0703418, 0.0493912, 128, False),
+                                                  ("q16", 0.0371, 0.0815, 256, True),
+                                                  ("planted", 0.0371, 0.0815, 256, True)])
+def test_paged_prefill_rescale(lib, case, ks, vs, D, bridged):
+    # power-of-two k_scale: the exact decode; otherwise the K conversion in
+    # LDS (in place) or the bridge into the workspace and the FP16 kernel
     Hq, Hkv, q_rows, q_real, kv_len = 6, 1, 128, 100, 4096
     ks, vs = float(np.float32(ks)), float(np.float32(vs))
     shape = (1, Hq, Hkv, D, q_rows, q_real, kv_len)
@@ -371,8 +376,10 @@ def test_paged_prefill_rescale(lib, case, ks, vs, D):
     forced = raises_forced(q, kf, lib.default_scale(D), rk, 32)
     say(f"  (row, segment) pairs forced to raise: {forced} of {len(rk)}")
     assert forced >= (len(rk) // 4 if case == "q16" else len(chosen))
-    nws = int(lib.load().attn_fwd_paged_e4m3_workspace(1, Hq, Hkv, D, q_rows, kv_len))
+    nws = lib.paged_e4m3_workspace(1, Hq, Hkv, D, q_rows, kv_len, ks if bridged else None)
     assert nws > 0
+    if bridged:
+        assert nws >= 4 * Hkv * kv_len * D  # the FP16 K and V are in it
     o, lse, ws = guarded_out(1, Hq, q_rows, D), guarded_lse(1, Hq, q_rows), guarded_ws(nws)
     lib.attn_fwd_paged_e4m3(dev(q), dev(kc), dev(vc), dev(table), kv_len, q_real, ks, vs, out=o.view,
                             lse=lse.view, workspace=ws.view)
