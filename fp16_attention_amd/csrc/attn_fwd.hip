@@ -7,8 +7,10 @@
 //     the key range into FP32 partial states that a second kernel merges
 //     ("[Kernel][SM70] Integrate FP32 v37 prefill and exact E4M3 bridge",
 //     Implementation),
-//   - the same prefill reading K/V from a paged E4M3 cache, decoded exactly
-//     to FP16 in registers as the MFMA operands (same page, Purpose),
+//   - the same prefill reading K/V from a paged E4M3 cache: the codes stream
+//     through LDS and are decoded exactly to FP16 in registers as the MFMA
+//     operands, or, for a k_scale that is not a power of two, K is converted
+//     once per workgroup into FP16 tiles in LDS (same page, Purpose),
 //   - block-sparse attention over per-query-block KV block lists with dense
 //     prefix query blocks ("[Video] Integrate H3 SM70 execution, metrics and
 //     VSA diagnostics", Purpose).
@@ -25,7 +27,7 @@
 //     E4M3 code tiles (one 32-token page each) move into the ring the same
 //     way, half the bytes of FP16 tiles; each wave decodes the codes of every
 //     operand it reads exactly to FP16 in registers, right before the MFMA
-//     that consumes it. K and V are stored row-major with 16-byte chunks
+//     that consumes it (scaled K: from the workgroup's converted FP16 tile). K and V are stored row-major with 16-byte chunks
 //     XOR-swizzled by the row, which keeps the K operand reads and the
 //     transposing V reads (16-bit or 8-bit) free of bank conflicts.
 //   - Scores are computed transposed, S^T = K Q^T, with

@@ -14,9 +14,9 @@ namespace fa {
 // KV_E4M3_PAGED: E4M3 codes decoded exactly to FP16 in registers; used when
 // k_scale is a power of two that keeps every decode * k_scale an exact FP16
 // value, so folding k_scale into the softmax constant changes nothing.
-// KV_E4M3_PAGED_SCALED: the K operands are converted in registers to exactly
-// the FP16 value the conversion defines, RNE16(RNE32(decode * k_scale)), for
-// any other k_scale.
+// KV_E4M3_PAGED_SCALED: for any other k_scale, each workgroup converts every
+// K code tile once, in LDS, into the FP16 values the conversion defines,
+// RNE16(RNE32(decode * k_scale)); V is decoded exactly in registers.
 // KV_FP8QK: dense attention whose queries and keys are E4M3 codes with an
 // FP32 scale per row (QK^T on the FP8 matrix cores, the row scales applied to
 // the FP32 scores); V, P and O are BF16.
