@@ -498,7 +498,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--iters", type=int, default=10, help="timed launches of each extra workload")
+    ap.add_argument("--iters", type=int, default=20, help="timed launches of each extra workload")
     ap.add_argument("--only", choices=["dense", "causal", "ragged", "paged", "prefix", "fp8", "vsa", "copy", "ceiling"],
                     default=None,
                     help="run one workload only (for profiling); 'copy' runs the plain 1 GiB "
