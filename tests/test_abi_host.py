@@ -417,3 +417,20 @@ def test_block_list_and_tile_mean_rejections():
     assert means(L=0) == fa.FA_ERR_SHAPE
     assert means(out=O + 4) == fa.FA_ERR_ALIGN
     assert means(out=A + 256) == fa.FA_ERR_ALIAS
+
+
+def test_abi_from_plain_c(tmp_path):
+    """include/fa16attn.h compiles as C99 (gcc -pedantic -Werror) and the library links and answers through
+    it: version, error strings, workspace queries and host-side rejections (tests/abi_c_check.c)."""
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    lib_dir = os.path.dirname(fa.LIB_PATH)
+    exe = str(tmp_path / "abi_c_check")
+    src = os.path.join(os.path.dirname(__file__), "abi_c_check.c")
+    inc = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+    subprocess.check_call([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", inc, src, "-L",
+                           lib_dir, "-l:libfa16attn.so", f"-Wl,-rpath,{lib_dir}", "-o", exe])
+    out = subprocess.run([exe], capture_output=True, text=True)
+    assert out.returncode == 0 and out.stdout.strip() == "OK", out.stdout + out.stderr
