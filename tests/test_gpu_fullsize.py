@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import synth.workloads as wl
-from parity_util import BF16_MAX_ABS, BF16_REL_L2, LSE_ABS, assert_close, sample_rows, say
+from parity_util import BF16_LSE_ABS, BF16_MAX_ABS, BF16_REL_L2, LSE_ABS, assert_close, sample_rows, say
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -158,3 +158,41 @@ def test_vsa_full(lib):
     ref, _ = oracle.attention(q, k, v, lib.default_scale(w["D"]), mode=oracle.MODE_BLOCKS, idx=ref_idx,
                               block=w["block"], dense_prefix=w["dense_prefix"], rows=rows)
     assert_close(_rows_of(out.cpu().numpy(), rows), ref, f"O ({len(rows)} rows)")
+
+
+def test_prefix_fp8_attention_full(lib):
+    """The FP8-QK prefix attention at the video shape the benchmark times (B1 H8 D128 Lq = Lkv = 36864,
+    BF16 N(0,1) operands): the E4M3 codes and row scales of all of Q and K bit-exact, sampled output rows
+    and their LSE within the BF16 bounds of FP64 attention over the dequantized values."""
+    import synth
+    w = wl.VIDEO_DENSE
+    B, H, L, D = w["B"], w["H"], w["Lq"], w["D"]
+    say("full FP8 prefix attention", B, H, L, D)
+    q = synth.normal_bf16(w["seed"], synth.TID_Q, (B, H, L, D))
+    k = synth.normal_bf16(w["seed"], synth.TID_K, (B, H, L, D))
+    v = synth.normal_bf16(w["seed"], synth.TID_V, (B, H, L, D))
+    as_bf16 = lambda x: torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    ws = torch.empty(lib.prefix_fp8_workspace(B, H, L, L), dtype=torch.uint8, device="cuda")
+    lse = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+    out = lib.attn_fwd_prefix_fp8(as_bf16(q), as_bf16(k), as_bf16(v), lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    qc, qs = oracle.fp8_quantize_rows(q)
+    kc, ks = oracle.fp8_quantize_rows(k)
+    wsn = ws.cpu().numpy()
+    n = B * H * L * D
+    pad = lambda x: (x + 255) // 256 * 256
+    assert np.array_equal(wsn[:n].reshape(qc.shape), qc), "Q codes differ"
+    assert np.array_equal(wsn[pad(n):pad(n) + n].reshape(kc.shape), kc), "K codes differ"
+    o0 = 2 * pad(n)
+    assert np.array_equal(wsn[o0:o0 + 4 * B * H * L].view(np.float32).reshape(qs.shape), qs), "Q scales differ"
+    o1 = o0 + pad(4 * B * H * L)
+    assert np.array_equal(wsn[o1:o1 + 4 * B * H * L].view(np.float32).reshape(ks.shape), ks), "K scales differ"
+    del wsn, ws
+    rows = sample_rows(B, H, L, 8, seed=9, tile=4096)
+    vd = (v.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref, ref_lse = oracle.attention(oracle.fp8_dequant(qc, qs), oracle.fp8_dequant(kc, ks), vd,
+                                    lib.default_scale(D), rows=rows)
+    got = out.float().cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]].astype(np.float64)
+    assert_close(got, ref, f"O ({len(rows)} rows)", BF16_MAX_ABS, BF16_REL_L2)
+    got_lse = lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert np.abs(got_lse - ref_lse).max() < BF16_LSE_ABS
