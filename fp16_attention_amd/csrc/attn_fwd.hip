@@ -1050,16 +1050,19 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
                 DL::issue_one(sg.v, dl.voff, vslot(PV{}), wave, j);
             }
         }
+        // P and PV of this tile first, then the scores of the next: the scores
+        // of the two tiles are never live together (fewer registers than the
+        // pipelined iteration needs)
+        h8 pk[KS];
+        exp_tile(scur, pk);
+        compute_pv(vslot(p), pk);
         f16x sn[NSB];
 #pragma unroll
         for (int kb = 0; kb < NSB; ++kb) sn[kb] = f16x{};
-        h8 pk[KS];
         if (it + 1 < n_tiles) {
             compute_s(ktile(PN{}), sn);
             kscale_tile(sn, kscl(PN{}) + wave * KT);
         }
-        exp_tile(scur, pk);
-        compute_pv(vslot(p), pk);
         if constexpr (KCONV) {
             // K(it+2) into the FP16 tile K(it) vacated (past the last tile the
             // codes are the zeros of an empty load; they are never used)
