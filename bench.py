@@ -3,7 +3,7 @@
 
     python bench.py [--steps K] [--warmup W] [--only NAME] [--no-cpu] [--no-extra]
 
-Headline (one step = one attn_fwd_dense launch over the whole workload): the
+Headline (one step = one attn_fwd_dense call over the whole workload): the
 dense non-causal D128 attention of a video diffusion transformer, B1 H8
 L36864, FP16 inputs N(0,1), FP32 accumulation, FP16 output. `value` is its
 algorithmic throughput, 4*D FLOP per (query, key) pair, in TFLOP/s.
@@ -566,8 +566,10 @@ def main():
                        "inputs": "N(0,1) FP16, counter-based generator seed 2"},
             "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": traffic,
-                         "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                         "kernel": "attn_fwd_kernel (dense, D128)", "launch_ms_mean": avg_ms,
+                         "traffic_unit": "HBM bytes per call, both kernels (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                         "kernel": "attn_fwd_kernel (dense, D128): the whole rounds, then the last half round "
+                                   "with each item's keys split between the halves of 8-wave workgroups",
+                         "launch_ms_mean": avg_ms,
                          "algorithmic_flop_per_launch": flop},
         }
         result["headline_stats"] = stats(ms)

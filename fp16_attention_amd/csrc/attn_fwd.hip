@@ -299,10 +299,15 @@ struct Tiling {
     static constexpr int PH = R;  // phases of the unrolled loop
 };
 
-template <int D, int WAVES, int SRC, int MODE, bool SPLIT>
-__global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kernel(const AttnArgs a)
+template <int D, int WAVES, int SRC, int MODE, bool SPLIT, bool HALVES = false>
+__global__ __launch_bounds__(WAVES * 64, (D == 128 && !HALVES ? 2 : 1)) void attn_fwd_kernel(const AttnArgs a)
 {
-    constexpr int M = WAVES * kRowsPerWave;
+    // HALVES: 8 waves over 128 rows; waves 0-3 stream keys [0, key_split),
+    // waves 4-7 keys [key_split, Lkv) for the same rows, through one ring whose
+    // slots hold both halves' tiles; the two states merge in LDS at the end
+    static_assert(!HALVES || (WAVES == 8 && SRC == KV_FP16 && MODE == KEYS_DENSE && !SPLIT), "dense halves");
+    constexpr int NHALF = HALVES ? 2 : 1;
+    constexpr int M = (WAVES / NHALF) * kRowsPerWave;
     constexpr int KT = Tiling<D, SRC, MODE>::KT;
     constexpr int NSB = KT / 32;  // 32-key score blocks per tile
     constexpr int KS = KT / 16;   // 16-key PV k-steps per tile
@@ -322,8 +327,8 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     constexpr int ROW = (VDIRECT ? 2 : 1) * D;      // bytes per LDS row of the V ring slots
     constexpr int KRROW = (DIRECT ? 2 : 1) * D;     // bytes per LDS row of the K ring slots
     constexpr int KROW = (DIRECT || KCONV ? 2 : 1) * D;  // bytes per row of the K operand tiles
-    constexpr int TB = KT * ROW;                    // V slot bytes
-    constexpr int TBK = KT * KRROW;                 // K slot bytes
+    constexpr int TB = NHALF * KT * ROW;            // V slot bytes
+    constexpr int TBK = NHALF * KT * KRROW;         // K slot bytes
     constexpr int R = Tiling<D, SRC, MODE>::R;
     // D = 256: the loads of a ring group are spread over the next iteration's
     // MFMA steps instead of being issued together after the barrier (the
@@ -355,8 +360,9 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     __shared__ __attribute__((aligned(1024))) unsigned char khalf1[KCONV ? KT * 2 * D : 16];
     // s_waitcnt that leaves the (ring depth - 2) most recent load groups in
     // flight (ring depth - 3 when K is converted a tile earlier)
-    constexpr int kGroupLoads = (DIRECT ? DirectLoader<D, WAVES, KT>::kLoads : ByteLoader<D, WAVES, KT>::kLoads) +
-                                (VDIRECT ? DirectLoader<D, WAVES, KT>::kLoads : ByteLoader<D, WAVES, KT>::kLoads) +
+    using DLT = DirectLoader<D, WAVES, NHALF * KT>;  // the FP16 tiles (both halves' with HALVES)
+    constexpr int kGroupLoads = (DIRECT ? DLT::kLoads : ByteLoader<D, WAVES, KT>::kLoads) +
+                                (VDIRECT ? DLT::kLoads : ByteLoader<D, WAVES, KT>::kLoads) +
                                 (F8 ? 1 : 0);
     constexpr int kVmLeft = (R - (KCONV ? 3 : 2)) * kGroupLoads;
     static_assert(kVmLeft < 64, "vmcnt range");
@@ -369,6 +375,8 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int hlf = lane >> 5;
+    const int half = HALVES ? wave >> 2 : 0;  // the half of the keys this wave streams
+    const int rwave = HALVES ? wave & 3 : wave;  // the wave's 32 rows within the tile
 
     // ---- work item -> (b, h, query tile, key range) ----------------------
     // (the decode every launcher and the host-side checker share)
@@ -381,9 +389,14 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     const int g = h / a.group;
     const int q0 = qt * M;
     // keys [key_begin, key_stop) are streamed; key_end bounds every row's keys
-    const int key_begin = wi.key_begin, key_stop = wi.key_stop, key_end = wi.key_end;
+    // (HALVES: this wave's half; both halves run the iterations of the first,
+    // the longer, and tiles past the second's keys are masked out)
+    const int key_begin = HALVES ? half * a.key_split : wi.key_begin;
+    const int key_stop = HALVES ? (half ? wi.key_stop : a.key_split) : wi.key_stop;
+    const int key_end = wi.key_end;
     const int32_t* blist = wi.list ? a.idx + (((int64_t)b * a.Hq + h) * a.nqb + qt) * a.topk : nullptr;
-    const int n_tiles = wi.list ? a.topk * (kTileN / KT) : (key_stop - key_begin + KT - 1) / KT;
+    const int n_tiles = wi.list ? a.topk * (kTileN / KT)
+                                : ((HALVES ? a.key_split : key_stop - key_begin) + KT - 1) / KT;
     const int key_last = key_end - 1;
     const int nblk = (a.Lkv + kTileN - 1) / kTileN;  // the last block may be partial
 
@@ -401,7 +414,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     const _Float16* kbase = nullptr;
     const _Float16* vbase = nullptr;
     const int32_t* table = nullptr;
-    DirectLoader<D, WAVES, KT> dl;
+    DLT dl;
     ByteLoader<D, WAVES, KT> bl;
     // F8: K codes and scales of this (b, kv head), contiguous rows of D codes
     const uint8_t* kcbase = nullptr;
@@ -435,6 +448,23 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         const int rows = ok ? min(KT, key_end - key0) : 0;
         bl.issue(cache + ((int64_t)page * 32 * a.Hkv + g) * D, rows * a.Hkv * D, slot, wave);
     };
+    // HALVES: a slot holds tile it of both halves, rows [0, KT) from keys
+    // it * KT and rows [KT, 2 KT) from keys key_split + it * KT. A wave's
+    // loads j < kLoads / 2 fill the first half's rows, the others the second's,
+    // read through a descriptor whose base is KT rows before that tile, so the
+    // loader's row offsets (of rows KT .. 2 KT - 1) land on it; rows past a
+    // half's keys read as zero.
+    auto issue_halves = [&](const _Float16* base, int64_t ss, const int* off, int it, unsigned char* slot) {
+        const bool ok = it < n_tiles;
+        const int k0 = ok ? it * KT : 0;
+        const int k1 = a.key_split + k0;
+        const int r0 = __builtin_amdgcn_readfirstlane(ok ? max(0, min(KT, a.key_split - k0)) : 0);
+        const int r1 = __builtin_amdgcn_readfirstlane(ok ? max(0, min(KT, key_end - k1)) : 0);
+        const __amdgpu_buffer_rsrc_t d0 = DLT::rsrc(base + (int64_t)k0 * ss, ss, r0);
+        const __amdgpu_buffer_rsrc_t d1 = DLT::rsrc(base + (int64_t)(k1 - KT) * ss, ss, KT + r1);
+#pragma unroll
+        for (int j = 0; j < DLT::kLoads; ++j) DLT::issue_one(j < DLT::kLoads / 2 ? d0 : d1, off, slot, wave, j);
+    };
     auto issue_k = [&](int it, unsigned char* slot) {
         if constexpr (F8) {
             // the tile's codes, and its keys' scales (each wave its own copy of
@@ -449,28 +479,30 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(sc + wave * KT), 4, lane * 4, 0, 0, 0);
         } else if constexpr (!DIRECT) {
             issue_b(a.kc, it, slot);
+        } else if constexpr (HALVES) {
+            issue_halves(kbase, a.k_ss, dl.koff, it, slot);
         } else {
             const bool ok = it < n_tiles;
             const int key0 = tile_key0(ok ? it : n_tiles - 1);
-            DirectLoader<D, WAVES, KT>::issue(kbase + (int64_t)key0 * a.k_ss, a.k_ss, dl.koff,
-                                              valid_rows(ok, key0), slot, wave);
+            DLT::issue(kbase + (int64_t)key0 * a.k_ss, a.k_ss, dl.koff, valid_rows(ok, key0), slot, wave);
         }
     };
     auto issue_v = [&](int it, unsigned char* slot) {
         if constexpr (!VDIRECT) {
             issue_b(a.vc, it, slot);
+        } else if constexpr (HALVES) {
+            issue_halves(vbase, a.v_ss, dl.voff, it, slot);
         } else {
             const bool ok = it < n_tiles;
             const int key0 = tile_key0(ok ? it : n_tiles - 1);
-            DirectLoader<D, WAVES, KT>::issue(vbase + (int64_t)key0 * a.v_ss, a.v_ss, dl.voff,
-                                              valid_rows(ok, key0), slot, wave);
+            DLT::issue(vbase + (int64_t)key0 * a.v_ss, a.v_ss, dl.voff, valid_rows(ok, key0), slot, wave);
         }
     };
 
     // ---- this lane's query row: head qh, position my_row ------------------------
     // Decode packs the group's heads: tile row r is head h + r / Lq, position
     // r % Lq; rows past the group are computed on a clamped head and dropped.
-    int my_row = q0 + wave * kRowsPerWave + l32, qh = h;
+    int my_row = q0 + rwave * kRowsPerWave + l32, qh = h;
     bool row_ok = my_row < a.Lq;
     if (MODE == KEYS_DECODE) {
         const int r = my_row, j = r / a.Lq;
@@ -539,12 +571,13 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         const int vrow = 4 * (grp >> 1) + (sl >> 2);
         const int vbyte = (sl & 1) * 8;
         const int vchunk = 2 * (grp & 1) + ((sl & 3) >> 1);
+        const int hoff = half * KT * ROW;  // HALVES: this half's rows of the slot
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) koff_s[kk] = tile_off<D>(l32, 2 * kk + hlf);
+        for (int kk = 0; kk < KK; ++kk) koff_s[kk] = tile_off<D>(l32, 2 * kk + hlf) + hoff;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            voff_a[db] = tile_off<D>(vrow, 4 * db + vchunk) + vbyte;
-            voff_b[db] = tile_off<D>(vrow + 8, 4 * db + vchunk) + vbyte;
+            voff_a[db] = tile_off<D>(vrow, 4 * db + vchunk) + vbyte + hoff;
+            voff_b[db] = tile_off<D>(vrow + 8, 4 * db + vchunk) + vbyte + hoff;
         }
     } else {
         const int vrow = 4 * (grp >> 1) + ((sl >> 1) & 3) + 8 * (sl >> 3);
@@ -1081,7 +1114,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
         const int64_t lim = min(a.offset + q0 + 1, (int64_t)key_end);  // keys every row of the tile sees
         n_plain = (int)max((int64_t)0, min((int64_t)n_tiles, (lim - key_begin) / KT));
     } else if (MODE == KEYS_DENSE) {
-        n_plain = key_end / KT;
+        n_plain = min(n_tiles, (key_end - key_begin) / KT);
     } else if (MODE == KEYS_BLOCKS && a.Lkv % kTileN != 0) {
         // a partial last block: a dense-prefix item's keys ascend, so only its
         // last tiles need the tail mask; a list may hold the partial block at
@@ -1112,7 +1145,43 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 ? 2 : 1)) void attn_fwd_kerne
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
     // ---- epilogue ------------------------------------------------------------
-    const float l_tot = wave_half_sum(l_run);
+    float l_tot = wave_half_sum(l_run);
+    if constexpr (HALVES) {
+        // the second half's waves leave O^T, the maximum and the row sum in the
+        // first K slots (16 KB of O per wave, lane-major float4s) and the
+        // first V slot; the first half's waves merge them into theirs:
+        // M = max(m0, m1), O = O0 2^(m0 - M) + O1 2^(m1 - M), l likewise
+        __syncthreads();  // every wave is done with the ring
+        float4* xo = (float4*)((rwave < 2 ? kslot0 : kslot1) + (rwave & 1) * 16384);
+        float2* xml = (float2*)vslot0 + rwave * 64;
+        if (half == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4)
+                    xo[(db * 4 + g4) * 64 + lane] = float4{oacc[db][4 * g4], oacc[db][4 * g4 + 1],
+                                                           oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
+            xml[lane] = float2{m_run, l_tot};
+        }
+        __syncthreads();
+        if (half == 1) return;
+        const float2 ml1 = xml[lane];
+        const float mx = fmaxf(m_run, ml1.x);
+        const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+        const float a1 = ml1.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml1.x - mx);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const float4 o1 = xo[(db * 4 + g4) * 64 + lane];
+                oacc[db][4 * g4] = oacc[db][4 * g4] * a0 + o1.x * a1;
+                oacc[db][4 * g4 + 1] = oacc[db][4 * g4 + 1] * a0 + o1.y * a1;
+                oacc[db][4 * g4 + 2] = oacc[db][4 * g4 + 2] * a0 + o1.z * a1;
+                oacc[db][4 * g4 + 3] = oacc[db][4 * g4 + 3] * a0 + o1.w * a1;
+            }
+        l_tot = l_tot * a0 + ml1.y * a1;
+        m_run = mx;
+    }
     if (!row_ok) return;
     const int64_t bh = (int64_t)b * a.Hq + qh;
     // block lists split only the dense-prefix query blocks
@@ -1278,6 +1347,17 @@ static hipError_t launch_one(const AttnArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Dense D = 128: the last partial round's items as 8-wave workgroups that
+// split each item's keys between their two halves.
+hipError_t launch_dense_halves(const AttnArgs& a, hipStream_t stream)
+{
+    int grid = a.per_xcd > 0 ? a.per_xcd * 8 : a.n_items;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL((attn_fwd_kernel<128, 8, KV_FP16, KEYS_DENSE, false, true>), dim3(grid), dim3(512), 0, stream,
+                       a);
+    return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_d(const AttnArgs& a, KvSource src, KeyMode mode, bool split,
                            hipStream_t stream)
@@ -1333,6 +1413,7 @@ hipError_t launch_attn(const AttnArgs& a, int D, KvSource src, KeyMode mode, boo
 // otherwise left the launch stubs of the paged E4M3 kernels undefined (the
 // shared library then fails to load), with no diagnostic.
 template __global__ void attn_fwd_kernel<128, 4, KV_FP16, KEYS_DENSE, false>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 8, KV_FP16, KEYS_DENSE, false, true>(const AttnArgs);
 template __global__ void attn_fwd_kernel<256, 4, KV_FP16, KEYS_DENSE, false>(const AttnArgs);
 template __global__ void attn_fwd_kernel<128, 4, KV_BF16, KEYS_DENSE, false>(const AttnArgs);
 template __global__ void attn_fwd_kernel<256, 4, KV_BF16, KEYS_DENSE, false>(const AttnArgs);

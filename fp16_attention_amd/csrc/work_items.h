@@ -54,6 +54,8 @@ struct Geometry {
     int topk;          // block lists: selected blocks per query block
     int n_items;       // work items
     int per_xcd;       // work items per XCD slice (0: identity mapping)
+    int item_base;     // added to each decoded item (a launch over a later range of a plan's items)
+    int key_split;     // dense halves: keys [0, key_split) and [key_split, Lkv) per work item (0: none)
 };
 
 // The work item of workgroup `block` (the XCD-aware mapping gives each of the
@@ -77,6 +79,7 @@ struct Item {
 // `rows` query rows (decode: packed rows).
 FA_HD inline Item decode_item(int mode, const Geometry& g, int item, int rows)
 {
+    item += g.item_base;
     Item it;
     it.seg = 0;
     it.list = false;
@@ -248,6 +251,7 @@ inline void clear_geometry(Geometry& g)
     g.B = g.Hq = g.Hkv = g.group = g.Lq = g.Lkv = 0;
     g.offset = 0;
     g.n_qt = g.nseg = g.part_lq = g.dense_prefix = g.nqb = g.topk = g.n_items = g.per_xcd = 0;
+    g.item_base = g.key_split = 0;
 }
 
 // Dense non-causal: one item per (b, h, 128-row query tile).
@@ -262,6 +266,30 @@ inline bool dense_geometry(Geometry& g, int B, int H, int Lq, int Lkv)
     g.n_qt = (Lq + kRowsPerTile - 1) / kRowsPerTile;
     g.nseg = 1;
     return set_items(g, (int64_t)B * H * g.n_qt, true);
+}
+
+// Dense D = 128, the last partial round (two workgroups per CU in the main
+// rounds). When the items leave at most half a round after the whole ones,
+// that rest runs as a launch of its own with 8-wave workgroups, each of whose
+// two 4-wave halves streams half of the keys for the same 128 rows (the
+// halves' states merge in LDS): two waves per SIMD again, each with half the
+// work, instead of a lone 4-wave workgroup per CU streaming every key.
+// `main` then covers the whole rounds and `tail` the rest; false (and `tail`
+// with no items) when the split does not apply.
+inline bool dense_tail_split(const Geometry& all, Geometry& main, Geometry& tail)
+{
+    tail = all;
+    tail.n_items = 0;
+    const int64_t slots = (int64_t)kComputeUnits * 2;
+    const int64_t rest = all.n_items % slots;
+    const int units = (all.Lkv + kTileN - 1) / kTileN;
+    if (rest == 0 || rest > slots / 2 || units < 2) return false;
+    main = all;
+    if (!set_items(main, all.n_items - rest, true)) return false;
+    if (!set_items(tail, rest, true)) return false;
+    tail.item_base = (int)(all.n_items - rest);
+    tail.key_split = seg_units(units, 2) * kTileN;
+    return true;
 }
 
 // Causal prefill (decode = false: one item per (b, query head, query tile,

@@ -29,6 +29,26 @@ def test_dense_items(shape):
     assert work_items.check("dense", *shape).startswith("OK")
 
 
+# dense shapes whose items leave a partial last round of at most half the
+# slots: the whole rounds, then the rest with each item's keys split in halves
+DENSE_TAIL = [(1, 8, 36864, 36864, 128), (1, 56, 15360, 29678, 128), (1, 4, 16640, 200, 128),
+              (1, 4, 16640, 130, 128), (1, 4, 16640, 65, 128), (1, 4, 16640, 4100, 128)]
+
+
+@pytest.mark.parametrize("shape", DENSE_TAIL)
+def test_dense_tail_items(shape):
+    assert work_items.check("dense_tail", *shape).startswith("OK")
+
+
+def test_dense_tail_split_applies_only_after_whole_rounds():
+    # fewer items than one round, a full last round, and a rest past half a
+    # round all keep the single launch
+    for shape in [(1, 2, 600, 4100, 128), (1, 8, 32768, 32768, 128), (1, 6, 16640, 4100, 128),
+                  (1, 4, 16640, 64, 128)]:
+        rc, out = work_items.run("dense_tail", *shape)
+        assert rc == 1 and "no split" in out, (shape, out)
+
+
 @pytest.mark.parametrize("shape", CAUSAL)
 def test_causal_items(shape):
     assert work_items.check("causal", *shape).startswith("OK")

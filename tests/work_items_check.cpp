@@ -11,6 +11,7 @@
 //   work_items_check causal B Hq Hkv D q_rows q_real kv_len
 //   work_items_check decode B Hq Hkv D q_rows q_real kv_len
 //   work_items_check blocks B H L D block topk dense_prefix
+//   work_items_check dense_tail B H Lq Lkv D   the whole rounds and the split rest
 //   [--list]  also print one line per item: b h qt seg key_begin key_stop key_end list empty
 //   [--decode-as MODE]  decode the items with another mode's decode (to show
 //                       that the checks catch a launcher/kernel mismatch)
@@ -37,6 +38,45 @@ static int fail(const char* what, int item, const Item& it)
     return 1;
 }
 
+// Dense with the last partial round split: the whole-round launch and the
+// rest launch together cover every item of the dense geometry once, each
+// launch's block map is a bijection, and the rest's two key halves tile
+// [0, Lkv) with the first no shorter than the second (both halves run the
+// first's iterations).
+static int check_dense_tail(const std::vector<long>& v)
+{
+    Geometry all, whole, rest;
+    if (!dense_geometry(all, (int)v[0], (int)v[1], (int)v[2], (int)v[3])) return printf("FAIL geometry\n"), 1;
+    if (!dense_tail_split(all, whole, rest)) return printf("FAIL no split\n"), 1;
+    if (whole.n_items % (2 * kComputeUnits) != 0) return printf("FAIL whole rounds\n"), 1;
+    std::vector<int> seen(all.n_items, 0);
+    for (const Geometry* g : {&whole, &rest}) {
+        const int grid = g->per_xcd > 0 ? g->per_xcd * 8 : g->n_items;
+        std::vector<int> hit(g->n_items, 0);
+        for (int blk = 0; blk < grid; ++blk) {
+            const int item = item_of_block(*g, blk);
+            if (item < 0) continue;
+            if (item >= g->n_items || hit[item]++) return printf("FAIL block map at block %d\n", blk), 1;
+            const Item it = decode_item(KEYS_DENSE, *g, item, kRowsPerTile);
+            if (it.b < 0 || it.b >= all.B || it.h < 0 || it.h >= all.Hq || it.qt < 0 || it.qt >= all.n_qt)
+                return fail("item out of range", item, it);
+            if (it.key_begin != 0 || it.key_stop != all.Lkv || it.key_end != all.Lkv)
+                return fail("key range", item, it);
+            const int idx = (it.b * all.Hq + it.h) * all.n_qt + it.qt;
+            if (seen[idx]++) return fail("item decoded twice", item, it);
+        }
+        for (int i = 0; i < g->n_items; ++i)
+            if (!hit[i]) return printf("FAIL item %d has no workgroup\n", i), 1;
+    }
+    for (int i = 0; i < all.n_items; ++i)
+        if (!seen[i]) return printf("FAIL dense item %d not covered\n", i), 1;
+    const int ks = rest.key_split;
+    if (ks <= 0 || ks >= all.Lkv || ks % kTileN) return printf("FAIL key split %d\n", ks), 1;
+    if (all.Lkv - ks > ks) return printf("FAIL second half longer than the first\n"), 1;
+    printf("OK %d + %d items, key split %d\n", whole.n_items, rest.n_items, ks);
+    return 0;
+}
+
 int main(int argc, char** argv)
 {
     if (argc < 2) return 2;
@@ -52,6 +92,7 @@ int main(int argc, char** argv)
         else
             v.push_back(atol(argv[i]));
     }
+    if (mode_s == "dense_tail" && v.size() == 5) return check_dense_tail(v);
     Geometry g;
     SplitPlan p{0, 1, 0};
     int mode, rows, D;
