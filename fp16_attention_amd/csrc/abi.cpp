@@ -206,12 +206,12 @@ int run_dense(fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse, in
     a.c = scale * 1.4426950408889634f;
     a.oscale = 1.f;
     AttnArgs whole = a, rest = a;
-    if (src == fa::KV_FP16 && D == 128 && fa::dense_tail_split(a, whole, rest)) {
+    if (D == 128 && fa::dense_tail_split(a, whole, rest)) {
         // the whole rounds, then the rest of the items with their keys split
         // between the halves of 8-wave workgroups
         const hipError_t e = fa::launch_attn(whole, D, src, fa::KEYS_DENSE, false, (hipStream_t)stream);
         if (e != hipSuccess) return hip_status(e);
-        return hip_status(fa::launch_dense_halves(rest, (hipStream_t)stream));
+        return hip_status(fa::launch_dense_halves(rest, src, (hipStream_t)stream));
     }
     return hip_status(fa::launch_attn(a, D, src, fa::KEYS_DENSE, false, (hipStream_t)stream));
 }

@@ -305,7 +305,8 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 && !HALVES ? 2 : 1)) void att
     // HALVES: 8 waves over 128 rows; waves 0-3 stream keys [0, key_split),
     // waves 4-7 keys [key_split, Lkv) for the same rows, through one ring whose
     // slots hold both halves' tiles; the two states merge in LDS at the end
-    static_assert(!HALVES || (WAVES == 8 && SRC == KV_FP16 && MODE == KEYS_DENSE && !SPLIT), "dense halves");
+    static_assert(!HALVES || (WAVES == 8 && (SRC == KV_FP16 || SRC == KV_BF16) && MODE == KEYS_DENSE && !SPLIT),
+                  "dense halves");
     constexpr int NHALF = HALVES ? 2 : 1;
     constexpr int M = (WAVES / NHALF) * kRowsPerWave;
     constexpr int KT = Tiling<D, SRC, MODE>::KT;
@@ -1349,12 +1350,18 @@ static hipError_t launch_one(const AttnArgs& a, hipStream_t stream)
 
 // Dense D = 128: the last partial round's items as 8-wave workgroups that
 // split each item's keys between their two halves.
-hipError_t launch_dense_halves(const AttnArgs& a, hipStream_t stream)
+hipError_t launch_dense_halves(const AttnArgs& a, KvSource src, hipStream_t stream)
 {
     int grid = a.per_xcd > 0 ? a.per_xcd * 8 : a.n_items;
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_fwd_kernel<128, 8, KV_FP16, KEYS_DENSE, false, true>), dim3(grid), dim3(512), 0, stream,
-                       a);
+    if (src == KV_BF16)
+        hipLaunchKernelGGL((attn_fwd_kernel<128, 8, KV_BF16, KEYS_DENSE, false, true>), dim3(grid), dim3(512), 0,
+                           stream, a);
+    else if (src == KV_FP16)
+        hipLaunchKernelGGL((attn_fwd_kernel<128, 8, KV_FP16, KEYS_DENSE, false, true>), dim3(grid), dim3(512), 0,
+                           stream, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -1414,6 +1421,7 @@ hipError_t launch_attn(const AttnArgs& a, int D, KvSource src, KeyMode mode, boo
 // shared library then fails to load), with no diagnostic.
 template __global__ void attn_fwd_kernel<128, 4, KV_FP16, KEYS_DENSE, false>(const AttnArgs);
 template __global__ void attn_fwd_kernel<128, 8, KV_FP16, KEYS_DENSE, false, true>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 8, KV_BF16, KEYS_DENSE, false, true>(const AttnArgs);
 template __global__ void attn_fwd_kernel<256, 4, KV_FP16, KEYS_DENSE, false>(const AttnArgs);
 template __global__ void attn_fwd_kernel<128, 4, KV_BF16, KEYS_DENSE, false>(const AttnArgs);
 template __global__ void attn_fwd_kernel<256, 4, KV_BF16, KEYS_DENSE, false>(const AttnArgs);

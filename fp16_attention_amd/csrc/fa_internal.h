@@ -97,9 +97,10 @@ int paged_decode_from(const WorkspaceSource* wsrc, const void* q, int64_t q_sb, 
 hipError_t launch_attn(const AttnArgs& a, int D, KvSource src, KeyMode mode, bool split,
                        hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& m, int D, hipStream_t stream);
-// Dense D = 128, FP16: the items of a geometry from dense_tail_split's tail,
-// each on an 8-wave workgroup whose halves split its keys at key_split.
-hipError_t launch_dense_halves(const AttnArgs& a, hipStream_t stream);
+// Dense D = 128, FP16 or BF16: the items of a geometry from
+// dense_tail_split's tail, each on an 8-wave workgroup whose halves split its
+// keys at key_split.
+hipError_t launch_dense_halves(const AttnArgs& a, KvSource src, hipStream_t stream);
 
 hipError_t launch_e4m3_bridge(const uint8_t* kc, const uint8_t* vc, const int32_t* table,
                               int64_t table_stride, int num_pages, int B, int Hkv, int D,

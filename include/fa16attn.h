@@ -94,8 +94,9 @@ const char* fa_error_string(int code);
  * scaled scores; NULL to skip.
  * Domain: B,H >= 1; Lq >= 0 (0 is a no-op); 1 <= Lkv; D in {128, 256};
  * B*H*ceil(Lq/128) < 2^31. o must not overlap q, k, v or lse.
- * At D = 128, when the 128-row query tiles fill whole rounds of the chip and
- * then at most half a round more, that rest is computed with each tile's
+ * At D = 128 (here and for BF16 operands), when the 128-row query tiles fill
+ * whole rounds of the chip and then at most half a round more, that rest is
+ * computed with each tile's
  * keys in two halves whose FP32 softmax states are merged (the same bounds
  * apply; the rounding order of those rows differs from one pass over the
  * keys). Two kernels run on the stream then.

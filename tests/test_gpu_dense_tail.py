@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import work_items
-from parity_util import LSE_ABS, assert_close, qkv, sample_rows, say
+from parity_util import BF16_LSE_ABS, BF16_MAX_ABS, BF16_REL_L2, LSE_ABS, assert_close, qkv, qkv_bf16, sample_rows, say
 from test_gpu_rescale_edges import check_guards, guarded_lse, guarded_out, plant
 
 torch = pytest.importorskip("torch")
@@ -92,3 +92,21 @@ def test_dense_tail_split_rescale(lib, case):
             j = (Lkv - 1 - n) if n % 2 == 0 else (ks - 1 - n)
             got = o.view[0, 3, i].double().cpu().numpy()
             assert np.abs(got - v[0, 3, j].astype(np.float64)).max() < 2e-3
+
+
+def test_dense_tail_split_bf16(lib):
+    """The same split on BF16 operands (P and O in BF16), at the BF16 bounds."""
+    Lkv = 4100
+    say(f"dense tail split bf16: Lkv {Lkv}, key split {key_split(Lkv)}")
+    q, k, v = qkv_bf16(43, B, H, LQ, Lkv, D)
+    rows = np.concatenate([split_rows(), sample_rows(B, H, LQ, 16, seed=43)])
+    o, lse = guarded_out(B, H, LQ, D, torch.bfloat16), guarded_lse(B, H, LQ)
+    dq, dk, dv = (dev(x.view(np.int16)).view(torch.bfloat16) for x in (q, k, v))
+    lib.attn_fwd_dense(dq, dk, dv, out=o.view, lse=lse.view)
+    torch.cuda.synchronize()
+    check_guards(o, lse)
+    ref, ref_lse = oracle.attention(q, k, v, lib.default_scale(D), bf16=True, rows=rows)
+    got = o.view.double().cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert_close(got, ref, f"bf16 O ({len(rows)} rows)", BF16_MAX_ABS, BF16_REL_L2)
+    got_lse = lse.view.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert np.abs(got_lse - ref_lse).max() < BF16_LSE_ABS
