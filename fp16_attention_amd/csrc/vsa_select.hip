@@ -14,8 +14,8 @@
 //   2. vsa_scores_kernel: s[i][j] = sum over d ascending of qbar[i][d] *
 //      kbar[j][d], one FP64 FMA chain per (i, j) (each FP32 x FP32 product is
 //      exact in FP64, so every step rounds exactly like "acc + product").
-//      A workgroup computes a 64 x 64 tile of one (b, h) with the means staged
-//      in LDS d-major; each thread keeps a 4 x 4 block of chains.
+//      A workgroup computes a 64 x 64 tile of one (b, h) on the FP64 matrix
+//      cores, whose 16x16x4 step is four such FMAs in ascending k.
 //   3. vsa_topk_kernel: one wave per query block. The scores are mapped to
 //      order-preserving 64-bit keys and a bitwise radix select finds the
 //      topk-th largest value T, stopping as soon as the keys that share T's
@@ -106,76 +106,94 @@ __global__ __launch_bounds__(256) void vsa_pool_kernel(const uint16_t* __restric
     }
 }
 
-// grid: (ceil(NB/64)^2, B*H); 256 threads. Thread t owns query blocks
-// i0 + 4*(t/16) .. +3 and key blocks j0 + t%16 + 16c, c < 4, of the tile.
-// The means are staged 32 dimensions at a time, widened to FP64 and d-major
-// (32 KB, four workgroups per CU). Both the staging writes (consecutive lanes,
-// consecutive blocks) and the key reads (consecutive lanes, consecutive
-// doubles) are free of LDS bank conflicts; the query reads are broadcasts.
-constexpr int kST = 64;  // score tile edge
-constexpr int kDC = 32;  // dimensions per staged chunk
+// grid: (ceil(NB/64)^2, B*H); 4 waves per 64 x 64 tile of one (b, h), each
+// wave a 32 x 32 quarter, on the FP64 matrix cores: each k-step feeds four
+// v_mfma_f64_16x16x4f64, one per 16 x 16 part of the quarter. That
+// instruction folds its four products into each output as four FMAs in
+// ascending k, so the 32 steps are the same ascending-d FMA chain per (i, j)
+// as an FP64 loop. The tile's 64 query means and 64 key means are staged in
+// LDS 64 dimensions at a time, as FP32 rows padded to 68 floats (35 KB, four
+// workgroups per CU), so the operand reads below hit 64 distinct banks. At
+// step s lane l supplies row l % 16, dimension 4 s + l / 16 of the A (query)
+// and B (key) operands, widened to FP64 exactly; output register r of lane l
+// is row l / 16 + 4 r, column l % 16.
+constexpr int kST = 64;       // score tile edge
+constexpr int kDC = 64;       // dimensions per staged chunk
+constexpr int kRowPad = 68;   // floats per staged row
 __global__ __launch_bounds__(256) void vsa_scores_kernel(const float* __restrict__ qbar,
                                                          const float* __restrict__ kbar, int NB,
                                                          double* __restrict__ scores)
 {
-    __shared__ __attribute__((aligned(16))) double qs[kDC][kST];  // qs[d][i]
-    __shared__ __attribute__((aligned(16))) double ks[kDC][kST];
-    const int tid = threadIdx.x;
+    typedef double d4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) float qs[kST][kRowPad];
+    __shared__ __attribute__((aligned(16))) float ks[kST][kRowPad];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tiles = (NB + kST - 1) / kST;
     const int i0 = (blockIdx.x / tiles) * kST, j0 = (blockIdx.x % tiles) * kST;
     const int64_t bh = blockIdx.y;
     const float* qb = qbar + bh * (int64_t)NB * kD;
     const float* kb = kbar + bh * (int64_t)NB * kD;
-    const int ti = 4 * (tid >> 4), tj = tid & 15;
-    const int sr = tid & 63, sd = (tid >> 6) * 8;  // staging: tile row sr, dimensions sd .. sd+7
-    double acc[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = 0.0;
+    const int rr = lane & 15, kq = lane >> 4;
+    const int qr = 32 * (wave >> 1) + rr, kr = 32 * (wave & 1) + rr;
+    d4 c00 = {0, 0, 0, 0}, c01 = c00, c10 = c00, c11 = c00;
     for (int d0 = 0; d0 < kD; d0 += kDC) {
-        if (d0 > 0) __syncthreads();  // every thread is done with the previous chunk
-        float4 qv0 = {0.f, 0.f, 0.f, 0.f}, qv1 = qv0, kv0 = qv0, kv1 = qv0;
-        if (i0 + sr < NB) {
-            const float* src = qb + (int64_t)(i0 + sr) * kD + d0 + sd;
-            qv0 = *(const float4*)src;
-            qv1 = *(const float4*)(src + 4);
-        }
-        if (j0 + sr < NB) {
-            const float* src = kb + (int64_t)(j0 + sr) * kD + d0 + sd;
-            kv0 = *(const float4*)src;
-            kv1 = *(const float4*)(src + 4);
-        }
-        const float qf[8] = {qv0.x, qv0.y, qv0.z, qv0.w, qv1.x, qv1.y, qv1.z, qv1.w};
-        const float kf[8] = {kv0.x, kv0.y, kv0.z, kv0.w, kv1.x, kv1.y, kv1.z, kv1.w};
+        if (d0 > 0) __syncthreads();  // every wave is done with the previous chunk
+        // 64 rows x 16 float4 per tensor, 4 per thread each; rows past NB are
+        // zeros (their scores are not written)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            qs[sd + e][sr] = qf[e];
-            ks[sd + e][sr] = kf[e];
+        for (int u = 0; u < 4; ++u) {
+            const int e = tid + 256 * u;  // float4 index in the 64 x 16 grid
+            const int r = e >> 4, c4 = e & 15;
+            float4 qv = {0.f, 0.f, 0.f, 0.f}, kv = qv;
+            if (i0 + r < NB) qv = *(const float4*)(qb + (int64_t)(i0 + r) * kD + d0 + 4 * c4);
+            if (j0 + r < NB) kv = *(const float4*)(kb + (int64_t)(j0 + r) * kD + d0 + 4 * c4);
+            *(float4*)&qs[r][4 * c4] = qv;
+            *(float4*)&ks[r][4 * c4] = kv;
         }
         __syncthreads();
-#pragma unroll 4
-        for (int d = 0; d < kDC; ++d) {
-            const double2 q01 = *(const double2*)&qs[d][ti], q23 = *(const double2*)&qs[d][ti + 2];
-            const double qd[4] = {q01.x, q01.y, q23.x, q23.y};
-            double kd[4];
+        // the operands of step s + 2 are read while the MFMAs of step s issue
+        constexpr int kSteps = kDC / 4, kAhead = 2;
+        float op[kAhead][4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) kd[c] = ks[d][tj + 16 * c];
+        for (int t = 0; t < kAhead; ++t) {
+            op[t][0] = qs[qr][4 * t + kq];
+            op[t][1] = qs[qr + 16][4 * t + kq];
+            op[t][2] = ks[kr][4 * t + kq];
+            op[t][3] = ks[kr + 16][4 * t + kq];
+        }
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc[a][c] = fma(qd[a], kd[c], acc[a][c]);
+        for (int st = 0; st < kSteps; ++st) {
+            const int slot = st % kAhead;
+            const double a0 = op[slot][0], a1 = op[slot][1], b0 = op[slot][2], b1 = op[slot][3];
+            if (st + kAhead < kSteps) {
+                const int k0 = 4 * (st + kAhead);
+                op[slot][0] = qs[qr][k0 + kq];
+                op[slot][1] = qs[qr + 16][k0 + kq];
+                op[slot][2] = ks[kr][k0 + kq];
+                op[slot][3] = ks[kr + 16][k0 + kq];
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this step's MFMAs
+            c00 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, c00, 0, 0, 0);
+            c01 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, c01, 0, 0, 0);
+            c10 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, c10, 0, 0, 0);
+            c11 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, c11, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+    const int col = lane & 15, rq = lane >> 4;
+    auto put = [&](const d4& c, int ti, int tj) {
+        const int j = j0 + 32 * (wave & 1) + 16 * tj + col;
+        if (j >= NB) return;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int i = i0 + ti + a;
-        if (i >= NB) continue;
-        double* row = scores + (bh * NB + i) * (int64_t)NB;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (j0 + tj + 16 * c < NB) row[j0 + tj + 16 * c] = acc[a][c];
-    }
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 32 * (wave >> 1) + 16 * ti + rq + 4 * r;
+            if (i < NB) scores[(bh * NB + i) * (int64_t)NB + j] = c[r];
+        }
+    };
+    put(c00, 0, 0);
+    put(c01, 0, 1);
+    put(c10, 1, 0);
+    put(c11, 1, 1);
 }
 
 // Order-preserving map of a double to uint64 (larger value -> larger key);
