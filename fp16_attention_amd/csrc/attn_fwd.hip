@@ -1269,19 +1269,22 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const MergeArgs m)
     if (m.lse && lane == 0) m.lse[bh * m.lse_sh + i] = (mmax + __log2f(den)) * 0.69314718055994530942f;
 }
 
-// The same merge for splits with many segments (decode): one workgroup per
-// (query row, 64 output columns). The segment weights 2^(m_s - M) are formed
-// once in LDS; wave w then sums segments w, w + 4, ... for its lane's column,
-// and the four partial sums are added in wave order, so the result is still
-// fixed run to run.
+// The same merge for splits with many segments (decode): one 1024-thread
+// workgroup per query row. The segment weights 2^(m_s - M) are formed once in
+// LDS; then the threads split into streams of D / 4 threads, each thread one
+// float4 of columns, stream t summing segments t, t + S, t + 2S, ... (S
+// streams), so every load of a stream reads one whole partial row; the S
+// partial sums are added in stream order, so the result is fixed run to run.
 constexpr int kWideMaxSeg = 1024;
+constexpr int kWideThreads = 1024;
 template <int D>
-__global__ __launch_bounds__(256) void attn_merge_wide_kernel(const MergeArgs m)
+__global__ __launch_bounds__(kWideThreads) void attn_merge_wide_kernel(const MergeArgs m)
 {
+    constexpr int TPR = D / 4;                  // threads per stream
+    constexpr int S = kWideThreads / TPR;       // streams
+    constexpr int W = kWideThreads / 64;        // waves
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    constexpr int NCH = D / 64;
-    const int64_t row_id = blockIdx.x / NCH;
-    const int col = (blockIdx.x % NCH) * 64 + lane;
+    const int64_t row_id = blockIdx.x;
     const int i = (int)(row_id % m.Lq);
     const int64_t bh = row_id / m.Lq;
     const int b = (int)(bh / m.Hq), h = (int)(bh % m.Hq);
@@ -1294,11 +1297,11 @@ __global__ __launch_bounds__(256) void attn_merge_wide_kernel(const MergeArgs m)
     const int64_t seg_stride = (int64_t)m.B * m.Hq * m.Lq;
 
     __shared__ float wgt[kWideMaxSeg];
-    __shared__ float red[4];
-    __shared__ float part[4][64];
+    __shared__ float red[W];
+    __shared__ float4 part[S][TPR];
     // M = max of the segment maxima
     float mx = -INFINITY;
-    for (int s = tid; s < nseg; s += 256) {
+    for (int s = tid; s < nseg; s += kWideThreads) {
         const float ms = m.ml_part[(s * seg_stride + row_id) * 2];
         wgt[s] = ms;
         mx = fmaxf(mx, ms);
@@ -1307,11 +1310,13 @@ __global__ __launch_bounds__(256) void attn_merge_wide_kernel(const MergeArgs m)
     for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     if (lane == 0) red[wave] = mx;
     __syncthreads();
-    const float mmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float mmax = red[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) mmax = fmaxf(mmax, red[w]);
     __syncthreads();
     // weights, and sum w_s l_s (each thread its segments, then in wave order)
     float den = 0.f;
-    for (int s = tid; s < nseg; s += 256) {
+    for (int s = tid; s < nseg; s += kWideThreads) {
         const float ls = m.ml_part[(s * seg_stride + row_id) * 2 + 1];
         const float w = ls == 0.f ? 0.f : __builtin_amdgcn_exp2f(wgt[s] - mmax);  // no visible key: no weight
         wgt[s] = w;
@@ -1321,18 +1326,40 @@ __global__ __launch_bounds__(256) void attn_merge_wide_kernel(const MergeArgs m)
     for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
     if (lane == 0) red[wave] = den;
     __syncthreads();
-    const float dsum = ((red[0] + red[1]) + red[2]) + red[3];
+    float dsum = red[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) dsum += red[w];
 
-    float acc = 0.f;
-    const float* op = m.o_part + row_id * D + col;
-#pragma unroll 8
-    for (int s = wave; s < nseg; s += 4) acc += wgt[s] * op[s * seg_stride * D];
-    part[wave][lane] = acc;
+    const int st = tid / TPR, c = tid % TPR;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    const float4* op = (const float4*)(m.o_part + row_id * D) + c;
+#pragma unroll 4
+    for (int s = st; s < nseg; s += S) {
+        const float4 v = op[s * seg_stride * (D / 4)];
+        const float w = wgt[s];
+        acc.x += w * v.x;
+        acc.y += w * v.y;
+        acc.z += w * v.z;
+        acc.w += w * v.w;
+    }
+    part[st][c] = acc;
     __syncthreads();
-    if (wave != 0) return;
-    const float sum = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
-    m.o[(int64_t)b * m.o_sb + (int64_t)h * m.o_sh + (int64_t)i * m.o_ss + col] = (_Float16)(sum * (m.oscale / dsum));
-    if (m.lse && col == 0) m.lse[bh * m.lse_sh + i] = (mmax + __log2f(dsum)) * 0.69314718055994530942f;
+    if (st != 0) return;
+    float4 sum = part[0][c];
+#pragma unroll
+    for (int t = 1; t < S; ++t) {
+        sum.x += part[t][c].x;
+        sum.y += part[t][c].y;
+        sum.z += part[t][c].z;
+        sum.w += part[t][c].w;
+    }
+    const float inv = m.oscale / dsum;
+    _Float16* o = m.o + (int64_t)b * m.o_sb + (int64_t)h * m.o_sh + (int64_t)i * m.o_ss + 4 * c;
+    o[0] = (_Float16)(sum.x * inv);
+    o[1] = (_Float16)(sum.y * inv);
+    o[2] = (_Float16)(sum.z * inv);
+    o[3] = (_Float16)(sum.w * inv);
+    if (m.lse && c == 0) m.lse[bh * m.lse_sh + i] = (mmax + __log2f(dsum)) * 0.69314718055994530942f;
 }
 
 // ---------------------------------------------------------------------------
@@ -1449,13 +1476,13 @@ hipError_t launch_merge(const MergeArgs& m, int D, hipStream_t stream)
 {
     int64_t rows = (int64_t)m.B * m.Hq * m.Lq;
     if (m.nseg >= 16) {
-        // many segments per row: a workgroup per (row, 64 columns)
+        // many segments per row: a workgroup per row
         if (rows <= 0) return hipSuccess;
-        if (m.nseg > kWideMaxSeg || rows * (D / 64) > 0x7fffffff) return hipErrorInvalidValue;
+        if (m.nseg > kWideMaxSeg || rows > 0x7fffffff) return hipErrorInvalidValue;
         if (D == 128)
-            hipLaunchKernelGGL(attn_merge_wide_kernel<128>, dim3((unsigned)(rows * 2)), dim3(256), 0, stream, m);
+            hipLaunchKernelGGL(attn_merge_wide_kernel<128>, dim3((unsigned)rows), dim3(kWideThreads), 0, stream, m);
         else if (D == 256)
-            hipLaunchKernelGGL(attn_merge_wide_kernel<256>, dim3((unsigned)(rows * 4)), dim3(256), 0, stream, m);
+            hipLaunchKernelGGL(attn_merge_wide_kernel<256>, dim3((unsigned)rows), dim3(kWideThreads), 0, stream, m);
         else
             return hipErrorInvalidValue;
         return hipGetLastError();
