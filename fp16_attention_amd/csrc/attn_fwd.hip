@@ -137,8 +137,21 @@ __device__ __forceinline__ int tile_off(int row, int chunk)
     return row * (2 * D) + ((chunk ^ swz(row & 15)) << 4);
 }
 
-__device__ __forceinline__ float wave_half_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float wave_half_sum(float x) { return x + __shfl_xor(x, 32); }
+// Lanes l and l ^ 32 hold the same query row. v_permlane32_swap trades the
+// upper half of one register with the lower half of another; applied to two
+// copies of x it leaves x of lanes 0-31 in the first and x of lanes 32-63 in
+// the second, in every lane, without the LDS round trip of a bpermute. The
+// elements are copied out before the bit casts: a bit cast of a vector
+// element expression reads element 0.
+__device__ __forceinline__ float2 half_pair(float x)
+{
+    const unsigned a = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+    const unsigned lo = r[0], hi = r[1];
+    return {__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi)};
+}
+__device__ __forceinline__ float wave_half_max(float x) { const float2 p = half_pair(x); return fmaxf(p.x, p.y); }
+__device__ __forceinline__ float wave_half_sum(float x) { const float2 p = half_pair(x); return p.x + p.y; }
 
 // Three-input maximum; the compiler emits one v_max3_f32 per call. It must
 // stay compiled code (no inline asm): the scores it reads come straight from
@@ -999,11 +1012,11 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 && !HALVES ? 2 : 1)) void att
 
         // ---- block C ----
         __builtin_amdgcn_sched_barrier(0);
-        float macc = -INFINITY, mpart = -INFINITY;
+        float macc = -INFINITY, mfull = -INFINITY;
         constexpr int NMX = 8 * NSB;  // max3 units: two scores each
         // Steps carrying the max units. With one wave per SIMD (D = 256) the
-        // maximum is finished in the first half of the block and its lane-half
-        // exchange is issued there, so the remaining MFMAs cover its latency;
+        // maximum is finished, and exchanged between the lane halves, in the
+        // first half of the block, so the remaining MFMAs cover its latency;
         // with two waves per SIMD (D = 128) the other wave covers it, and the
         // units are better spread over the whole block.
         constexpr bool XCHG_EARLY = D == 256;
@@ -1063,10 +1076,10 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 && !HALVES ? 2 : 1)) void att
                     macc = vmax3(macc, sn[e / 16][e % 16], sn[(e + 1) / 16][(e + 1) % 16]);
                 }
             }
-            if (XCHG_EARLY && i == MX0 + MXS - 1) mpart = __shfl_xor(macc, 32);
+            if (XCHG_EARLY && i == MX0 + MXS - 1) mfull = wave_half_max(macc);
             __builtin_amdgcn_sched_barrier(0);
         }
-        raise_max((XCHG_EARLY ? fmaxf(macc, mpart) : wave_half_max(macc)) * crow);
+        raise_max((XCHG_EARLY ? mfull : wave_half_max(macc)) * crow);
         refill(p, it);
 #pragma unroll
         for (int kb = 0; kb < NSB; ++kb) scur[kb] = sn[kb];
