@@ -1142,6 +1142,22 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 && !HALVES ? 2 : 1)) void att
         if constexpr (PH > 2) iteration_main(P2{}, it + 2);
         if constexpr (PH > 3) iteration_main(P3{}, it + 3);
     }
+    if constexpr (MODE == KEYS_DECODE) {
+        // short items: every plain tile whose successor is plain takes the
+        // pipelined path, not only those of whole unrolled rounds
+        for (; it + 1 < n_plain; ++it) {
+            const int ph = it % PH;
+            if (ph == 0)
+                iteration_main(P0{}, it);
+            else if (ph == 1)
+                iteration_main(P1{}, it);
+            else if (ph == 2) {
+                if constexpr (PH > 2) iteration_main(P2{}, it);
+            } else {
+                if constexpr (PH > 3) iteration_main(P3{}, it);
+            }
+        }
+    }
     for (; it < n_tiles; ++it) {
         const int ph = it % PH;
         if (ph == 0)
