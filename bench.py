@@ -322,6 +322,19 @@ def bench_paged(fa, torch, iters, timer, flush):
     decode = {"workload": wd["name"] + f" k_scale={ks:.6g} v_scale={vs:.6g}", "bytes": nb, **stats(ms),
               "gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS, "llc_flushed": True,
               "workspace_bytes": int(ws_d.numel())}
+    # the same cache decoded for one new position per head (6 packed rows: the
+    # one-wave workgroups), timing only
+    q1 = qd[:, :, :1].contiguous()
+    ws_1 = torch.empty(fa.load().attn_fwd_paged_e4m3_decode_workspace(wd["B"], wd["Hq"], wd["Hkv"], wd["D"], 1,
+                                                                       wd["kv_len"]),
+                       dtype=torch.uint8, device="cuda")
+    o1 = torch.empty_like(q1)
+    fn = lambda: fa.attn_fwd_paged_e4m3_decode(q1, dkc, dvc, dt, wd["kv_len"], 1, ks, vs, out=o1, workspace=ws_1)
+    ms1, _ = timer.run(fn, iters, 2, flush=flush)
+    gbs1 = nb / (np.median(ms1) * 1e-3) / 1e9
+    log(f"paged decode, one position: {np.median(ms1) * 1e3:.1f} us  {gbs1:.0f} GB/s")
+    decode["one_position"] = {"q_rows": 1, **stats(ms1), "gbs": gbs1, "frac_hbm_peak": gbs1 / HBM_PEAK_GBS,
+                              "workspace_bytes": int(ws_1.numel())}
     return fused, bridge, decode
 
 

@@ -295,7 +295,7 @@ struct ByteLoader {
 // of 32-key pages (32 KB at D = 256; two for decode), decoded in registers as
 // operands.
 // ---------------------------------------------------------------------------
-template <int D, int SRC, int MODE>
+template <int D, int SRC, int MODE, bool KREG = false>
 struct Tiling {
     // dense D = 128: 64-key tiles in a two-slot ring (half the barriers and
     // per-tile overhead of 32-key tiles, same LDS, two workgroups per CU).
@@ -305,15 +305,18 @@ struct Tiling {
     static constexpr int KT = WIDE ? 64 : 32;
     // decode items stream only a few dozen tiles each: there the two-slot
     // ring's shorter unrolled loop measured faster than four slots
-    // (the scaled E4M3 source converts K two tiles ahead, so it needs four)
+    // (the scaled E4M3 source converts K two tiles ahead, so it needs four,
+    // unless its small decode workgroups convert K in registers)
     static constexpr int R = WIDE ? 2
-                             : (SRC == KV_E4M3_PAGED_SCALED || (MODE != KEYS_BLOCKS && MODE != KEYS_DECODE)) ? 4
-                                                                                                              : 2;
+                             : ((SRC == KV_E4M3_PAGED_SCALED && !KREG) || (MODE != KEYS_BLOCKS && MODE != KEYS_DECODE))
+                                 ? 4
+                                 : 2;
     static constexpr int PH = R;  // phases of the unrolled loop
 };
 
 template <int D, int WAVES, int SRC, int MODE, bool SPLIT, bool HALVES = false>
-__global__ __launch_bounds__(WAVES * 64, (D == 128 && !HALVES ? 2 : 1)) void attn_fwd_kernel(const AttnArgs a)
+__global__ __launch_bounds__(WAVES * 64, (D == 128 && !HALVES ? 2 : 1) * (WAVES < 4 ? 4 / WAVES : 1))
+void attn_fwd_kernel(const AttnArgs a)
 {
     // HALVES: 8 waves over 128 rows; waves 0-3 stream keys [0, key_split),
     // waves 4-7 keys [key_split, Lkv) for the same rows, through one ring whose
@@ -336,14 +339,20 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 && !HALVES ? 2 : 1)) void att
     constexpr bool DIRECT = VDIRECT && !F8;
     // The scaled E4M3 source converts each K code tile once per workgroup into
     // an FP16 tile (each wave a quarter of it, between its PV MFMAs), from
-    // which every wave reads its K operands as the 16-bit sources do.
-    constexpr bool KCONV = SRC == KV_E4M3_PAGED_SCALED;
+    // which every wave reads its K operands as the 16-bit sources do. Decode
+    // workgroups of one or two waves (a few packed rows) instead convert the
+    // K operands in registers where the MFMAs consume them, as V is decoded:
+    // with so few waves the shared tile saves little, and without its FP16
+    // slots and deeper ring four such workgroups fit a CU's LDS.
+    constexpr bool KREG = SRC == KV_E4M3_PAGED_SCALED && WAVES < 4;
+    constexpr bool KCONV = SRC == KV_E4M3_PAGED_SCALED && !KREG;
+    static_assert(!KREG || MODE == KEYS_DECODE, "register-converted K: decode only");
     constexpr int ROW = (VDIRECT ? 2 : 1) * D;      // bytes per LDS row of the V ring slots
     constexpr int KRROW = (DIRECT ? 2 : 1) * D;     // bytes per LDS row of the K ring slots
     constexpr int KROW = (DIRECT || KCONV ? 2 : 1) * D;  // bytes per row of the K operand tiles
     constexpr int TB = NHALF * KT * ROW;            // V slot bytes
     constexpr int TBK = NHALF * KT * KRROW;         // K slot bytes
-    constexpr int R = Tiling<D, SRC, MODE>::R;
+    constexpr int R = Tiling<D, SRC, MODE, KREG>::R;
     // D = 256: the loads of a ring group are spread over the next iteration's
     // MFMA steps instead of being issued together after the barrier (the
     // tile's bytes then arrive in LDS spread out too; measured 3-4% faster on
@@ -351,7 +360,7 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 && !HALVES ? 2 : 1)) void att
     constexpr bool SPREAD = DIRECT && D == 256;
     // P, the PV product and O in BF16
     constexpr bool BF = SRC == KV_BF16 || F8;
-    constexpr int PH = Tiling<D, SRC, MODE>::PH;
+    constexpr int PH = Tiling<D, SRC, MODE, KREG>::PH;
     static_assert(R >= 2 && R <= 4, "ring depth");
     static_assert(VDIRECT || KT == 32, "an E4M3 tile is one 32-token page");
     static_assert(!F8 || (D == 128 && KT == 64 && R == 2 && MODE == KEYS_DENSE), "FP8 source: dense D128");
@@ -644,12 +653,20 @@ __global__ __launch_bounds__(WAVES * 64, (D == 128 && !HALVES ? 2 : 1)) void att
         return __builtin_bit_cast(uint32_t, h2{(_Float16)x0, (_Float16)x1});
     };
     auto opuse_k = [&](const KRawK& r) -> h8 {
-        if constexpr (DIRECT || KCONV)
+        if constexpr (DIRECT || KCONV) {
             return r;
-        else if constexpr (F8)
+        } else if constexpr (F8) {
             return h8{};  // unused: F8 codes go to the FP8 MFMA as they are
-        else
+        } else if constexpr (KREG) {
+            // the 8 codes' converted values, in the order decode8 gives
+            const u4 w = {convert2(__builtin_amdgcn_cvt_pk_f32_fp8(r.x, false)),
+                          convert2(__builtin_amdgcn_cvt_pk_f32_fp8(r.x, true)),
+                          convert2(__builtin_amdgcn_cvt_pk_f32_fp8(r.y, false)),
+                          convert2(__builtin_amdgcn_cvt_pk_f32_fp8(r.y, true))};
+            return __builtin_bit_cast(h8, w);
+        } else {
             return decode8(r);
+        }
     };
     // Conversion of one K code tile into its FP16 tile, in 16-code chunks:
     // wave w converts chunks (w + WAVES * j) * 64 + lane, j < CV. A chunk is
@@ -1298,22 +1315,26 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const MergeArgs m)
     if (m.lse && lane == 0) m.lse[bh * m.lse_sh + i] = (mmax + __log2f(den)) * 0.69314718055994530942f;
 }
 
-// The same merge for splits with many segments (decode): one 1024-thread
-// workgroup per query row. The segment weights 2^(m_s - M) are formed once in
-// LDS; then the threads split into streams of D / 4 threads, each thread one
-// float4 of columns, stream t summing segments t, t + S, t + 2S, ... (S
-// streams), so every load of a stream reads one whole partial row; the S
+// The same merge for splits with many segments (decode): one 256-thread
+// workgroup per (query row, COLS columns), so that a decode of a few rows
+// still spreads over the CUs (COLS = 16 then, else 64). Its threads split into
+// streams of COLS / 4 threads, each thread one float4 of the columns, stream t
+// summing segments t, t + S, t + 2S, ... (S streams) in that order. Each
+// thread issues its first kPre partial loads before the segment weights
+// 2^(m_s - M) are formed in LDS, so that the two latencies overlap; the S
 // partial sums are added in stream order, so the result is fixed run to run.
-constexpr int kWideMaxSeg = 1024;
-constexpr int kWideThreads = 1024;
-template <int D>
+constexpr int kWideMaxSeg = kMaxDecodeSeg;
+constexpr int kWideThreads = 256;
+template <int D, int COLS>
 __global__ __launch_bounds__(kWideThreads) void attn_merge_wide_kernel(const MergeArgs m)
 {
-    constexpr int TPR = D / 4;                  // threads per stream
-    constexpr int S = kWideThreads / TPR;       // streams
+    constexpr int TPS = COLS / 4;               // threads per stream
+    constexpr int S = kWideThreads / TPS;       // streams
     constexpr int W = kWideThreads / 64;        // waves
+    constexpr int kPre = 1024 / S < 16 ? 1024 / S : 16;  // partial loads per thread and round
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t row_id = blockIdx.x;
+    const int col0 = blockIdx.y * COLS;
     const int i = (int)(row_id % m.Lq);
     const int64_t bh = row_id / m.Lq;
     const int b = (int)(bh / m.Hq), h = (int)(bh % m.Hq);
@@ -1325,15 +1346,29 @@ __global__ __launch_bounds__(kWideThreads) void attn_merge_wide_kernel(const Mer
     const int nseg = (nt + su - 1) / su;  // <= kWideMaxSeg (checked at launch)
     const int64_t seg_stride = (int64_t)m.B * m.Hq * m.Lq;
 
+    const int st = tid / TPS, c = tid % TPS;
+    const float4* op = (const float4*)(m.o_part + row_id * D + col0) + c;
+    float4 v[kPre];
+    auto load_round = [&](int base) {
+#pragma unroll
+        for (int j = 0; j < kPre; ++j) {
+            const int sg = base + st + S * j;
+            if (sg < nseg) v[j] = op[sg * seg_stride * (D / 4)];
+        }
+    };
+    load_round(0);
+
     __shared__ float wgt[kWideMaxSeg];
+    __shared__ float lsg[kWideMaxSeg];
     __shared__ float red[W];
-    __shared__ float4 part[S][TPR];
+    __shared__ float4 part[S][TPS];
     // M = max of the segment maxima
     float mx = -INFINITY;
-    for (int s = tid; s < nseg; s += kWideThreads) {
-        const float ms = m.ml_part[(s * seg_stride + row_id) * 2];
-        wgt[s] = ms;
-        mx = fmaxf(mx, ms);
+    for (int sg = tid; sg < nseg; sg += kWideThreads) {
+        const float2 ml = *(const float2*)(m.ml_part + (sg * seg_stride + row_id) * 2);
+        wgt[sg] = ml.x;
+        lsg[sg] = ml.y;
+        mx = fmaxf(mx, ml.x);
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
@@ -1345,10 +1380,10 @@ __global__ __launch_bounds__(kWideThreads) void attn_merge_wide_kernel(const Mer
     __syncthreads();
     // weights, and sum w_s l_s (each thread its segments, then in wave order)
     float den = 0.f;
-    for (int s = tid; s < nseg; s += kWideThreads) {
-        const float ls = m.ml_part[(s * seg_stride + row_id) * 2 + 1];
-        const float w = ls == 0.f ? 0.f : __builtin_amdgcn_exp2f(wgt[s] - mmax);  // no visible key: no weight
-        wgt[s] = w;
+    for (int sg = tid; sg < nseg; sg += kWideThreads) {
+        const float ls = lsg[sg];
+        const float w = ls == 0.f ? 0.f : __builtin_amdgcn_exp2f(wgt[sg] - mmax);  // no visible key: no weight
+        wgt[sg] = w;
         den += w * ls;
     }
 #pragma unroll
@@ -1359,17 +1394,20 @@ __global__ __launch_bounds__(kWideThreads) void attn_merge_wide_kernel(const Mer
 #pragma unroll
     for (int w = 1; w < W; ++w) dsum += red[w];
 
-    const int st = tid / TPR, c = tid % TPR;
     float4 acc = {0.f, 0.f, 0.f, 0.f};
-    const float4* op = (const float4*)(m.o_part + row_id * D) + c;
-#pragma unroll 4
-    for (int s = st; s < nseg; s += S) {
-        const float4 v = op[s * seg_stride * (D / 4)];
-        const float w = wgt[s];
-        acc.x += w * v.x;
-        acc.y += w * v.y;
-        acc.z += w * v.z;
-        acc.w += w * v.w;
+    for (int base = 0; base < nseg; base += S * kPre) {
+        if (base > 0) load_round(base);
+#pragma unroll
+        for (int j = 0; j < kPre; ++j) {
+            const int sg = base + st + S * j;
+            if (sg < nseg) {
+                const float w = wgt[sg];
+                acc.x += w * v[j].x;
+                acc.y += w * v[j].y;
+                acc.z += w * v[j].z;
+                acc.w += w * v[j].w;
+            }
+        }
     }
     part[st][c] = acc;
     __syncthreads();
@@ -1383,12 +1421,12 @@ __global__ __launch_bounds__(kWideThreads) void attn_merge_wide_kernel(const Mer
         sum.w += part[t][c].w;
     }
     const float inv = m.oscale / dsum;
-    _Float16* o = m.o + (int64_t)b * m.o_sb + (int64_t)h * m.o_sh + (int64_t)i * m.o_ss + 4 * c;
+    _Float16* o = m.o + (int64_t)b * m.o_sb + (int64_t)h * m.o_sh + (int64_t)i * m.o_ss + col0 + 4 * c;
     o[0] = (_Float16)(sum.x * inv);
     o[1] = (_Float16)(sum.y * inv);
     o[2] = (_Float16)(sum.z * inv);
     o[3] = (_Float16)(sum.w * inv);
-    if (m.lse && c == 0) m.lse[bh * m.lse_sh + i] = (mmax + __log2f(dsum)) * 0.69314718055994530942f;
+    if (m.lse && blockIdx.y == 0 && c == 0) m.lse[bh * m.lse_sh + i] = (mmax + __log2f(dsum)) * 0.69314718055994530942f;
 }
 
 // ---------------------------------------------------------------------------
@@ -1452,14 +1490,24 @@ hipError_t launch_attn(const AttnArgs& a, int D, KvSource src, KeyMode mode, boo
     if (mode == KEYS_DECODE) {
         // always split: the merge writes the output
         if (!split) return hipErrorInvalidValue;
+        // the workgroup holds the packed rows in as few waves as fit them
+        const int waves = decode_waves(a.group * a.Lq);
         if (src == KV_E4M3_PAGED_SCALED) {
-            if (D == 128) return launch_one<128, 4, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(a, stream);
-            if (D == 256) return launch_one<256, 4, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(a, stream);
+            if (D == 128)
+                return waves == 1 ? launch_one<128, 1, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(a, stream)
+                                  : launch_one<128, 4, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(a, stream);
+            if (D == 256)
+                return waves == 1 ? launch_one<256, 1, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(a, stream)
+                                  : launch_one<256, 4, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(a, stream);
             return hipErrorInvalidValue;
         }
         if (src != KV_E4M3_PAGED) return hipErrorInvalidValue;
-        if (D == 128) return launch_one<128, 4, KV_E4M3_PAGED, KEYS_DECODE, true>(a, stream);
-        if (D == 256) return launch_one<256, 4, KV_E4M3_PAGED, KEYS_DECODE, true>(a, stream);
+        if (D == 128)
+            return waves == 1 ? launch_one<128, 1, KV_E4M3_PAGED, KEYS_DECODE, true>(a, stream)
+                              : launch_one<128, 4, KV_E4M3_PAGED, KEYS_DECODE, true>(a, stream);
+        if (D == 256)
+            return waves == 1 ? launch_one<256, 1, KV_E4M3_PAGED, KEYS_DECODE, true>(a, stream)
+                              : launch_one<256, 4, KV_E4M3_PAGED, KEYS_DECODE, true>(a, stream);
         return hipErrorInvalidValue;
     }
     if (mode == KEYS_BLOCKS) {
@@ -1500,20 +1548,33 @@ template __global__ void attn_fwd_kernel<256, 4, KV_E4M3_PAGED_SCALED, KEYS_CAUS
 template __global__ void attn_fwd_kernel<256, 4, KV_E4M3_PAGED_SCALED, KEYS_CAUSAL, true>(const AttnArgs);
 template __global__ void attn_fwd_kernel<128, 4, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(const AttnArgs);
 template __global__ void attn_fwd_kernel<256, 4, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 1, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(const AttnArgs);
+template __global__ void attn_fwd_kernel<256, 1, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(const AttnArgs);
+template __global__ void attn_fwd_kernel<128, 1, KV_E4M3_PAGED, KEYS_DECODE, true>(const AttnArgs);
+template __global__ void attn_fwd_kernel<256, 1, KV_E4M3_PAGED, KEYS_DECODE, true>(const AttnArgs);
 
 hipError_t launch_merge(const MergeArgs& m, int D, hipStream_t stream)
 {
     int64_t rows = (int64_t)m.B * m.Hq * m.Lq;
     if (m.nseg >= 16) {
-        // many segments per row: a workgroup per row
+        // many segments per row: a workgroup per (row, 64 columns), or per
+        // (row, 16 columns) when that leaves fewer workgroups than CUs
         if (rows <= 0) return hipSuccess;
         if (m.nseg > kWideMaxSeg || rows > 0x7fffffff) return hipErrorInvalidValue;
-        if (D == 128)
-            hipLaunchKernelGGL(attn_merge_wide_kernel<128>, dim3((unsigned)rows), dim3(kWideThreads), 0, stream, m);
-        else if (D == 256)
-            hipLaunchKernelGGL(attn_merge_wide_kernel<256>, dim3((unsigned)rows), dim3(kWideThreads), 0, stream, m);
-        else
-            return hipErrorInvalidValue;
+        if (D != 128 && D != 256) return hipErrorInvalidValue;
+        const bool narrow = rows * (D / 64) < kComputeUnits;
+        const dim3 grid((unsigned)rows, (unsigned)(D / (narrow ? 16 : 64)));
+        if (D == 128) {
+            if (narrow)
+                hipLaunchKernelGGL((attn_merge_wide_kernel<128, 16>), grid, dim3(kWideThreads), 0, stream, m);
+            else
+                hipLaunchKernelGGL((attn_merge_wide_kernel<128, 64>), grid, dim3(kWideThreads), 0, stream, m);
+        } else {
+            if (narrow)
+                hipLaunchKernelGGL((attn_merge_wide_kernel<256, 16>), grid, dim3(kWideThreads), 0, stream, m);
+            else
+                hipLaunchKernelGGL((attn_merge_wide_kernel<256, 64>), grid, dim3(kWideThreads), 0, stream, m);
+        }
         return hipGetLastError();
     }
     int grid = (int)((rows + 3) / 4);

@@ -25,11 +25,17 @@ constexpr int kTileN = 64;
 constexpr int kRowsPerWave = 32;
 // Query rows per workgroup of the dense and causal launches (4 waves).
 constexpr int kRowsPerTile = 128;
-// Packed (head, position) rows of a decode work item.
+// Packed (head, position) rows of a decode work item, at most.
 constexpr int kDecodeRows = 128;
 constexpr int kComputeUnits = 256;  // MI355X
 constexpr int kMaxSeg = 16;         // key segments per query tile, at most
 constexpr int kMinSegUnits = 16;    // at least 1024 keys per segment
+constexpr int kMaxDecodeSeg = 1024; // key segments of a decode, at most
+
+// Waves (32 packed rows each) of a decode workgroup for `rows` packed rows:
+// one when they fit one wave, so that a few live rows do not carry a full
+// 128-row tile and four such workgroups share a CU, else four.
+FA_HD inline int decode_waves(int rows) { return rows <= 32 ? 1 : 4; }
 
 // KEYS_DECODE: causal rows of a few query positions (Lq <= 16), with the
 // rows of every query head of a kv-head group packed into one tile, so each
@@ -198,16 +204,20 @@ inline SplitPlan plan_split(int B, int Hq, int D, int q_rows, int kv_len)
     return p;
 }
 
-// Decode: one work item per (b, kv head, segment), as many segments (of at
-// least 1024 keys) as it takes to give every CU its own stream of the cache.
+// Decode: one work item per (b, kv head, segment), as many segments as it
+// takes to give every workgroup slot of the GPU (4 / waves per CU, twice that
+// at D = 128) its own stream of the cache, each segment at least
+// 1024 * waves / 4 keys, and at most kMaxDecodeSeg segments.
 inline SplitPlan plan_decode(int B, int Hq, int Hkv, int D, int q_rows, int kv_len)
 {
     SplitPlan p;
     p.n_qt = 1;
     const int max_units = (kv_len + kTileN - 1) / kTileN;
-    const int64_t slots = (int64_t)kComputeUnits * (D == 128 ? 2 : 1);
+    const int waves = decode_waves((Hq / Hkv) * q_rows);
+    const int64_t slots = (int64_t)kComputeUnits * (D == 128 ? 2 : 1) * (4 / waves);
     const int64_t want = (slots + (int64_t)B * Hkv - 1) / ((int64_t)B * Hkv);
-    int cap = max_units / kMinSegUnits;
+    int cap = max_units / (kMinSegUnits * waves / 4);
+    if (cap > kMaxDecodeSeg) cap = kMaxDecodeSeg;
     if (cap < 1) cap = 1;
     int64_t n = want < 1 ? 1 : want;
     p.nseg = (int)(n < cap ? n : cap);

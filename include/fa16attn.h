@@ -208,7 +208,12 @@ int attn_fwd_paged_e4m3(fa_tensor q, const uint8_t* k_cache, const uint8_t* v_ca
  * j <= kv_len - q_real + i). The rows of all Hq / Hkv query heads of a kv head
  * are computed together, so each cache byte is read once per kv head; the key
  * range is split into segments whose FP32 states are merged by a second
- * kernel. Arguments, layouts and scales as attn_fwd_paged_e4m3.
+ * kernel. Arguments, layouts and scales as attn_fwd_paged_e4m3, without the
+ * bridged plan: with a k_scale that is not a power of two the K operands take
+ * the same converted values, formed once per workgroup in LDS, or, when the
+ * packed rows (Hq / Hkv) * q_rows fit one 32-row wave, in registers where
+ * the MFMAs use them (such one-wave workgroups run four to a CU, on segments
+ * of at least 256 keys).
  * Domain: B >= 1, Hkv >= 1, Hq % Hkv == 0; D in {128, 256};
  * 1 <= q_rows <= 16 with (Hq / Hkv) * q_rows <= 128; 1 <= q_real <= q_rows;
  * q_real < kv_len <= 262144; kv_len % 32 == 0; page_size == 32;

@@ -136,7 +136,15 @@ def test_paged_e4m3_parity(lib, Hq, Hkv, D, q_rows, q_real, kv_len, pages, ks, v
     (6, 1, 256, 5, 3, 2080, 70, 0.0625, 0.03125),      # padded rows, 32-key tail
     (4, 2, 128, 1, 1, 1024, 40, 0.0371, 0.0815),       # one position, two kv heads
     (8, 1, 128, 16, 16, 8192, 260, 1.0, 1.0),          # 8 heads x 16 rows fill the 128-row tile
-    (4, 2, 128, 2, 2, 16416, 520, 0.0625, 1.0),        # 16 segments: the workgroup-per-row merge
+    (4, 2, 128, 2, 2, 16416, 520, 0.0625, 1.0),        # 64 segments: the wide merge
+    # one-wave workgroups (at most 32 packed rows): K converted in registers
+    # (scaled) or decoded exactly (power-of-two k_scale), many short segments,
+    # the merge in 16-column slices
+    (6, 1, 256, 1, 1, 131072, 4100, 0.0371, 0.0815),   # one position: 6 rows, 512 segments
+    (6, 1, 256, 5, 4, 32768, 1030, 0.0703, 0.05),      # 30 rows, padded, scaled
+    (6, 1, 256, 4, 4, 8192, 260, 1.0, 1.0),            # 24 rows, power-of-two scale
+    (2, 1, 128, 16, 16, 65536, 2050, 0.0371, 0.0815),  # 32 rows fill the wave, D128
+    (8, 2, 128, 4, 3, 32800, 1030, 0.125, 0.0815),     # two kv heads, D128, a 32-key tail
 ])
 def test_paged_decode_parity(lib, Hq, Hkv, D, q_rows, q_real, kv_len, pages, ks, vs):
     say(f"paged decode Hq{Hq} Hkv{Hkv} D{D} q{q_rows} real{q_real} kv{kv_len} scales {ks} {vs}")

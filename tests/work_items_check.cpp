@@ -105,7 +105,8 @@ int main(int argc, char** argv)
         const bool decode = mode_s == "decode";
         mode = decode ? KEYS_DECODE : KEYS_CAUSAL;
         D = (int)v[3];
-        rows = decode ? kDecodeRows : kRowsPerTile;
+        // decode: the launcher's workgroup of 1 or 4 waves for the packed rows
+        rows = decode ? kRowsPerWave * decode_waves((int)(v[1] / v[2]) * (int)v[4]) : kRowsPerTile;
         p = decode ? plan_decode((int)v[0], (int)v[1], (int)v[2], D, (int)v[4], (int)v[6])
                    : plan_split((int)v[0], (int)v[1], D, (int)v[4], (int)v[6]);
         if (!causal_geometry(g, p, (int)v[0], (int)v[1], (int)v[2], (int)v[4], (int)v[5], (int)v[6], decode))
