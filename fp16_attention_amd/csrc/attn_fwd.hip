@@ -340,9 +340,9 @@ void attn_fwd_kernel(const AttnArgs a)
     // The scaled E4M3 source converts each K code tile once per workgroup into
     // an FP16 tile (each wave a quarter of it, between its PV MFMAs), from
     // which every wave reads its K operands as the 16-bit sources do. Decode
-    // workgroups of one or two waves (a few packed rows) instead convert the
+    // workgroups of a single wave (at most 32 packed rows) instead convert the
     // K operands in registers where the MFMAs consume them, as V is decoded:
-    // with so few waves the shared tile saves little, and without its FP16
+    // a lone wave has no one to share the tile with, and without its FP16
     // slots and deeper ring four such workgroups fit a CU's LDS.
     constexpr bool KREG = SRC == KV_E4M3_PAGED_SCALED && WAVES < 4;
     constexpr bool KCONV = SRC == KV_E4M3_PAGED_SCALED && !KREG;
