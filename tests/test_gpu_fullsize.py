@@ -107,11 +107,16 @@ def test_paged_e4m3_full(lib, unit_scales, bridged):
     assert_close(_rows_of(out.cpu().numpy(), rows), ref, f"O ({len(rows)} rows)")
 
 
-def test_paged_decode_full(lib):
-    """Every one of the 96 (head, position) rows of the decode workload, non-unit scales."""
+@pytest.mark.parametrize("positions", [16, 1])
+def test_paged_decode_full(lib, positions):
+    """Every (head, position) row of the decode workload, non-unit scales: its 16 positions (96 rows, the
+    128-row workgroups), and its first position alone (6 rows, the one-wave workgroups, 1000 segments)."""
     w = wl.PAGED_DECODE
     q, kc, vc, table, ks, vs = wl.paged_inputs(w, unit_scales=False)
-    say("full paged decode", w["name"], "scales", ks, vs)
+    if positions != w["q_rows"]:
+        w = dict(w, q_rows=positions, q_real=positions)
+        q = np.ascontiguousarray(q[:, :, :positions])
+    say("full paged decode", w["name"], "positions", positions, "scales", ks, vs)
     lse = torch.empty((w["B"], w["Hq"], w["q_rows"]), dtype=torch.float32, device="cuda")
     out = lib.attn_fwd_paged_e4m3_decode(dev(q), dev(kc), dev(vc), dev(table), w["kv_len"], w["q_real"], ks, vs,
                                          lse=lse)
