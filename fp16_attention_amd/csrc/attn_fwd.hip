@@ -109,6 +109,8 @@ constexpr float kRescaleSlack = 8.0f;
 // s_waitcnt immediates (gfx9 encoding): vmcnt in [3:0] and [15:14], expcnt in
 // [6:4], lgkmcnt in [11:8].
 constexpr int kWaitVm0 = 0x0F70;
+// vmcnt(0) and lgkmcnt(0)
+constexpr int kWaitAll = 0x0070;
 
 // Workgroup barrier for the K/V ring: the caller's s_waitcnt (vmcnt(n) with
 // lgkmcnt(0)) makes this wave's loads into LDS older than the n most recent
@@ -1267,6 +1269,282 @@ void attn_fwd_kernel(const AttnArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Decode of 33..64 packed rows at D = 256 from the paged E4M3 cache: 16-row
+// waves on v_mfma_f32_16x16x32_f16, NR = 4 of them per key half, two key
+// halves per workgroup (eight waves, two per SIMD, where the four-wave kernel
+// has one wave per SIMD and two 32-row waves of padding), the halves' states
+// merged in LDS at the end. (Six row waves for 65..96 rows, three waves per
+// SIMD, leave too few registers to read operands ahead and are not used.)
+//
+// MFMA layouts (16x16x32): A lane l holds row l % 16, k = 8 (l / 16) .. +7;
+// B lane l holds column l % 16, the same k; D register r of lane l is row
+// 4 (l / 16) + r, column l % 16. With lane (q, g) = (l % 16, l / 16):
+//  - S^T = K Q^T per 16-key block kb: A = FP16 K rows 16 kb + q, dims
+//    32 kk + 8 g .. +7 (eight k-steps over D); B = Q^T of query row q (the
+//    wave's packed row 16 rw + q); lane (q, g) gets the scores of keys
+//    16 kb + 4 g + r for its query q.
+//  - P^T, the B operand of O^T += V^T P^T, takes them in that order: k-index
+//    8 g + i stands for key pi(8 g + i) = 4 g + i (i < 4), 16 + 4 g + i - 4.
+//  - V^T, the A operand (16 d x 32 k), lane (d, g): codes of keys pi(8 g .. +7)
+//    at column 16 db + d, through ds_read_b64_tr_b8 (source lane 2 j + h of
+//    group g points at key row pi(8 g + j), bytes 16 db + 8 h .. +7).
+//  - O^T per 16-wide d block db: lane (q, g) holds d = 16 db + 4 g + r.
+// Ring per iteration j: all waves convert K(j+1)'s codes into its FP16 tile
+// (both halves), compute S(j) and PV(j), wait for every load issued before
+// the previous barrier, pass the barrier, and issue K(j+3) and V(j+2) into
+// the code slots just freed: two K code slots, two V code slots and two FP16
+// K slots, each holding both halves' tiles (132 KB). Eight waves issue the
+// loads, one 1 KB block of each 8 KB tile each.
+// ---------------------------------------------------------------------------
+template <int NR, bool SCALED>
+__global__ __launch_bounds__(NR * 128, 1) void attn_decode16_kernel(const AttnArgs a)
+{
+    constexpr int D = 256, KT = 32, NW = 2 * NR, NT = NW * 64;
+    constexpr int TB = KT * D;      // code tile bytes
+    constexpr int FROW = 2 * D + 16;  // FP16 tile row bytes, padded: the 16 rows of an operand read fall in
+                                      // 16 distinct 16-byte bank groups, and k-steps are immediate offsets
+    constexpr int TF = KT * FROW;     // FP16 tile bytes
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(1024))) unsigned char kcs0[2 * TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kcs1[2 * TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char vcs0[2 * TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char vcs1[2 * TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kfs0[2 * TF];
+    __shared__ __attribute__((aligned(1024))) unsigned char kfs1[2 * TF];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = wave / NR, rw = wave % NR;
+    const int q = lane & 15, gq = lane >> 4;
+
+    const int item = item_of_block(a, blockIdx.x);
+    if (item < 0) return;
+    const Item wi = decode_item(KEYS_DECODE, a, item, kDecodeRows);
+    if (wi.empty) return;
+    const int b = wi.b, h0 = wi.h, seg = wi.seg;
+    const int g = h0 / a.group;
+    // tiles of the segment, the first half's share first
+    const int n_all = (wi.key_stop - wi.key_begin + KT - 1) / KT;
+    const int n0 = (n_all + 1) / 2;
+    const int n_my = half ? n_all - n0 : n0;
+    const int key_begin = wi.key_begin + (half ? n0 * KT : 0);
+    const int key_stop = wi.key_stop;
+
+    // this lane's packed row: head h0 + r / Lq, position r % Lq
+    const int r = 16 * rw + q, jh = r / a.Lq;
+    const int pos = r - jh * a.Lq, qh = h0 + min(jh, a.group - 1);
+    const bool row_ok = jh < a.group;
+    h8 qf[8];
+    {
+        const _Float16* qp = a.q + (int64_t)b * a.q_sb + (int64_t)qh * a.q_sh + (int64_t)pos * a.q_ss;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) qf[kk] = *(const h8*)(qp + 32 * kk + 8 * gq);
+    }
+    const float crow = a.c;
+    const int64_t qlim = a.offset + pos;  // the last key this row sees
+
+    // loads: waves 0-7, one 1 KB block of a tile each
+    const int32_t* table = a.table + (int64_t)b * a.table_stride;
+    ByteLoader<D, 8, KT> bl;
+    if (wave < 8) bl.init(a.Hkv * D, wave, lane);
+    auto issue_tile = [&](const uint8_t* cache, int hf, int t, unsigned char* slot) {
+        const int nh = hf ? n_all - n0 : n0;
+        const bool ok = t < nh;
+        const int key0 = wi.key_begin + (hf ? n0 * KT : 0) + (ok ? t : 0) * KT;
+        const int page = min(max(scalar_load(table, key0 >> 5), 0), a.num_pages - 1);
+        const int rows = ok ? min(KT, key_stop - key0) : 0;
+        bl.issue(cache + ((int64_t)page * 32 * a.Hkv + g) * D, rows * a.Hkv * D, slot + hf * TB, wave);
+    };
+    auto issue_k = [&](int t, unsigned char* slot) {
+        if (wave < 8) {
+            issue_tile(a.kc, 0, t, slot);
+            issue_tile(a.kc, 1, t, slot);
+        }
+    };
+    auto issue_v = [&](int t, unsigned char* slot) {
+        if (wave < 8) {
+            issue_tile(a.vc, 0, t, slot);
+            issue_tile(a.vc, 1, t, slot);
+        }
+    };
+
+    // K code tile -> FP16 tile (both halves): 1024 chunks of 16 codes
+    const float kscale = a.kscale;
+    auto conv2 = [&](f2 d) -> uint32_t {
+        if constexpr (SCALED) {
+            float x0 = d.x * kscale, x1 = d.y * kscale;
+            asm volatile("" : "+v"(x0), "+v"(x1));
+            return __builtin_bit_cast(uint32_t, h2{(_Float16)x0, (_Float16)x1});
+        } else {
+            return __builtin_bit_cast(uint32_t, h2{(_Float16)d.x, (_Float16)d.y});  // exact
+        }
+    };
+    auto convert = [&](const unsigned char* cs, unsigned char* fs) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = tid + NT * j;
+            if (c < 1024) {
+                const int hf = c >> 9, cc = c & 511, row = cc >> 4, ch = cc & 15;
+                const u4 w = *(const u4*)(cs + hf * TB + row * D + ((ch ^ bswz<D>(row)) << 4));
+                u4 lo, hi;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t word = w[u];
+                    const uint32_t p0 = conv2(__builtin_amdgcn_cvt_pk_f32_fp8(word, false));
+                    const uint32_t p1 = conv2(__builtin_amdgcn_cvt_pk_f32_fp8(word, true));
+                    if (u < 2) {
+                        lo[2 * u] = p0;
+                        lo[2 * u + 1] = p1;
+                    } else {
+                        hi[2 * (u - 2)] = p0;
+                        hi[2 * (u - 2) + 1] = p1;
+                    }
+                }
+                *(u4*)(fs + hf * TF + row * FROW + 32 * ch) = lo;
+                *(u4*)(fs + hf * TF + row * FROW + 32 * ch + 16) = hi;
+            }
+        }
+    };
+
+    f4 oacc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[i] = f4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const h2 ones = {(_Float16)1.f, (_Float16)1.f};
+
+    // per-lane LDS offsets: K operand (row 16 kb + q, FP16 chunk 4 kk + gq: the
+    // k-step and the block are immediate offsets) and the V tr8 source (key
+    // row pi(8 gq + sl / 2), bytes 8 (sl % 2) .. +7 of the chunk of d block db)
+    const int sl = lane & 15, vj = sl >> 1, vh = sl & 1;
+    const int vrow = vj < 4 ? 4 * gq + vj : 16 + 4 * gq + vj - 4;
+    const int koff = q * FROW + 16 * gq;
+    const int vbase = vrow * D + 8 * vh, vx = (vrow & 15) << 4;  // chunk db sits at db ^ (row % 16)
+
+    // one tile: scores, softmax, PV (the wave's half, tile t of it)
+    auto tile = [&](const unsigned char* kf, const unsigned char* vc, int t) {
+        const unsigned char* kt = kf + half * TF;
+        const unsigned char* vt = vc + half * TB;
+        f4 s[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8*)(kt + koff + kb * 16 * FROW + 64 * kk),
+                                                               qf[kk], s[kb], 0, 0, 0);
+        const int key0 = key_begin + t * KT;
+        if ((int64_t)key0 + KT > a.offset + 1 || key0 + KT > key_stop) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = key0 + 16 * kb + 4 * gq + i;
+                    if (key >= key_stop || key > qlim) s[kb][i] = -INFINITY;
+                }
+        }
+        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mc = mx * crow;
+        const bool raise = mc > m_run + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+            const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - mc) : 1.f;
+            m_run = raise ? mc : m_run;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[i] *= alpha;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        h8 pk;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+                const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][i], crow, -m_use));
+                const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][i + 1], crow, -m_use));
+                const h2 p = {(_Float16)e0, (_Float16)e1};
+                l_run = __builtin_amdgcn_fdot2(p, ones, l_run, false);
+                pk[4 * kb + i] = p.x;
+                pk[4 * kb + i + 1] = p.y;
+            }
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+            const u2 c = __builtin_bit_cast(
+                u2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (lds_v2i_t*)(vt + vbase + ((db << 4) ^ vx))));
+            const u2 lo = e4m3x4_to_f16(c.x), hi = e4m3x4_to_f16(c.y);
+            const h8 vop = __builtin_bit_cast(h8, u4{lo.x, lo.y, hi.x, hi.y});
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pk, oacc[db], 0, 0, 0);
+        }
+    };
+
+    // prologue: K(0), K(1), V(0), V(1); K(0) converted; then K(2)
+    issue_k(0, kcs0);
+    issue_k(1, kcs1);
+    issue_v(0, vcs0);
+    issue_v(1, vcs1);
+    ring_barrier<kWaitAll>();  // vmcnt(0), lgkmcnt(0)
+    convert(kcs0, kfs0);
+    ring_barrier<kWaitAll>();
+    issue_k(2, kcs0);
+
+    // iteration j: convert K(j+1), tile j, then wait, barrier, K(j+3), V(j+2)
+    auto iteration = [&](auto p, int j) {
+        constexpr int P = decltype(p)::value;
+        unsigned char* kc_next = P == 0 ? kcs1 : kcs0;  // K(j+1)'s codes
+        unsigned char* kf_next = P == 0 ? kfs1 : kfs0;
+        const unsigned char* kf_cur = P == 0 ? kfs0 : kfs1;
+        unsigned char* vc_cur = P == 0 ? vcs0 : vcs1;
+        convert(kc_next, kf_next);
+        if (j < n_my) tile(kf_cur, vc_cur, j);
+        ring_barrier<kWaitAll>();
+        issue_k(j + 3, kc_next);
+        issue_v(j + 2, vc_cur);
+    };
+    using Q0 = std::integral_constant<int, 0>;
+    using Q1 = std::integral_constant<int, 1>;
+    int j = 0;
+    for (; j + 1 < n0; j += 2) {
+        iteration(Q0{}, j);
+        iteration(Q1{}, j + 1);
+    }
+    if (j < n0) iteration(Q0{}, j);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no load into LDS in flight at the end
+
+    // row sums over the four lanes of a query; then the halves' merge
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    __syncthreads();
+    {
+        // half 1 leaves O (16 KB per wave) and (m, l) in the ring's space
+        unsigned char* xb = rw < 2 ? kfs0 : rw < 4 ? kfs1 : rw == 4 ? vcs0 : vcs1;
+        f4* xo = (f4*)(xb + (rw < 4 ? (rw & 1) * 16384 : 0));
+        f2* xml = (f2*)kcs0 + rw * 64;
+        if (half == 1) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xo[i * 64 + lane] = oacc[i];
+            xml[lane] = f2{m_run, l_run};
+        }
+        __syncthreads();
+        if (half == 1) return;
+        const f2 ml1 = xml[lane];
+        const float mx = fmaxf(m_run, ml1.x);
+        const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+        const float a1 = ml1.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml1.x - mx);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[i] = oacc[i] * a0 + xo[i * 64 + lane] * a1;
+        l_run = l_run * a0 + ml1.y * a1;
+        m_run = mx;
+    }
+    if (!row_ok) return;
+    const int64_t bh = (int64_t)b * a.Hq + qh;
+    float* op = a.o_part + (((int64_t)seg * a.B * a.Hq + bh) * a.part_lq + pos) * D;
+#pragma unroll
+    for (int db = 0; db < 16; ++db) *(f4*)(op + 16 * db + 4 * gq) = oacc[db];
+    if (gq == 0) *(f2*)(a.ml_part + (((int64_t)seg * a.B * a.Hq + bh) * a.part_lq + pos) * 2) = f2{m_run, l_run};
+}
+
+// ---------------------------------------------------------------------------
 // Merge of split-KV partial states, in segment order:
 //   M = max_s m_s, w_s = 2^(m_s - M), O = sum_s w_s O_s / sum_s w_s l_s.
 // One wave per query row.
@@ -1490,8 +1768,19 @@ hipError_t launch_attn(const AttnArgs& a, int D, KvSource src, KeyMode mode, boo
     if (mode == KEYS_DECODE) {
         // always split: the merge writes the output
         if (!split) return hipErrorInvalidValue;
-        // the workgroup holds the packed rows in as few waves as fit them
+        // the workgroup holds the packed rows in as few waves as fit them; at
+        // D = 256, 33..64 rows take the 16-row-wave kernel
         const int waves = decode_waves(a.group * a.Lq);
+        const int rows = a.group * a.Lq;
+        if (D == 256 && rows > 32 && rows <= 64 && (src == KV_E4M3_PAGED_SCALED || src == KV_E4M3_PAGED)) {
+            const int grid = a.per_xcd > 0 ? a.per_xcd * 8 : a.n_items;
+            if (grid <= 0) return hipSuccess;
+            if (src == KV_E4M3_PAGED_SCALED)
+                hipLaunchKernelGGL((attn_decode16_kernel<4, true>), dim3(grid), dim3(512), 0, stream, a);
+            else
+                hipLaunchKernelGGL((attn_decode16_kernel<4, false>), dim3(grid), dim3(512), 0, stream, a);
+            return hipGetLastError();
+        }
         if (src == KV_E4M3_PAGED_SCALED) {
             if (D == 128)
                 return waves == 1 ? launch_one<128, 1, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(a, stream)
@@ -1552,6 +1841,8 @@ template __global__ void attn_fwd_kernel<128, 1, KV_E4M3_PAGED_SCALED, KEYS_DECO
 template __global__ void attn_fwd_kernel<256, 1, KV_E4M3_PAGED_SCALED, KEYS_DECODE, true>(const AttnArgs);
 template __global__ void attn_fwd_kernel<128, 1, KV_E4M3_PAGED, KEYS_DECODE, true>(const AttnArgs);
 template __global__ void attn_fwd_kernel<256, 1, KV_E4M3_PAGED, KEYS_DECODE, true>(const AttnArgs);
+template __global__ void attn_decode16_kernel<4, true>(const AttnArgs);
+template __global__ void attn_decode16_kernel<4, false>(const AttnArgs);
 
 hipError_t launch_merge(const MergeArgs& m, int D, hipStream_t stream)
 {

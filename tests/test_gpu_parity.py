@@ -145,6 +145,10 @@ def test_paged_e4m3_parity(lib, Hq, Hkv, D, q_rows, q_real, kv_len, pages, ks, v
     (6, 1, 256, 4, 4, 8192, 260, 1.0, 1.0),            # 24 rows, power-of-two scale
     (2, 1, 128, 16, 16, 65536, 2050, 0.0371, 0.0815),  # 32 rows fill the wave, D128
     (8, 2, 128, 4, 3, 32800, 1030, 0.125, 0.0815),     # two kv heads, D128, a 32-key tail
+    (6, 1, 256, 8, 8, 8192, 260, 0.0703, 0.05),        # 48 rows, scaled
+    (4, 1, 256, 16, 11, 32992, 1040, 0.0625, 0.0815),  # 64 rows, power-of-two scale, padded positions
+    (6, 1, 256, 11, 9, 20000, 630, 0.0371, 0.0815),    # 66 rows, scaled, padded
+    (6, 1, 256, 16, 16, 1056, 40, 0.0703, 0.05),       # one short segment: an odd tile count
 ])
 def test_paged_decode_parity(lib, Hq, Hkv, D, q_rows, q_real, kv_len, pages, ks, vs):
     say(f"paged decode Hq{Hq} Hkv{Hkv} D{D} q{q_rows} real{q_real} kv{kv_len} scales {ks} {vs}")

@@ -23,7 +23,9 @@ DECODE = [(1, 6, 1, 256, 16, 16, 256000), (1, 6, 1, 256, 16, 16, 4096), (1, 6, 1
           (1, 6, 1, 256, 1, 1, 256000), (1, 6, 1, 256, 5, 5, 256000), (1, 8, 1, 128, 4, 4, 262144),
           (2, 4, 2, 256, 3, 2, 40000), (1, 6, 1, 256, 1, 1, 65536), (1, 6, 1, 256, 6, 6, 100000),
           (1, 6, 1, 256, 1, 1, 131072), (1, 6, 1, 256, 5, 4, 32768), (1, 6, 1, 256, 4, 4, 8192),
-          (1, 2, 1, 128, 16, 16, 65536), (1, 8, 2, 128, 4, 3, 32800)]
+          (1, 2, 1, 128, 16, 16, 65536), (1, 8, 2, 128, 4, 3, 32800),
+          (1, 6, 1, 256, 8, 8, 8192), (1, 4, 1, 256, 16, 11, 32992), (1, 6, 1, 256, 11, 9, 20000),
+          (1, 6, 1, 256, 16, 16, 1056)]
 BLOCKS = [(1, 8, 36864, 128, 64, 64, 2), (1, 2, 2048, 128, 64, 8, 2), (1, 2, 1280, 128, 64, 20, 0),
           (1, 2, 1024, 128, 64, 3, 16), (1, 2, 64 * 30 + 37, 128, 64, 7, 2), (1, 2, 64 * 6 + 1, 128, 64, 7, 7),
           (2, 3, 64 * 12 + 5, 128, 64, 5, 1), (1, 1, 50, 128, 64, 1, 1), (1, 8, 36864, 128, 64, 116, 2)]
