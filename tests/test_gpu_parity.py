@@ -331,6 +331,8 @@ def test_bitwise_repeatability_without_sync(lib):
 @pytest.mark.parametrize("decode,Hq,Hkv,D,q_rows,q_real,kv_len", [
     (False, 4, 2, 128, 128, 100, 640),   # prefill, two sequences with their own page lists
     (True, 6, 1, 256, 16, 16, 1056),     # decode, two sequences, a 32-key tail
+    (True, 8, 2, 256, 12, 10, 4128),     # decode, two sequences and kv heads, 48 rows (16-row waves)
+    (True, 4, 2, 256, 3, 3, 2080),       # decode, two sequences and kv heads, 6 rows (one-wave workgroups)
 ])
 def test_paged_two_sequences_parity(lib, decode, Hq, Hkv, D, q_rows, q_real, kv_len):
     say(f"paged {'decode' if decode else 'prefill'} B2 Hq{Hq} Hkv{Hkv} D{D} q{q_rows} real{q_real} kv{kv_len}")

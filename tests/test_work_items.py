@@ -25,7 +25,7 @@ DECODE = [(1, 6, 1, 256, 16, 16, 256000), (1, 6, 1, 256, 16, 16, 4096), (1, 6, 1
           (1, 6, 1, 256, 1, 1, 131072), (1, 6, 1, 256, 5, 4, 32768), (1, 6, 1, 256, 4, 4, 8192),
           (1, 2, 1, 128, 16, 16, 65536), (1, 8, 2, 128, 4, 3, 32800),
           (1, 6, 1, 256, 8, 8, 8192), (1, 4, 1, 256, 16, 11, 32992), (1, 6, 1, 256, 11, 9, 20000),
-          (1, 6, 1, 256, 16, 16, 1056)]
+          (1, 6, 1, 256, 16, 16, 1056), (2, 8, 2, 256, 12, 10, 4128), (2, 4, 2, 256, 3, 3, 2080)]
 BLOCKS = [(1, 8, 36864, 128, 64, 64, 2), (1, 2, 2048, 128, 64, 8, 2), (1, 2, 1280, 128, 64, 20, 0),
           (1, 2, 1024, 128, 64, 3, 16), (1, 2, 64 * 30 + 37, 128, 64, 7, 2), (1, 2, 64 * 6 + 1, 128, 64, 7, 7),
           (2, 3, 64 * 12 + 5, 128, 64, 5, 1), (1, 1, 50, 128, 64, 1, 1), (1, 8, 36864, 128, 64, 116, 2)]
