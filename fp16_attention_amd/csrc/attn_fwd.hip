@@ -152,6 +152,15 @@ __device__ __forceinline__ float2 half_pair(float x)
     const unsigned lo = r[0], hi = r[1];
     return {__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi)};
 }
+// The same for lanes l and l ^ 16 through v_permlane16_swap, which trades
+// the odd 16-lane rows of one register with the even rows of another.
+__device__ __forceinline__ float2 row_pair(float x)
+{
+    const unsigned a = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+    const unsigned lo = r[0], hi = r[1];
+    return {__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi)};
+}
 __device__ __forceinline__ float wave_half_max(float x) { const float2 p = half_pair(x); return fmaxf(p.x, p.y); }
 __device__ __forceinline__ float wave_half_sum(float x) { const float2 p = half_pair(x); return p.x + p.y; }
 
@@ -1299,6 +1308,7 @@ void attn_fwd_kernel(const AttnArgs a)
 template <int NR, bool SCALED>
 __global__ __launch_bounds__(NR * 128, 1) void attn_decode16_kernel(const AttnArgs a)
 {
+    static_assert(NR >= 1 && NR <= 6, "row waves: the merge space holds six waves' states");
     constexpr int D = 256, KT = 32, NW = 2 * NR, NT = NW * 64;
     constexpr int TB = KT * D;      // code tile bytes
     constexpr int FROW = 2 * D + 16;  // FP16 tile row bytes, padded: the 16 rows of an operand read fall in
@@ -1443,8 +1453,8 @@ __global__ __launch_bounds__(NR * 128, 1) void attn_decode16_kernel(const AttnAr
         }
         float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                          fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float2 m16 = row_pair(mx);
+        mx = wave_half_max(fmaxf(m16.x, m16.y));
         const float mc = mx * crow;
         const bool raise = mc > m_run + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(raise)) {
@@ -1512,8 +1522,8 @@ __global__ __launch_bounds__(NR * 128, 1) void attn_decode16_kernel(const AttnAr
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no load into LDS in flight at the end
 
     // row sums over the four lanes of a query; then the halves' merge
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    const float2 l16 = row_pair(l_run);
+    l_run = wave_half_sum(l16.x + l16.y);
     __syncthreads();
     {
         // half 1 leaves O (16 KB per wave) and (m, l) in the ring's space
