@@ -322,19 +322,20 @@ def bench_paged(fa, torch, iters, timer, flush):
     decode = {"workload": wd["name"] + f" k_scale={ks:.6g} v_scale={vs:.6g}", "bytes": nb, **stats(ms),
               "gbs": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS, "llc_flushed": True,
               "workspace_bytes": int(ws_d.numel())}
-    # the same cache decoded for one new position per head (6 packed rows: the
-    # one-wave workgroups), timing only
-    q1 = qd[:, :, :1].contiguous()
-    ws_1 = torch.empty(fa.load().attn_fwd_paged_e4m3_decode_workspace(wd["B"], wd["Hq"], wd["Hkv"], wd["D"], 1,
-                                                                       wd["kv_len"]),
-                       dtype=torch.uint8, device="cuda")
-    o1 = torch.empty_like(q1)
-    fn = lambda: fa.attn_fwd_paged_e4m3_decode(q1, dkc, dvc, dt, wd["kv_len"], 1, ks, vs, out=o1, workspace=ws_1)
-    ms1, _ = timer.run(fn, iters, 2, flush=flush)
-    gbs1 = nb / (np.median(ms1) * 1e-3) / 1e9
-    log(f"paged decode, one position: {np.median(ms1) * 1e3:.1f} us  {gbs1:.0f} GB/s")
-    decode["one_position"] = {"q_rows": 1, **stats(ms1), "gbs": gbs1, "frac_hbm_peak": gbs1 / HBM_PEAK_GBS,
-                              "workspace_bytes": int(ws_1.numel())}
+    # the same cache decoded for fewer new positions per head, timing only: one
+    # (6 packed rows: one-wave workgroups) and eight (48 rows: 16-row waves)
+    for n, key in ((1, "one_position"), (8, "eight_positions")):
+        qn = qd[:, :, :n].contiguous()
+        ws_n = torch.empty(fa.load().attn_fwd_paged_e4m3_decode_workspace(wd["B"], wd["Hq"], wd["Hkv"], wd["D"], n,
+                                                                           wd["kv_len"]),
+                           dtype=torch.uint8, device="cuda")
+        on = torch.empty_like(qn)
+        fn = lambda: fa.attn_fwd_paged_e4m3_decode(qn, dkc, dvc, dt, wd["kv_len"], n, ks, vs, out=on, workspace=ws_n)
+        msn, _ = timer.run(fn, iters, 2, flush=flush)
+        gbsn = nb / (np.median(msn) * 1e-3) / 1e9
+        log(f"paged decode, {n} position{'s' if n > 1 else ''}: {np.median(msn) * 1e3:.1f} us  {gbsn:.0f} GB/s")
+        decode[key] = {"q_rows": n, **stats(msn), "gbs": gbsn, "frac_hbm_peak": gbsn / HBM_PEAK_GBS,
+                       "workspace_bytes": int(ws_n.numel())}
     return fused, bridge, decode
 
 
