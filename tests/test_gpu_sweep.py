@@ -134,6 +134,34 @@ def test_sweep_paged_decode(lib, case):
 
 
 @pytest.mark.parametrize("case", range(6))
+def test_sweep_paged_decode_mid_rows(lib, case):
+    """33..64 packed rows at D256 (the 16-row-wave decode): random groups, positions, lengths and scales."""
+    r = draw(case, 6)
+    Hq, Hkv = [(6, 1), (8, 2), (4, 1), (8, 1), (12, 3)][int(r.integers(0, 5))]
+    group = Hq // Hkv
+    q_rows = int(r.integers((32 // group) + 1, min(16, 64 // group) + 1))
+    q_real = int(r.integers(1, q_rows + 1))
+    B, D = int(r.integers(1, 3)), 256
+    kv_len = (q_real + 1 + int(r.integers(0, 12000)) + 31) // 32 * 32
+    per_seq = kv_len // 32
+    pages = B * per_seq + int(r.integers(0, 8))
+    ks = float(np.float32(r.uniform(0.01, 0.1))) if case % 2 else float(2.0 ** -int(r.integers(1, 6)))
+    vs = float(np.float32(r.uniform(0.01, 0.1)))
+    say(f"sweep decode rows {group * q_rows}: B{B} Hq{Hq} Hkv{Hkv} q{q_rows} real{q_real} kv{kv_len} scales {ks} {vs}")
+    seed = 700 + case
+    q = synth.normal_f16(seed, synth.TID_Q, (B, Hq, q_rows, D))
+    kc = synth.e4m3_codes(seed, synth.TID_K, (pages, 32, Hkv, D), ks)
+    vc = synth.e4m3_codes(seed, synth.TID_V, (pages, 32, Hkv, D), vs)
+    table = synth.permutation(seed, synth.TID_TABLE, pages)[: B * per_seq].reshape(B, per_seq).copy()
+    lse = torch.empty((B, Hq, q_rows), dtype=torch.float32, device="cuda")
+    out = lib.attn_fwd_paged_e4m3_decode(dev(q), dev(kc), dev(vc), dev(table), kv_len, q_real, ks, vs, lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = _paged_ref(lib, q, kc, vc, table, kv_len, q_real, ks, vs, D)
+    assert_close(out.cpu().numpy().reshape(-1, D), ref, "O")
+    assert np.abs(lse.cpu().numpy().ravel() - ref_lse).max() < LSE_ABS
+
+
+@pytest.mark.parametrize("case", range(6))
 def test_sweep_vsa(lib, case):
     r = draw(case, 5)
     B, H = int(r.integers(1, 3)), int(r.integers(1, 4))
